@@ -1,0 +1,186 @@
+/*
+ * mi_moe.h -- C ABI of the MI355X (gfx950) routed-MoE hot path.
+ *
+ * Operations (sources are cited by page title and section):
+ *   - mi_grouped_mm_bf16      ragged per-expert grouped GEMM
+ *                             (flashinfer.grouped_mm.grouped_mm_bf16, formula)
+ *   - mi_moe_fc2_lora_delta   FC2 LoRA delta of a routed MoE
+ *                             (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta, formula)
+ *   - mi_mm_nvfp4_lora        NVFP4 GEMM with an fp32 LoRA epilogue, raw and prepared
+ *                             (flashinfer.gemm.mm_nvfp4_lora, formula and the two bullets)
+ *   - mi_prepare_lora_fold    the prepared-path fold
+ *                             (flashinfer.gemm.prepare_nvfp4_lora_adapter, description and `out=`)
+ *   - mi_nvfp4_dequant_bf16   NVFP4 -> bf16 dequantisation with the GEMM's own decoder
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or retains them and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on that stream and returns; nothing is read
+ *     back to the host.  Results are valid once the stream reaches the work.
+ *   - Arguments are validated on the host BEFORE any HIP call.  A violation
+ *     returns MI_EINVAL (or MI_EUNSUPPORTED for a valid but unimplemented
+ *     dtype/shape) and mi_last_error() names the violated requirement; nothing
+ *     is enqueued.  MI_EHIP means a HIP launch error (message from HIP).
+ *   - Device-resident index data (m_indptr, ids, permutations) is not read on
+ *     the host; kernels clamp/skip out-of-range values so they stay memory-safe.
+ *   - Calls are thread-safe; the error message is thread-local.
+ *   - Row-major layouts; "bf16" is IEEE binary32 truncated to its top 16 bits
+ *     (rounding, where a result is produced, is to nearest even).
+ */
+#ifndef MI_MOE_H
+#define MI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MI_API __attribute__((visibility("default")))
+#else
+#define MI_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MI_OK = 0,
+  MI_EINVAL = 1,        /* invalid argument: maps to ValueError */
+  MI_EUNSUPPORTED = 2,  /* valid request this build does not implement */
+  MI_EHIP = 3           /* HIP runtime error while enqueueing */
+} mi_status;
+
+typedef enum { MI_BF16 = 0, MI_F16 = 1, MI_F32 = 2 } mi_dtype;
+
+/* Message of the last failing call on this thread ("" after success). */
+MI_API const char* mi_last_error(void);
+
+/* ABI version of this library (bumped on any signature change). */
+MI_API int mi_abi_version(void);
+
+/*
+ * Ragged grouped GEMM (flashinfer.grouped_mm.grouped_mm_bf16, formula and
+ * parameters): for every expert e with s = m_indptr[e], t = m_indptr[e+1],
+ *     out[s:t, :] = a[s:t, :] @ b[e]^T
+ * accumulated in fp32 and rounded once to out_dtype.
+ *
+ *   a         bf16 [m_rows, k]
+ *   b         bf16 [batch, n, k]    (K-major: row j of b[e] is output column j)
+ *   m_indptr  int32 [batch + 1], device, non-decreasing, 0 <= values <= m_rows;
+ *             read on the device only -- empty groups are skipped, no padding
+ *   out       [m_rows, n] of out_dtype (MI_BF16 or MI_F32); only rows
+ *             [m_indptr[0], m_indptr[batch]) are written, the rest untouched
+ * Requirements: m_rows >= 0, batch >= 1, n % 256 == 0, k % 64 == 0 (the
+ * device-walk backend's shape rule on the page), k >= 64.
+ */
+MI_API mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k,
+                             const void* b, int64_t batch, int64_t n,
+                             const int32_t* m_indptr,
+                             void* out, mi_dtype out_dtype, void* stream);
+
+/*
+ * FC2 LoRA delta of a routed MoE (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta,
+ * formula and parameters):
+ *     delta[t] = scale * sum_j w[t,j] * B_down[l,e] @ (A_down[l,e] @ act[perm[t*top_k+j]])
+ * with e = topk_ids[t,j], w = topk_weights[t,j], l = lora_ids[t].
+ *
+ *   act          lora_dtype [padded_rows, inter_size]  permuted post-activation rows
+ *   expanded_idx_to_permuted_idx  int32 [num_tokens * top_k]; < 0 = inactive slot
+ *   w_ptr_a      int64 [num_experts]: byte address (16-byte aligned) of A_down[0,e], a [rank, inter_size]
+ *                block; adapter l starts lora_stride_a ELEMENTS later
+ *   w_ptr_b      int64 [num_experts]: byte address (16-byte aligned) of B_down[0,e], a [hidden, rank]
+ *                block; adapter l starts lora_stride_b ELEMENTS later
+ *   topk_ids     int32 [num_tokens, top_k];  topk_weights fp32 [num_tokens, top_k]
+ *   lora_ids     int32 [num_tokens]; < 0 = no adapter.  Ids >= num_adapters, slots
+ *                whose permuted row is >= padded_rows and expert ids outside
+ *                [0, num_experts) are treated as inactive (memory safety only;
+ *                they are caller errors).
+ *   out          out_dtype [num_tokens, hidden]; EVERY element is written (+0 for
+ *                tokens without adapter or without an active slot)
+ *   workspace    device scratch of at least mi_moe_fc2_lora_delta_workspace_size()
+ *                bytes, 256-byte aligned; contents need no initialisation
+ * The intermediate A_down @ act stays fp32; the result is rounded once.
+ * Requirements: lora_dtype MI_BF16; out_dtype MI_BF16 or MI_F32; rank % 8 == 0,
+ * 8 <= rank <= 128; inter_size % 8 == 0; hidden % 128 == 0; 1 <= top_k <= 32;
+ * top_k * rank <= 512; lora strides multiples of 8; num_adapters * num_experts <= 8192.
+ */
+MI_API size_t mi_moe_fc2_lora_delta_workspace_size(int64_t num_tokens, int64_t top_k,
+                                            int64_t num_experts, int64_t num_adapters,
+                                            int64_t rank);
+MI_API mi_status mi_moe_fc2_lora_delta(const void* act, int64_t padded_rows, int64_t inter_size,
+                                const int32_t* expanded_idx_to_permuted_idx,
+                                const int64_t* w_ptr_a, int64_t lora_stride_a,
+                                const int64_t* w_ptr_b, int64_t lora_stride_b,
+                                const int32_t* topk_ids, const float* topk_weights,
+                                const int32_t* lora_ids,
+                                int64_t num_tokens, int64_t top_k, int64_t num_experts,
+                                int64_t num_adapters, int64_t rank, int64_t hidden_size,
+                                mi_dtype lora_dtype, float scale, mi_dtype out_dtype,
+                                void* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * NVFP4 GEMM with a BF16 LoRA correction (flashinfer.gemm.mm_nvfp4_lora):
+ *   raw      : out = bf16( alpha*acc + lora_scale*(d @ lora_b^T) [+ bias] )
+ *   prepared : out = bf16( alpha*(acc + d @ b_folded^T) [+ bias] )
+ *   off      : out = bf16( alpha*acc [+ bias] )
+ * acc = dequant(a) @ dequant(b)^T accumulated in fp32; one rounding to bf16.
+ *
+ *   a, b        uint8 [m, k/2], [n, k/2]: two E2M1 codes per byte, element 2i in
+ *               the low nibble
+ *   a_sf, b_sf  UE4M3 scales, one per 16 elements along k, 128x4-tiled with rows
+ *               padded to 128 (tile = 128 rows x 4 scale columns = 512 bytes,
+ *               tiles row-block major; inside: (r%32)*16 + ((r%128)/32)*4 + c%4);
+ *               a_sf_bytes / b_sf_bytes give the buffer sizes (larger is fine)
+ *   alpha       fp32 device scalar (element 0 used)
+ *   d           bf16 [m, rank] or NULL;  rank = d's column count
+ *   lora_b      raw path: bf16 [n, rank];  lora_scale fp32 device scalar.
+ *               lora_scale == NULL -> adapter off even if d / lora_b are given.
+ *               *lora_scale == 0 (read on the device) -> the adapter-off program
+ *               path, bitwise identical to the off call.
+ *   b_folded    prepared path: bf16 [n, rank] from mi_prepare_lora_fold, with its
+ *               fold_flags word; bit 0 set (zero adapter) -> the off path.
+ *   bias        bf16 [n] or NULL, added in fp32 before the single rounding
+ *   out         bf16 [m, n]
+ * Requirements: m >= 1, n >= 1, k % 256 == 0 (k >= 256); rank % 8 == 0 and
+ * 8 <= rank <= 128 when an adapter is given; not both adapter forms; a prepared
+ * adapter needs d; scale buffers large enough for the padded layout.
+ */
+MI_API mi_status mi_mm_nvfp4_lora(const uint8_t* a, const uint8_t* b,
+                           const uint8_t* a_sf, size_t a_sf_bytes,
+                           const uint8_t* b_sf, size_t b_sf_bytes,
+                           const float* alpha, int64_t m, int64_t n, int64_t k,
+                           const void* d, int64_t rank,
+                           const void* lora_b, const float* lora_scale,
+                           const void* b_folded, const uint32_t* fold_flags,
+                           const void* bias, void* out, void* stream);
+
+/*
+ * The prepared-path fold (flashinfer.gemm.prepare_nvfp4_lora_adapter):
+ *   ratio       = fp32 division, round to nearest even: *lora_scale / alpha[0]
+ *   b_folded[i] = bf16_rne(fp32(lora_b[i]) * ratio)        (IEEE, subnormals kept)
+ *   fold_flags[0] = (*lora_scale == 0) ? 1 : 0              (bit 0: zero adapter)
+ * Everything happens on the device (no host read), so the same call is the
+ * in-place refold.  alpha == 0 is NOT checked here (it folds to Inf/NaN); the
+ * eager prepare checks it with its one documented host read.
+ *   lora_b bf16 [n, rank]; b_folded bf16 [n, rank] (may not alias lora_b);
+ *   lora_scale, alpha fp32 device scalars; fold_flags uint32 [1].
+ */
+MI_API mi_status mi_prepare_lora_fold(const void* lora_b, int64_t n, int64_t rank,
+                               const float* lora_scale, const float* alpha,
+                               void* b_folded, uint32_t* fold_flags, void* stream);
+
+/*
+ * Dequantise an NVFP4 matrix with the GEMM's own in-register decoder:
+ * out[r, j] = E2M1(code[r, j]) * UE4M3(scale of (r, j/16)) as bf16 (exact).
+ *   codes uint8 [rows, k/2]; sf as for mi_mm_nvfp4_lora; out bf16 [rows, k].
+ * Requirements: rows >= 1, k % 64 == 0.
+ */
+MI_API mi_status mi_nvfp4_dequant_bf16(const uint8_t* codes, const uint8_t* sf, size_t sf_bytes,
+                                int64_t rows, int64_t k, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MI_MOE_H */

@@ -1,0 +1,70 @@
+// Shared device/host helpers for the gfx950 kernels of libmi_moe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "mi_moe.h"
+
+namespace mi {
+
+// ---------------------------------------------------------------------------
+// host-side error reporting
+// ---------------------------------------------------------------------------
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define MI_REQUIRE(cond, ...)            \
+  do {                                   \
+    if (!(cond)) {                       \
+      ::mi::set_error(__VA_ARGS__);      \
+      return MI_EINVAL;                  \
+    }                                    \
+  } while (0)
+
+#define MI_REQUIRE_SUPPORTED(cond, ...)  \
+  do {                                   \
+    if (!(cond)) {                       \
+      ::mi::set_error(__VA_ARGS__);      \
+      return MI_EUNSUPPORTED;            \
+    }                                    \
+  } while (0)
+
+mi_status launch_status(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// ---------------------------------------------------------------------------
+// device types
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// IEEE round-to-nearest-even float -> bf16 bits; NaN -> canonical 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T bitcast(const uint4& v) {
+  return __builtin_bit_cast(T, v);
+}
+
+}  // namespace mi

@@ -1,0 +1,449 @@
+// NVFP4 GEMM with a BF16 LoRA epilogue, the prepared-path fold, and the
+// NVFP4 dequantiser -- gfx950.
+//
+// What is computed (flashinfer.gemm.mm_nvfp4_lora, formula and the raw /
+// prepared bullets; flashinfer.gemm.prepare_nvfp4_lora_adapter, the fold):
+//   raw      out = bf16( alpha*acc + lora_scale*(d @ lora_b^T) [+ bias] )
+//   prepared out = bf16( alpha*(acc + d @ b_folded^T) [+ bias] )
+//   off      out = bf16( alpha*acc [+ bias] )
+// with acc = dequant(a) @ dequant(b)^T in fp32 and one final rounding.
+//
+// Decoding.  An E2M1 value (<= 2 significant bits) times a UE4M3 scale
+// (<= 4 significant bits, 2^-9 .. 448) has at most 6 significant bits and
+// lies in 2^-10 .. 2688, so it is exact in fp16.  Each byte of codes becomes
+// an fp16 pair with v_cvt_scalef32_pk_f16_fp4 at scale 1.0 (a pure format
+// conversion, exact), and one v_pk_mul_f16 by the block's scale (converted
+// exactly from its E4M3 byte) applies the scale -- exact as well.  The
+// decoded tile is written to LDS once per workgroup and feeds
+// v_mfma_f32_32x32x16_f16.  CDNA4's block-scaled MFMA takes power-of-two
+// (E8M0) scales on 32-wide blocks, so it cannot consume UE4M3 scales on
+// 16-wide blocks; this decode-to-fp16 route is exact instead.
+//
+// The LoRA term is an epilogue: after the K loop each 32x32 block gets one
+// bf16 MFMA per 16 ranks -- into the base accumulator on the prepared path,
+// into a separate fp32 accumulator on the raw path.  The adapter-off, raw
+// scale-0 and prepared zero-adapter cases all take the same epilogue code
+// with the LoRA skipped (the scale / the fold's zero flag is read on the
+// device), so their outputs are bitwise identical.  Epilogue arithmetic uses
+// explicitly rounded fp32 operations (no contraction).
+#include "common.hpp"
+
+namespace mi {
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int NV_BM = 256, NV_BN = 256, NV_BK = 64;  // BK in elements (32 code bytes)
+constexpr int NV_WM = 4, NV_WN = 2;
+constexpr int NV_NT = 64 * NV_WM * NV_WN;  // 512 threads
+constexpr int NV_GROUP_M = 4;
+
+__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// Byte offset of the UE4M3 scale of (row, scale column col) in the 128x4
+// tiled layout: 512-byte tiles of 128 rows x 4 columns, row-block major;
+// inside a tile (row%32)*16 + ((row%128)/32)*4 + col%4.  n_col_tiles =
+// ceil(k/16/4).  Columns col..col+3 with col%4 == 0 are 4 consecutive bytes.
+__device__ __forceinline__ long sf_tile_word(int row, int col4, int n_col_tiles) {
+  return (static_cast<long>(row >> 7) * n_col_tiles + col4) * 512 + (row & 31) * 16 +
+         ((row & 127) >> 5) * 4;
+}
+
+// UE4M3 byte -> fp16 pair (s, s); exact (4 significant bits, 2^-9 .. 448).
+__device__ __forceinline__ f16x2 scale_pair(uint32_t byte) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8(byte, 0);
+  const _Float16 h = static_cast<_Float16>(s);
+  return f16x2{h, h};
+}
+
+// 8 E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
+// times an fp16 scale pair -> 8 fp16 values, element order preserved.
+__device__ __forceinline__ u32x4 decode8(uint32_t w, f16x2 s) {
+  u32x4 r;
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  r.x = __builtin_bit_cast(uint32_t, p0);
+  r.y = __builtin_bit_cast(uint32_t, p1);
+  r.z = __builtin_bit_cast(uint32_t, p2);
+  r.w = __builtin_bit_cast(uint32_t, p3);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t f16_to_bf16_bits(uint32_t h) {
+  // exact: every decoded value is representable in bf16
+  const float f = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+  return __float_as_uint(f) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 GEMM + LoRA epilogue
+// ---------------------------------------------------------------------------
+struct NvArgs {
+  const uint8_t* a;
+  const uint8_t* b;
+  const uint8_t* a_sf;
+  const uint8_t* b_sf;
+  const float* alpha;
+  const uint16_t* d;
+  const uint16_t* lora_b;    // raw path
+  const float* lora_scale;   // raw path (NULL -> off)
+  const uint16_t* b_folded;  // prepared path
+  const uint32_t* fold_flags;
+  const uint16_t* bias;
+  uint16_t* out;
+  int m, n, k, rank;
+  int mode;  // 0 off, 1 raw, 2 prepared
+};
+
+__global__ __launch_bounds__(NV_NT) void nvfp4_lora_kernel(NvArgs p) {
+  constexpr int WTM = NV_BM / NV_WM, WTN = NV_BN / NV_WN;  // 64 x 128
+  constexpr int FM = WTM / 32, FN = WTN / 32;               // 2 x 4
+  constexpr int STAGE = (NV_BM + NV_BN) * NV_BK;            // fp16 elements
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NV_WN, wn = wave % NV_WN;
+
+  // ---- tile order: XCD-contiguous runs, GROUP_M m-tiles per n sweep ----
+  const int mt = (p.m + NV_BM - 1) / NV_BM, ntile = (p.n + NV_BN - 1) / NV_BN;
+  const int total = mt * ntile;
+  const int G = gridDim.x;  // == total rounded up to a multiple of 8
+  const int L = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  if (L >= total) return;
+  const int span = NV_GROUP_M * ntile;
+  const int grp = L / span, first = grp * NV_GROUP_M;
+  const int gsize = min(mt - first, NV_GROUP_M);
+  const int in_grp = L - grp * span;
+  const int m0 = (first + in_grp % gsize) * NV_BM;
+  const int n0 = (in_grp / gsize) * NV_BN;
+
+  // ---- per-thread load coordinates: thread t owns row t/2, code half t%2 ----
+  const int lrow = tid >> 1, half = tid & 1;
+  const int arow = min(m0 + lrow, p.m - 1);
+  const int brow = min(n0 + lrow, p.n - 1);
+  const long kb = p.k / 2;  // code bytes per row
+  const uint8_t* a_codes = p.a + static_cast<long>(arow) * kb + half * 16;
+  const uint8_t* b_codes = p.b + static_cast<long>(brow) * kb + half * 16;
+  const int n_col_tiles = (p.k / 16 + 3) / 4;
+  const uint8_t* a_sfw = p.a_sf + sf_tile_word(arow, 0, n_col_tiles);
+  const uint8_t* b_sfw = p.b_sf + sf_tile_word(brow, 0, n_col_tiles);
+  // LDS chunk positions of this thread's 4 chunks (k chunks half*4 .. half*4+3)
+  int lds_off[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) lds_off[c] = lrow * NV_BK + (((half * 4 + c) ^ lds_swz(lrow)) << 3);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  u32x4 ca, cb;       // 32 codes of A / B
+  uint32_t sa, sb;    // the row's 4 scale bytes of this K step
+
+  auto gload = [&](int kt) {
+    ca = *reinterpret_cast<const u32x4*>(a_codes + kt * (NV_BK / 2));
+    cb = *reinterpret_cast<const u32x4*>(b_codes + kt * (NV_BK / 2));
+    sa = *reinterpret_cast<const uint32_t*>(a_sfw + static_cast<long>(kt) * 512);
+    sb = *reinterpret_cast<const uint32_t*>(b_sfw + static_cast<long>(kt) * 512);
+  };
+  auto decode_store = [&](int buf) {
+    uint16_t* sA = smem + buf * STAGE;
+    uint16_t* sB = sA + NV_BM * NV_BK;
+    // this half covers scale columns 2*half and 2*half+1 of the step
+    const f16x2 sa0 = scale_pair((sa >> (16 * half)) & 0xff);
+    const f16x2 sa1 = scale_pair((sa >> (16 * half + 8)) & 0xff);
+    const f16x2 sb0 = scale_pair((sb >> (16 * half)) & 0xff);
+    const f16x2 sb1 = scale_pair((sb >> (16 * half + 8)) & 0xff);
+    *reinterpret_cast<u32x4*>(sA + lds_off[0]) = decode8(ca.x, sa0);
+    *reinterpret_cast<u32x4*>(sA + lds_off[1]) = decode8(ca.y, sa0);
+    *reinterpret_cast<u32x4*>(sA + lds_off[2]) = decode8(ca.z, sa1);
+    *reinterpret_cast<u32x4*>(sA + lds_off[3]) = decode8(ca.w, sa1);
+    *reinterpret_cast<u32x4*>(sB + lds_off[0]) = decode8(cb.x, sb0);
+    *reinterpret_cast<u32x4*>(sB + lds_off[1]) = decode8(cb.y, sb0);
+    *reinterpret_cast<u32x4*>(sB + lds_off[2]) = decode8(cb.z, sb1);
+    *reinterpret_cast<u32x4*>(sB + lds_off[3]) = decode8(cb.w, sb1);
+  };
+
+  const int KT = p.k / NV_BK;
+  gload(0);
+  decode_store(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    const uint16_t* sA = smem + cur * STAGE;
+    const uint16_t* sB = sA + NV_BM * NV_BK;
+#pragma unroll
+    for (int s = 0; s < NV_BK / 16; ++s) {
+      const int kc = 2 * s + (lane >> 5);
+      f16x8 fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        fa[i] = *reinterpret_cast<const f16x8*>(sA + r * NV_BK + ((kc ^ lds_swz(r)) << 3));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WTN + j * 32 + (lane & 31);
+        fb[j] = *reinterpret_cast<const f16x8*>(sB + r * NV_BK + ((kc ^ lds_swz(r)) << 3));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) decode_store(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  const float alpha = p.alpha[0];
+  bool lora = false;
+  float s_lora = 0.f;
+  const uint16_t* lb = nullptr;
+  if (p.mode == 1) {
+    s_lora = p.lora_scale[0];
+    lora = (s_lora != 0.f);
+    lb = p.lora_b;
+  } else if (p.mode == 2) {
+    lora = (p.fold_flags[0] & 1u) == 0u;
+    lb = p.b_folded;
+  }
+  const int kl = lane >> 5;  // which 8-rank half of a 16-rank step this lane feeds
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int rbase = m0 + wm * WTM + i * 32;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int cbase = n0 + wn * WTN + j * 32;
+      f32x16 accl;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) accl[q] = 0.f;
+      if (lora) {
+        // d rows rbase..+31 (clamped), lb rows cbase..+31 (clamped); K = rank
+        const int dr = min(rbase + (lane & 31), p.m - 1);
+        const int br = min(cbase + (lane & 31), p.n - 1);
+        const uint16_t* dp = p.d + static_cast<long>(dr) * p.rank + kl * 8;
+        const uint16_t* bp = lb + static_cast<long>(br) * p.rank + kl * 8;
+        if (p.mode == 2) {
+          for (int r0 = 0; r0 < p.rank; r0 += 16) {
+            u32x4 fd = {0, 0, 0, 0}, fl = {0, 0, 0, 0};
+            if (r0 + kl * 8 < p.rank) {
+              fd = *reinterpret_cast<const u32x4*>(dp + r0);
+              fl = *reinterpret_cast<const u32x4*>(bp + r0);
+            }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, fd), __builtin_bit_cast(bf16x8, fl), acc[i][j], 0, 0, 0);
+          }
+        } else {
+          for (int r0 = 0; r0 < p.rank; r0 += 16) {
+            u32x4 fd = {0, 0, 0, 0}, fl = {0, 0, 0, 0};
+            if (r0 + kl * 8 < p.rank) {
+              fd = *reinterpret_cast<const u32x4*>(dp + r0);
+              fl = *reinterpret_cast<const u32x4*>(bp + r0);
+            }
+            accl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, fd), __builtin_bit_cast(bf16x8, fl), accl, 0, 0, 0);
+          }
+        }
+      }
+      const int col = cbase + (lane & 31);
+      if (col < p.n) {
+        const bool has_bias = p.bias != nullptr;
+        const float bv = has_bias ? bf16_bits_to_f32(p.bias[col]) : 0.f;
+        const bool raw_lora = lora && p.mode == 1;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = rbase + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+          if (row < p.m) {
+            float v = __fmul_rn(alpha, acc[i][j][q]);
+            if (raw_lora) v = __fadd_rn(v, __fmul_rn(s_lora, accl[q]));
+            if (has_bias) v = __fadd_rn(v, bv);
+            p.out[static_cast<long>(row) * p.n + col] = static_cast<uint16_t>(f32_to_bf16_rne(v));
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fold: b_folded = bf16_rne(fp32(lora_b) * (lora_scale / alpha)), flag
+// ---------------------------------------------------------------------------
+__global__ void fold_kernel(const uint16_t* __restrict__ lora_b, long count,
+                            const float* __restrict__ lora_scale, const float* __restrict__ alpha,
+                            uint16_t* __restrict__ b_folded, uint32_t* __restrict__ flags) {
+  const float s = lora_scale[0];
+  const float ratio = __fdiv_rn(s, alpha[0]);  // IEEE division, round to nearest even
+  const long i0 = (static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+  if (i0 == 0) flags[0] = (s == 0.f) ? 1u : 0u;
+  if (i0 >= count) return;
+  if (i0 + 8 <= count) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lora_b + i0);
+    u32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float lo = __fmul_rn(bf16_bits_to_f32(v[c] & 0xffffu), ratio);
+      const float hi = __fmul_rn(bf16_bits_to_f32(v[c] >> 16), ratio);
+      o[c] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    }
+    *reinterpret_cast<u32x4*>(b_folded + i0) = o;
+  } else {
+    for (long i = i0; i < count; ++i)
+      b_folded[i] =
+          static_cast<uint16_t>(f32_to_bf16_rne(__fmul_rn(bf16_bits_to_f32(lora_b[i]), ratio)));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dequant: one thread per 8 codes of one row, the GEMM's decoder
+// ---------------------------------------------------------------------------
+__global__ void dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sf,
+                               int rows, int k, uint16_t* __restrict__ out) {
+  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int words = k / 8;
+  if (idx >= static_cast<long>(rows) * words) return;
+  const int row = static_cast<int>(idx / words), w = static_cast<int>(idx % words);
+  const int col = w / 2;  // 8 elements per word, 16 per scale
+  const int n_col_tiles = (k / 16 + 3) / 4;
+  const uint32_t sbyte = sf[sf_tile_word(row, col >> 2, n_col_tiles) + (col & 3)];
+  const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + static_cast<long>(row) * (k / 2) + w * 4);
+  const u32x4 h = decode8(cw, scale_pair(sbyte));
+  u32x4 o;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    o[c] = f16_to_bf16_bits(h[c] & 0xffffu) | (f16_to_bf16_bits(h[c] >> 16) << 16);
+  *reinterpret_cast<u32x4*>(out + static_cast<long>(row) * k + w * 8) = o;
+}
+
+size_t sf_needed(int64_t rows, int64_t k) {
+  return static_cast<size_t>((rows + 127) / 128) * static_cast<size_t>((k / 16 + 3) / 4) * 512;
+}
+
+}  // namespace
+}  // namespace mi
+
+extern "C" mi_status mi_mm_nvfp4_lora(const uint8_t* a, const uint8_t* b, const uint8_t* a_sf,
+                                      size_t a_sf_bytes, const uint8_t* b_sf, size_t b_sf_bytes,
+                                      const float* alpha, int64_t m, int64_t n, int64_t k,
+                                      const void* d, int64_t rank, const void* lora_b,
+                                      const float* lora_scale, const void* b_folded,
+                                      const uint32_t* fold_flags, const void* bias, void* out,
+                                      void* stream) {
+  using namespace mi;
+  clear_error();
+  MI_REQUIRE(m >= 1, "mm_nvfp4_lora: M >= 1 required (got %lld)", (long long)m);
+  MI_REQUIRE(n >= 1, "mm_nvfp4_lora: N >= 1 required (got %lld)", (long long)n);
+  MI_REQUIRE(k >= 256 && k % 256 == 0, "mm_nvfp4_lora: K must be a multiple of 256 (got %lld)",
+             (long long)k);
+  MI_REQUIRE(m < (1LL << 31) && n < (1LL << 31) && k < (1LL << 31) && m * n < (1LL << 40),
+             "mm_nvfp4_lora: shape too large");
+  MI_REQUIRE(a && b && a_sf && b_sf && alpha && out, "mm_nvfp4_lora: a, b, a_sf, b_sf, alpha and "
+             "out must be non-null");
+  MI_REQUIRE(a_sf_bytes >= sf_needed(m, k),
+             "mm_nvfp4_lora: a_sf holds %zu bytes, the 128x4 layout needs %zu", a_sf_bytes,
+             sf_needed(m, k));
+  MI_REQUIRE(b_sf_bytes >= sf_needed(n, k),
+             "mm_nvfp4_lora: b_sf holds %zu bytes, the 128x4 layout needs %zu", b_sf_bytes,
+             sf_needed(n, k));
+  const bool raw = lora_b != nullptr || lora_scale != nullptr;
+  const bool prepared = b_folded != nullptr;
+  MI_REQUIRE(!(raw && prepared),
+             "mm_nvfp4_lora: pass either the raw adapter (lora_b, lora_scale) or the prepared "
+             "adapter, not both");
+  int mode = 0;
+  if (prepared) {
+    MI_REQUIRE(d != nullptr, "mm_nvfp4_lora: the prepared path requires d");
+    MI_REQUIRE(fold_flags != nullptr, "mm_nvfp4_lora: the prepared adapter needs its fold flags");
+    mode = 2;
+  } else if (lora_scale != nullptr) {  // lora_scale NULL disables the adapter
+    MI_REQUIRE(d != nullptr && lora_b != nullptr,
+               "mm_nvfp4_lora: the raw path needs d and lora_b with lora_scale");
+    mode = 1;
+  }
+  if (mode != 0) {
+    MI_REQUIRE(rank >= 8 && rank <= 128 && rank % 8 == 0,
+               "mm_nvfp4_lora: LoRA rank must be a multiple of 8 in [8, 128] (got %lld)",
+               (long long)rank);
+    MI_REQUIRE(aligned16(d) && aligned16(mode == 1 ? lora_b : b_folded),
+               "mm_nvfp4_lora: d and lora_b rows must be 16-byte aligned");
+  }
+  MI_REQUIRE(aligned16(a) && aligned16(b), "mm_nvfp4_lora: a and b must be 16-byte aligned");
+  MI_REQUIRE((reinterpret_cast<uintptr_t>(a_sf) & 3) == 0 &&
+                 (reinterpret_cast<uintptr_t>(b_sf) & 3) == 0,
+             "mm_nvfp4_lora: scale buffers must be 4-byte aligned");
+
+  NvArgs args;
+  args.a = a;
+  args.b = b;
+  args.a_sf = a_sf;
+  args.b_sf = b_sf;
+  args.alpha = alpha;
+  args.d = static_cast<const uint16_t*>(d);
+  args.lora_b = static_cast<const uint16_t*>(lora_b);
+  args.lora_scale = lora_scale;
+  args.b_folded = static_cast<const uint16_t*>(b_folded);
+  args.fold_flags = fold_flags;
+  args.bias = static_cast<const uint16_t*>(bias);
+  args.out = static_cast<uint16_t*>(out);
+  args.m = static_cast<int>(m);
+  args.n = static_cast<int>(n);
+  args.k = static_cast<int>(k);
+  args.rank = static_cast<int>(rank);
+  args.mode = mode;
+  const long tiles = ((m + NV_BM - 1) / NV_BM) * ((n + NV_BN - 1) / NV_BN);
+  const long grid = ((tiles + 7) / 8) * 8;
+  hipLaunchKernelGGL(nvfp4_lora_kernel, dim3(grid), dim3(NV_NT), 0,
+                     static_cast<hipStream_t>(stream), args);
+  return launch_status("mm_nvfp4_lora");
+}
+
+extern "C" mi_status mi_prepare_lora_fold(const void* lora_b, int64_t n, int64_t rank,
+                                          const float* lora_scale, const float* alpha,
+                                          void* b_folded, uint32_t* fold_flags, void* stream) {
+  using namespace mi;
+  clear_error();
+  MI_REQUIRE(n >= 1 && rank >= 1, "prepare_lora_fold: N and rank must be >= 1");
+  MI_REQUIRE(lora_b && lora_scale && alpha && b_folded && fold_flags,
+             "prepare_lora_fold: null pointer argument");
+  MI_REQUIRE(lora_b != b_folded, "prepare_lora_fold: b_folded may not alias lora_b");
+  MI_REQUIRE(aligned16(lora_b) && aligned16(b_folded),
+             "prepare_lora_fold: lora_b and b_folded must be 16-byte aligned");
+  const long count = n * rank;
+  const long threads = (count + 7) / 8;
+  const int block = 256;
+  const long grid = (threads + block - 1) / block;
+  hipLaunchKernelGGL(fold_kernel, dim3(grid), dim3(block), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(lora_b), count, lora_scale, alpha,
+                     static_cast<uint16_t*>(b_folded), fold_flags);
+  return launch_status("prepare_lora_fold");
+}
+
+extern "C" mi_status mi_nvfp4_dequant_bf16(const uint8_t* codes, const uint8_t* sf,
+                                           size_t sf_bytes, int64_t rows, int64_t k, void* out,
+                                           void* stream) {
+  using namespace mi;
+  clear_error();
+  MI_REQUIRE(rows >= 1 && rows < (1LL << 31), "nvfp4_dequant: rows must be >= 1");
+  MI_REQUIRE(k >= 64 && k % 64 == 0 && k < (1LL << 31), "nvfp4_dequant: K %% 64 == 0 required");
+  MI_REQUIRE(codes && sf && out, "nvfp4_dequant: null pointer argument");
+  MI_REQUIRE(sf_bytes >= sf_needed(rows, k), "nvfp4_dequant: scale buffer too small");
+  MI_REQUIRE(aligned16(out) && (reinterpret_cast<uintptr_t>(codes) & 3) == 0,
+             "nvfp4_dequant: misaligned buffers");
+  const long threads = rows * (k / 8);
+  const int block = 256;
+  hipLaunchKernelGGL(dequant_kernel, dim3((threads + block - 1) / block), dim3(block), 0,
+                     static_cast<hipStream_t>(stream), codes, sf, static_cast<int>(rows),
+                     static_cast<int>(k), static_cast<uint16_t*>(out));
+  return launch_status("nvfp4_dequant");
+}

@@ -21,6 +21,7 @@ import torch
 __all__ = [
     "gen",
     "bf16_normal",
+    "bf16_ints",
     "route",
     "zipf_counts",
     "sf_buffer_bytes",

@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects invalid arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_expert_grouped_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", f)).read()
+            names |= set(re.findall(r"MI_API\s+[\w\s\*]+?\b(mi_\w+)\s*\(", txt))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    syms = header_symbols()
+    assert syms == set(_lib.EXPORTS)
+    for s in syms:
+        assert hasattr(L, s), s
+    assert L.mi_abi_version() == 1
+
+
+def _err(status):
+    with pytest.raises(ValueError) as ei:
+        _lib.check(status)
+    return str(ei.value)
+
+
+NULL = None
+FAKE = 0x100000  # never dereferenced: validation fails before any launch
+
+
+def test_grouped_mm_validation():
+    L = _lib.lib()
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, FAKE, 2, 100, FAKE, FAKE, _lib.MI_BF16, NULL))
+    assert "n % 256" in msg
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 96, FAKE, 2, 256, FAKE, FAKE, _lib.MI_BF16, NULL))
+    assert "k % 64" in msg
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, FAKE, 0, 256, FAKE, FAKE, _lib.MI_BF16, NULL))
+    assert "batch_size" in msg
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, FAKE, 2, 256, NULL, FAKE, _lib.MI_BF16, NULL))
+    assert "m_indptr" in msg
+    with pytest.raises(NotImplementedError):
+        _lib.check(L.mi_grouped_mm_bf16(FAKE, 64, 64, FAKE, 2, 256, FAKE, FAKE, _lib.MI_F16,
+                                        NULL))
+    # an empty a is a no-op that returns before touching the device
+    assert L.mi_grouped_mm_bf16(NULL, 0, 64, FAKE, 2, 256, FAKE, NULL, _lib.MI_BF16, NULL) == 0
+
+
+def _nv(**kw):
+    args = dict(a=FAKE, b=FAKE, a_sf=FAKE, a_sf_bytes=1 << 30, b_sf=FAKE, b_sf_bytes=1 << 30,
+                alpha=FAKE, m=128, n=256, k=512, d=NULL, rank=0, lora_b=NULL, lora_scale=NULL,
+                b_folded=NULL, fold_flags=NULL, bias=NULL, out=FAKE, stream=NULL)
+    args.update(kw)
+    return _lib.lib().mi_mm_nvfp4_lora(*args.values())
+
+
+def test_nvfp4_validation_names_the_rule():
+    assert "multiple of 256" in _err(_nv(k=320))
+    assert "M >= 1" in _err(_nv(m=0))
+    assert "N >= 1" in _err(_nv(n=0))
+    both = _err(_nv(d=FAKE, rank=16, lora_b=FAKE, lora_scale=FAKE, b_folded=FAKE,
+                    fold_flags=FAKE))
+    assert "not both" in both
+    assert "requires d" in _err(_nv(b_folded=FAKE, fold_flags=FAKE, rank=16))
+    assert "rank" in _err(_nv(d=FAKE, rank=12, lora_b=FAKE, lora_scale=FAKE))
+    assert "a_sf holds" in _err(_nv(a_sf_bytes=100))
+
+
+def test_fold_and_dequant_validation():
+    L = _lib.lib()
+    assert "null" in _err(L.mi_prepare_lora_fold(NULL, 16, 16, FAKE, FAKE, FAKE, FAKE, NULL))
+    assert "alias" in _err(L.mi_prepare_lora_fold(FAKE, 16, 16, FAKE, FAKE, FAKE, FAKE, NULL))
+    assert "K % 64" in _err(L.mi_nvfp4_dequant_bf16(FAKE, FAKE, 1 << 20, 4, 96, FAKE, NULL))
+
+
+def _delta(**kw):
+    args = dict(act=FAKE, padded_rows=64, inter=128, perm=FAKE, wa=FAKE, sa=1024, wb=FAKE,
+                sb=1024, ids=FAKE, w=FAKE, lids=FAKE, T=16, k=2, E=4, L=2, r=16, H=256,
+                ldt=_lib.MI_BF16, scale=2.0, odt=_lib.MI_BF16, out=FAKE, ws=FAKE,
+                wsb=1 << 30, stream=NULL)
+    args.update(kw)
+    return _lib.lib().mi_moe_fc2_lora_delta(*args.values())
+
+
+def test_delta_validation():
+    assert "rank" in _err(_delta(r=12))
+    assert "top_k" in _err(_delta(k=0))
+    assert "workspace" in _err(_delta(wsb=16))
+    assert "strides" in _err(_delta(sa=1001))
+    with pytest.raises(NotImplementedError):
+        _lib.check(_delta(H=200))
+    with pytest.raises(NotImplementedError):
+        _lib.check(_delta(ldt=_lib.MI_F16))
+    L = _lib.lib()
+    assert L.mi_moe_fc2_lora_delta_workspace_size(8192, 8, 64, 8, 16) > 8192 * 8 * 16 * 4
+    assert L.mi_moe_fc2_lora_delta_workspace_size(8, 0, 4, 2, 8) == 0

@@ -1,0 +1,136 @@
+"""GPU parity of the FC2 MoE LoRA delta against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from moe_expert_grouped_amd import bgmv_moe_gemm2_lora_delta
+from oracle.formats import f64_to_bf16_bits
+from oracle.lora_delta import moe_fc2_lora_delta
+from tests.delta_helpers import contiguous_tables, oracle_bank, scattered_bank
+from tests.parity import bits16, check_close, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(case, dev):
+    return synth.DeltaCase(case.name, case.act.to(dev), case.perm.to(dev), case.A.to(dev),
+                           case.B.to(dev), case.topk_ids.to(dev), case.topk_weights.to(dev),
+                           case.lora_ids.to(dev), case.scale, case.extra)
+
+
+def tables(case, scattered=False):
+    """(flatA, w_ptr_a, stride_a, flatB, w_ptr_b, stride_b); banks on the case's device."""
+    if scattered:
+        fa, wa, sa = scattered_bank(case.A, seed=3)
+        fb, wb, sb = scattered_bank(case.B, seed=4)
+        return fa, wa, sa, fb, wb, sb
+    wa, sa = contiguous_tables(case.A)
+    wb, sb = contiguous_tables(case.B)
+    return case.A, wa, sa, case.B, wb, sb
+
+
+def run_gpu(case, tb, out_dtype=torch.bfloat16, **over):
+    fa, wa, sa, fb, wb, sb = tb
+    kw = dict(perm=case.perm, topk_ids=case.topk_ids, topk_weights=case.topk_weights,
+              lora_ids=case.lora_ids, scale=case.scale)
+    kw.update(over)
+    dev = case.act.device
+    out = bgmv_moe_gemm2_lora_delta(case.act, kw["perm"], wa.to(dev), sa, wb.to(dev), sb,
+                                    kw["topk_ids"], kw["topk_weights"], kw["lora_ids"], case.rank,
+                                    case.H, num_adapters=case.L, scale=kw["scale"],
+                                    out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_oracle(case, tb, tokens=None, **over):
+    fa, wa, sa, fb, wb, sb = tb
+    kw = dict(perm=case.perm, topk_ids=case.topk_ids, topk_weights=case.topk_weights,
+              lora_ids=case.lora_ids, scale=case.scale)
+    kw.update(over)
+    c = lambda t: t.detach().cpu().numpy()
+    return moe_fc2_lora_delta(bits16(case.act), c(kw["perm"]), oracle_bank(fa), c(wa), sa,
+                              oracle_bank(fb), c(wb), sb, c(kw["topk_ids"]), c(kw["topk_weights"]),
+                              c(kw["lora_ids"]), case.rank, case.H, kw["scale"], tokens=tokens)
+
+
+def test_tiny(gpu):
+    case = to_dev(synth.delta_tiny(), gpu)
+    tb = tables(case)
+    out = run_gpu(case, tb)
+    check_close(to_f64(out), run_oracle(case, tb), "tiny delta")
+    no = (case.lora_ids < 0).cpu().numpy()
+    assert not bits16(out)[no].any(), "tokens without adapter must be +0"
+
+
+@pytest.mark.parametrize("r,I,H", [(16, 64, 256), (8, 200, 128), (32, 96, 384), (24, 128, 256)])
+def test_integer_probe_bitwise_scattered_bank(gpu, r, I, H):
+    case = to_dev(synth.delta_int_probe(r=r, I=I, H=H), gpu)
+    tb = tables(case, scattered=True)
+    out = run_gpu(case, tb)
+    ref = run_oracle(case, tb)
+    assert np.array_equal(bits16(out), f64_to_bf16_bits(ref))
+    out32 = run_gpu(case, tb, torch.float32)
+    assert np.array_equal(to_f64(out32), ref)
+
+
+def test_all_inactive_and_no_adapter_give_plus_zero(gpu):
+    case = to_dev(synth.delta_tiny(seed=3), gpu)
+    tb = tables(case)
+    z = run_gpu(case, tb, lora_ids=torch.full_like(case.lora_ids, -1))
+    assert not bits16(z).any()
+    z = run_gpu(case, tb, perm=torch.full_like(case.perm, -1))
+    assert not bits16(z).any()
+
+
+def test_out_of_range_ids_are_inactive(gpu):
+    case = to_dev(synth.delta_int_probe(seed=105), gpu)
+    tb = tables(case)
+    lids = case.lora_ids.clone()
+    lids[::3] = case.L + 2                      # adapter id past the bank
+    perm = case.perm.clone()
+    perm[1::5] = case.act.shape[0] + 10         # row past padded_rows
+    out = run_gpu(case, tb, lora_ids=lids, perm=perm)
+    ref = run_oracle(case, tb, lora_ids=torch.where(lids >= case.L, -1, lids),
+                     perm=torch.where(perm >= case.act.shape[0], -1, perm))
+    assert np.array_equal(bits16(out), f64_to_bf16_bits(ref))
+
+
+def test_scale_doubling_is_exact(gpu):
+    case = to_dev(synth.delta_tiny(seed=5), gpu)
+    tb = tables(case)
+    o1 = run_gpu(case, tb, torch.float32, scale=1.5)
+    o2 = run_gpu(case, tb, torch.float32, scale=3.0)
+    assert torch.equal(o1 * 2, o2)
+
+
+def test_deterministic(gpu):
+    case = to_dev(synth.delta_at_scale(T=1024, E=16, I=512, H=1024, L=4), gpu)
+    tb = tables(case)
+    o1 = run_gpu(case, tb)
+    o2 = run_gpu(case, tb)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_medium_random(gpu):
+    case = to_dev(synth.delta_at_scale(seed=9, T=512, top_k=4, E=12, I=256, H=512, L=3), gpu)
+    tb = tables(case)
+    out = run_gpu(case, tb)
+    check_close(to_f64(out), run_oracle(case, tb), "medium delta")
+
+
+@pytest.mark.slow
+def test_at_scale_sampled(gpu):
+    """T=8192, top_k=8, E=64, I=2048, H=4096, 8 adapters of rank 16 (the
+    bench's launch), checked on sampled tokens (all columns)."""
+    case = synth.delta_at_scale(device=gpu)
+    tb = tables(case)
+    out = run_gpu(case, tb)
+    rng = np.random.default_rng(2)
+    toks = np.sort(rng.choice(case.T, 48, replace=False)).tolist()
+    ref = run_oracle(case, tb, tokens=toks)
+    idx = torch.tensor(toks, device=gpu)
+    check_close(to_f64(out.index_select(0, idx)), ref, "delta at scale (sampled tokens)")
+    out2 = run_gpu(case, tb)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))

@@ -1,0 +1,118 @@
+"""GPU parity of the ragged grouped GEMM against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from moe_expert_grouped_amd import grouped_mm_bf16
+from oracle.formats import f64_to_bf16_bits
+from oracle.grouped_mm import grouped_mm, grouped_mm_rows
+from tests.parity import bits16, check_close, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, dev, out_dtype=torch.bfloat16, out=None):
+    a, b, mi = case.a.to(dev), case.b.to(dev), case.m_indptr.to(dev)
+    o = grouped_mm_bf16(a, b, mi, out=out, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o
+
+
+def _oracle(case):
+    return grouped_mm(bits16(case.a), bits16(case.b), case.m_indptr.numpy())
+
+
+def test_tiny_moe_fc2(gpu):
+    case = synth.grouped_tiny()
+    ref, written = _oracle(case)
+    out = _run(case, gpu)
+    check_close(to_f64(out)[written], ref[written], "tiny grouped GEMM")
+
+
+@pytest.mark.parametrize("counts,n,k", [
+    ((0, 1, 17, 128, 0, 255), 256, 128),          # small groups: 64x64 tiles
+    ((100, 0, 150, 177, 0, 229), 512, 192),       # medium: 128x64 tiles
+    ((300, 0, 513, 1, 256, 0, 390), 256, 256),    # large: 256x256 tiles, ragged tails
+])
+def test_integer_probe_bitwise(gpu, counts, n, k):
+    case = synth.grouped_int_probe(counts=counts, n=n, k=k)
+    ref, written = _oracle(case)
+    out = _run(case, gpu)
+    want = f64_to_bf16_bits(ref[written])
+    got = bits16(out)[written]
+    assert np.array_equal(got, want)
+    out32 = _run(case, gpu, torch.float32)
+    assert np.array_equal(to_f64(out32)[written], ref[written])
+
+
+def test_rows_outside_groups_untouched(gpu):
+    base = synth.grouped_int_probe(counts=(5, 0, 40), n=256, k=64)
+    cum = base.a.shape[0]
+    a = synth.bf16_ints((3 + cum + 7, 64), -3, 3, synth.gen(5))
+    case = synth.GroupedCase("offset", a, base.b, base.m_indptr + 3)  # 3 leading, 7 trailing rows
+    sentinel = torch.full((a.shape[0], 256), -7.0, dtype=torch.bfloat16, device=gpu)
+    out = _run(case, gpu, out=sentinel)
+    ref, written = _oracle(case)
+    assert not written[:3].any() and not written[-7:].any() and written[3:3 + cum].all()
+    assert (to_f64(out)[~written] == -7.0).all()
+    assert np.array_equal(bits16(out)[written], f64_to_bf16_bits(ref[written]))
+
+
+def test_uniform_full_size_bf16_and_fp32(gpu):
+    case = synth.grouped_uniform(device="cpu")
+    ref, written = _oracle(case)
+    for dt in (torch.bfloat16, torch.float32):
+        out = _run(case, gpu, dt)
+        check_close(to_f64(out), ref, f"uniform E=8 tpe=128 k=4096 n=2048 {dt}")
+
+
+def test_random_ragged_shapes_all_tile_configs(gpu):
+    g = np.random.default_rng(7)
+    for avg in (40, 130, 400):
+        E = 9
+        counts = g.integers(0, 2 * avg, E)
+        counts[g.integers(0, E)] = 0
+        mi = torch.zeros(E + 1, dtype=torch.int32)
+        mi[1:] = torch.from_numpy(np.cumsum(counts)).to(torch.int32)
+        gg = synth.gen(int(avg))
+        a = synth.bf16_normal((int(mi[-1]), 320), 1.0, gg)
+        b = synth.bf16_normal((E, 768, 320), 320 ** -0.5, gg)
+        case = synth.GroupedCase(f"avg{avg}", a, b, mi)
+        ref, written = _oracle(case)
+        out = _run(case, gpu)
+        check_close(to_f64(out)[written], ref[written], f"ragged avg={avg}")
+
+
+@pytest.mark.slow
+def test_zipf_full_size_sampled(gpu):
+    """Full-size skewed MoE FC2 (E=128, cum_m=32768, k=2048, n=7168) checked
+    on sampled rows (first/last row of every non-empty expert plus random
+    rows) and sampled columns, in the launch configuration the bench times."""
+    case = synth.grouped_zipf(device=gpu)
+    out = grouped_mm_bf16(case.a, case.b, case.m_indptr)
+    out2 = grouped_mm_bf16(case.a, case.b, case.m_indptr)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    mi = case.m_indptr.cpu().numpy()
+    rng = np.random.default_rng(0)
+    rows = set()
+    for e in range(len(mi) - 1):
+        if mi[e + 1] > mi[e]:
+            rows.update({int(mi[e]), int(mi[e + 1]) - 1})
+    rows.update(rng.integers(0, int(mi[-1]), 32).tolist())
+    rows = sorted(rows)
+    cols = np.sort(rng.choice(7168, 96, replace=False))
+    a_rows = bits16(case.a[rows])
+    colt = torch.from_numpy(cols).to(gpu)
+    ref = grouped_mm_rows(a_rows, lambda e, c: bits16(case.b[e].index_select(0, colt)), mi, rows,
+                          cols)
+    got = to_f64(out[rows][:, colt])
+    check_close(got, ref, "zipf sampled")
+
+
+def test_deterministic(gpu):
+    case = synth.grouped_int_probe(counts=(300, 0, 513, 1), n=512, k=256, lo=-100, hi=100)
+    o1 = _run(case, gpu)
+    o2 = _run(case, gpu)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
