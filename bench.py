@@ -1,0 +1,290 @@
+"""Benchmark of the routed-MoE hot path on one MI355X.
+
+One step is one pass over every operation of the path, each on its own
+synthetic workload, inputs resident in HBM:
+
+  1. grouped GEMM   -- uniform MoE: E=8 experts x 128 rows, k=4096, n=2048,
+                       bf16 out (the grouped_mm_bf16 example shape)
+  2. LoRA delta     -- T=8192 tokens, top_k=8, E=64, I=2048, H=4096,
+                       8 adapters of rank 16, 10% inactive slots
+  3. fold           -- lora_b [8192, 16] for the prepared path
+  4. NVFP4 raw      -- M=4096, N=8192, K=8192, r=16, with bias
+  5. NVFP4 prepared -- the same call on the folded adapter
+
+Prints one JSON line.  ``value`` is the whole step's algorithmic TFLOP/s;
+``ops`` carries each operation's own figures (TFLOP/s and % of the bf16 MFMA
+peak for the GEMMs, GB/s and % of HBM peak for the delta).  Op times come
+from HIP events recorded on the stream the library launches on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "grouped-GEMM TFLOP/s (% bf16 MFMA peak); LoRA-delta GB/s (% HBM peak)"
+PEAK_MFMA_TFLOPS = 2516.6   # bf16 / fp16 dense MFMA, MI355X
+PEAK_HBM_GBPS = 8000.0      # HBM3E
+KERNEL_SRC = os.path.join(ROOT, "moe_expert_grouped_amd", "csrc", "nvfp4_lora.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "nvfp4_lora_kernel_m4096_n8192_k8192_traffic.txt")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default="", help="comma list of ops to run (profiling aid)")
+    return p.parse_args()
+
+
+def src_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the NVFP4 kernel from the committed PMC summary,
+    or None when the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != src_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (the path is "
+                                   "data-parallel per GPU, see the sharding notes)"}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    import moe_expert_grouped_amd as mi
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    only = set(filter(None, args.only.split(",")))
+
+    # ---------------- inputs (resident in HBM before timing) ----------------
+    g2 = synth.grouped_uniform(device=dev)
+    out2 = torch.empty((g2.a.shape[0], g2.b.shape[1]), dtype=torch.bfloat16, device=dev)
+    dc = synth.delta_at_scale(device=dev)
+    wa, wb = mi.fill_w_ptr(dc.A), mi.fill_w_ptr(dc.B)
+    sa = dc.E * dc.rank * dc.I
+    sb = dc.E * dc.H * dc.rank
+    dout = torch.empty((dc.T, dc.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mi.delta_workspace_bytes(dc.T, dc.top_k, dc.E, dc.L, dc.rank),
+                     dtype=torch.uint8, device=dev)
+    nc = synth.nvfp4_lora_case(device=dev)
+    nout_raw = torch.empty((nc.M, nc.N), dtype=torch.bfloat16, device=dev)
+    nout_prep = torch.empty_like(nout_raw)
+    adapter = mi.prepare_nvfp4_lora_adapter(nc.lora_b, nc.lora_scale, nc.alpha)
+
+    # ---------------- algorithmic work per op ----------------
+    mi2 = g2.m_indptr.cpu().numpy()
+    cum_m, k2, n2, E2 = g2.a.shape[0], g2.a.shape[1], g2.b.shape[1], g2.b.shape[0]
+    gemm_flops = 2.0 * n2 * k2 * cum_m
+    gemm_bytes = 2.0 * cum_m * k2 + 2.0 * n2 * k2 * int((np.diff(mi2) > 0).sum()) + \
+        2.0 * cum_m * n2 + 4 * (E2 + 1)
+    perm = dc.perm.cpu().numpy().reshape(dc.T, dc.top_k)
+    lids = dc.lora_ids.cpu().numpy()
+    eids = dc.topk_ids.cpu().numpy()
+    act_mask = (perm >= 0) & (lids[:, None] >= 0)
+    n_active = int(act_mask.sum())
+    n_keys = len({(int(l), int(e)) for l, e in zip(np.broadcast_to(lids[:, None], eids.shape)[act_mask],
+                                                   eids[act_mask])})
+    delta_bytes = 2.0 * dc.I * n_active + 2.0 * (dc.rank * dc.I + dc.H * dc.rank) * n_keys + \
+        2.0 * dc.T * dc.H + 12.0 * dc.T * dc.top_k + 4.0 * dc.T + 16.0 * dc.E
+    delta_flops = n_active * (2.0 * dc.rank * dc.I + 2.0 * dc.H * dc.rank)
+    M, N, K, r = nc.M, nc.N, nc.K, nc.rank
+    nv_flops = 2.0 * M * N * K + 2.0 * M * N * r
+    nv_bytes = M * K / 2 + N * K / 2 + (M + N) * K / 16 + 2.0 * M * N + 2.0 * (M + N) * r + 2.0 * N
+    fold_bytes = 2.0 * 2 * N * r + 8
+    fold_flops = float(N * r)
+
+    stream = torch.cuda.current_stream(dev)
+    ops = {
+        "grouped_gemm": lambda: mi.grouped_mm_bf16(g2.a, g2.b, g2.m_indptr, out=out2),
+        "lora_delta": lambda: mi.bgmv_moe_gemm2_lora_delta(
+            dc.act, dc.perm, wa, sa, wb, sb, dc.topk_ids, dc.topk_weights, dc.lora_ids, dc.rank,
+            dc.H, num_adapters=dc.L, scale=dc.scale, out=dout, workspace=ws),
+        "fold": lambda: mi.prepare_nvfp4_lora_adapter(nc.lora_b, nc.lora_scale, nc.alpha,
+                                                      out=adapter),
+        "nvfp4_raw": lambda: mi.mm_nvfp4_lora(nc.a, nc.b, nc.a_sf, nc.b_sf, nc.alpha, nc.d,
+                                              nc.lora_b, nc.lora_scale, bias=nc.bias,
+                                              out=nout_raw),
+        "nvfp4_prepared": lambda: mi.mm_nvfp4_lora(nc.a, nc.b, nc.a_sf, nc.b_sf, nc.alpha, nc.d,
+                                                   lora_adapter=adapter, bias=nc.bias,
+                                                   out=nout_prep),
+    }
+    if only:
+        ops = {k: v for k, v in ops.items() if k in only}
+    work = {"grouped_gemm": (gemm_flops, gemm_bytes), "lora_delta": (delta_flops, delta_bytes),
+            "fold": (fold_flops, fold_bytes), "nvfp4_raw": (nv_flops, nv_bytes),
+            "nvfp4_prepared": (nv_flops, nv_bytes)}
+
+    def step(ev=None):
+        for i, (name, fn) in enumerate(ops.items()):
+            if ev is not None:
+                ev[name][0].record(stream)
+            fn()
+            if ev is not None:
+                ev[name][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for n in ops} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    per_op_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in ops}
+    print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall:.3f} s)",
+          file=sys.stderr, flush=True)
+
+    op_report = {}
+    for n, ms in per_op_ms.items():
+        fl, by = work[n]
+        sec = ms * 1e-3
+        rep = {"ms": round(ms, 5), "tflops": round(fl / sec / 1e12, 2), "gbps": round(by / sec / 1e9, 1),
+               "algorithmic_flops": fl, "algorithmic_bytes": by}
+        rep["frac_mfma_peak"] = round(fl / sec / 1e12 / PEAK_MFMA_TFLOPS, 4)
+        rep["frac_hbm_peak"] = round(by / sec / 1e9 / PEAK_HBM_GBPS, 4)
+        op_report[n] = rep
+    step_flops = sum(work[n][0] for n in ops)
+
+    roofline = None
+    if "nvfp4_raw" in ops and "nvfp4_prepared" in ops:
+        avg_ms = (per_op_ms["nvfp4_raw"] + per_op_ms["nvfp4_prepared"]) / 2
+        ach = nv_flops / (avg_ms * 1e-3) / 1e12
+        roofline = {"kernel": "nvfp4_lora_kernel", "bound": "mfma", "achieved": round(ach, 1),
+                    "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "traffic": read_traffic()}
+
+    cpu = None
+    if not args.no_cpu_baseline and not only:
+        cpu = cpu_baseline(g2, dc, nc, wa, wb, sa, sb)
+
+    line = {
+        "metric": METRIC,
+        "value": round(step_flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "moe-fc2-lora hot-path step: grouped GEMM (E=8, 128 rows/expert, k=4096, "
+                        "n=2048, bf16 out) + FC2 LoRA delta (T=8192, top_k=8, E=64, I=2048, "
+                        "H=4096, 8 adapters r=16) + fold + NVFP4+LoRA raw and prepared "
+                        "(M=4096, N=8192, K=8192, r=16)",
+            "value_definition": "sum of the step's algorithmic flops / step time",
+            "grouped_gemm_tflops": op_report.get("grouped_gemm", {}).get("tflops"),
+            "grouped_gemm_frac_bf16_mfma_peak": op_report.get("grouped_gemm", {}).get(
+                "frac_mfma_peak"),
+            "lora_delta_gbps": op_report.get("lora_delta", {}).get("gbps"),
+            "lora_delta_frac_hbm_peak": op_report.get("lora_delta", {}).get("frac_hbm_peak"),
+            "parallelism": "single GPU",
+        },
+        "ops": op_report,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(g2, dc, nc, wa, wb, sa, sb):
+    """The fp64 oracle, as it stands, on a bounded sample of the same step."""
+    import torch
+
+    from oracle import nvfp4 as NV
+    from oracle.grouped_mm import grouped_mm
+    from oracle.lora_delta import Bank, moe_fc2_lora_delta
+
+    def bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            cores = min(cores, max(blas))
+    except Exception:
+        pass
+    flops = 0.0
+    t_total = 0.0
+    # grouped GEMM: the whole uniform workload
+    a, b, mi_ = bits(g2.a), bits(g2.b), g2.m_indptr.cpu().numpy()
+    t = time.perf_counter()
+    grouped_mm(a, b, mi_)
+    t_total += time.perf_counter() - t
+    flops += 2.0 * g2.a.shape[0] * g2.a.shape[1] * g2.b.shape[1]
+    # LoRA delta: 2048 of the 8192 tokens
+    toks = list(range(0, dc.T, dc.T // 2048))
+    act = bits(dc.act)
+    ba, bb = Bank(bits(dc.A.reshape(-1)), dc.A.data_ptr()), Bank(bits(dc.B.reshape(-1)),
+                                                                 dc.B.data_ptr())
+    perm = dc.perm.cpu().numpy()
+    lids = dc.lora_ids.cpu().numpy()
+    t = time.perf_counter()
+    moe_fc2_lora_delta(act, perm, ba, wa.cpu().numpy(), sa, bb, wb.cpu().numpy(), sb,
+                       dc.topk_ids.cpu().numpy(), dc.topk_weights.cpu().numpy(), lids, dc.rank,
+                       dc.H, dc.scale, tokens=toks)
+    t_total += time.perf_counter() - t
+    pr = perm.reshape(dc.T, dc.top_k)
+    n_act = int(((pr[toks] >= 0) & (lids[toks][:, None] >= 0)).sum())
+    flops += n_act * (2.0 * dc.rank * dc.I + 2.0 * dc.H * dc.rank)
+    # NVFP4 raw: 512 of the 4096 rows, all columns
+    rows = np.arange(0, nc.M, nc.M // 512)
+    a_c = nc.a.cpu().numpy()[rows]
+    b_c, asf, bsf = nc.b.cpu().numpy(), nc.a_sf.cpu().numpy(), nc.b_sf.cpu().numpy()
+    t = time.perf_counter()
+    base = NV.base_product(a_c, b_c, asf, bsf, nc.K, rows, None)
+    NV.mm_nvfp4_raw(base, float(nc.alpha[0]), bits(nc.d)[rows], bits(nc.lora_b),
+                    float(nc.lora_scale[0]), bits(nc.bias))
+    t_total += time.perf_counter() - t
+    flops += 2.0 * len(rows) * nc.N * nc.K + 2.0 * len(rows) * nc.N * nc.rank
+    return {"value": round(flops / t_total / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(t_total, 2),
+            "sample": "whole grouped GEMM workload + LoRA delta on 2048 of 8192 tokens + NVFP4 "
+                      "raw on 512 of 4096 rows (all columns); flops of the sample / oracle time"}
+
+
+if __name__ == "__main__":
+    main()
