@@ -103,7 +103,7 @@ MI_API mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k,
  * The intermediate A_down @ act stays fp32; the result is rounded once.
  * Requirements: lora_dtype MI_BF16; out_dtype MI_BF16 or MI_F32; rank % 8 == 0,
  * 8 <= rank <= 128; inter_size % 8 == 0; hidden % 128 == 0; 1 <= top_k <= 32;
- * top_k * rank <= 512; lora strides multiples of 8; num_adapters * num_experts <= 8192.
+ * lora strides multiples of 8; num_experts <= 512.
  */
 MI_API size_t mi_moe_fc2_lora_delta_workspace_size(int64_t num_tokens, int64_t top_k,
                                             int64_t num_experts, int64_t num_adapters,

@@ -67,4 +67,18 @@ __device__ __forceinline__ T bitcast(const uint4& v) {
   return __builtin_bit_cast(T, v);
 }
 
+// Loads/stores through the global address space.  Pointers that reach a
+// kernel through structs, LDS tables or the pointer tables are otherwise
+// generic ("flat"); flat accesses share the LDS wait counter, so every LDS
+// wait would also wait for them.
+#define MI_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ T gld(const void* p) {
+  return *(const MI_GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ void gst(void* p, const T& v) {
+  *(MI_GLOBAL T*)(p) = v;
+}
+
 }  // namespace mi

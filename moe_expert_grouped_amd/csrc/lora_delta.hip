@@ -3,301 +3,507 @@
 // delta[t] = scale * sum_j w[t,j] * B_down[l,e] @ (A_down[l,e] @ act[perm[t*top_k+j]])
 // (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta, formula and parameters).
 //
+// Work is organised around token tiles: up to TT tokens of one adapter.
 // Three launches on the caller's stream, no host reads:
 //
-//  1. plan    (one workgroup) -- decodes every slot (t, j): it is active iff
-//             the permuted row p >= 0 (and < padded_rows), the adapter
-//             l = lora_ids[t] lies in [0, num_adapters) and the expert lies in
-//             [0, num_experts).  Active slots are bucketed by key (l, e) and
-//             tokens by adapter (bucket num_adapters = "no adapter").  It emits
-//             two work lists: shrink items (<= 16 slots of one key) and expand
-//             items (<= TT tokens of one adapter bucket).  Positions inside a
-//             bucket come from LDS atomics, so the order varies between runs;
-//             no result depends on it (every slot and every token is computed
-//             by the same instruction sequence wherever it lands).
-//  2. shrink  -- one wavefront per shrink item: u[slot, :] = (scale*w) *
-//             A_le @ act[p] with v_mfma_f32_16x16x32_bf16 (16 slots x 16 ranks,
-//             K = inter_size); the act rows are gathered straight from HBM and
-//             A_le is shared by the item's 16 slots.  u stays fp32.
-//  3. expand  -- one workgroup per (expand item, H range): the tile's tokens
-//             (one adapter, up to 32 per wavefront) walk the experts in
-//             increasing order; B_le[h-chunk, :] is staged through LDS once per
-//             workgroup and expert; each token contributes its slot's u for
-//             that expert (zero when it has none) as the MFMA A operand.  u is
-//             split exactly-enough into bf16 hi + lo parts (two MFMAs), so the
-//             intermediate keeps ~16 significand bits.  Accumulation per token
-//             runs over experts in a fixed order: bitwise repeatable.  Tokens
-//             of the "no adapter" bucket get +0 rows.
+//  1. plan    (one workgroup) -- buckets the T tokens by adapter (bucket
+//             num_adapters collects tokens without a valid adapter) and cuts
+//             every bucket into tiles of <= TT tokens.
+//  2. shrink  -- one workgroup per (tile, group of experts).  Every workgroup
+//             lists the tile's active slots (permuted row in [0, padded_rows),
+//             expert in [0, num_experts)) by expert in LDS, each expert's list
+//             sorted by slot, and cuts every expert's list into 16-slot
+//             blocks; the workgroup of expert group 0 stores the tile's block
+//             table (expert and token rows of each block) for the expand.  A
+//             wavefront turns one block into u = (scale*w) * A_le @ act[row]
+//             with v_mfma_f32_16x16x32_bf16: the activation rows and A_le are
+//             streamed with coalesced 16-byte loads (two stages in flight in
+//             registers) into a wave-private, swizzled LDS stage and read back
+//             as MFMA fragments.  (An MFMA fragment puts neighbouring lanes on
+//             different rows; loading fragments straight from memory would
+//             split every instruction into 64 scattered requests.)  u is
+//             written as bf16 hi = bf16(u) and lo = bf16(u - hi) (~16
+//             significand bits together), directly in the fragment order the
+//             expand consumes: one contiguous 1 KiB record per block and 16
+//             ranks; record i belongs to block i of the table.
+//  3. expand  -- one workgroup per (tile, 128 output columns), in an order
+//             that keeps the tiles of one column chunk on one XCD (they share
+//             B columns through its L2).  An fp32 accumulator [TT tokens x 128
+//             columns] lives in LDS.  Each of 4 wavefronts owns 32 columns and
+//             walks the block table in order; per block it issues, for each of
+//             its two 16-column groups, v_mfma_f32_16x16x32_bf16 on [B_le |
+//             B_le] (16 columns x 32) and [u_hi ; u_lo] (32 x 16 slots) and
+//             adds the 4 consecutive columns each lane holds into the slot's
+//             token row with one 16-byte LDS read-modify-write.  The u record,
+//             the B_le fragments (16 columns x 16 ranks are 512 contiguous
+//             bytes) and the token rows of a block are loaded several blocks
+//             ahead in a register ring.  The wavefront owns its columns and a
+//             block never holds one token twice (unless the routing repeats an
+//             expert for a token; such a tile uses LDS float atomics), so
+//             every accumulator element is updated by one wavefront in block
+//             order: the summation order per token is fixed and the result is
+//             bitwise repeatable.  Tokens without adapter get +0 rows.
 #include "common.hpp"
 
 namespace mi {
 namespace {
 
 constexpr int PLAN_THREADS = 1024;
-constexpr int MAX_KEYS = 8192;      // num_adapters * num_experts
 constexpr int MAX_ADAPTERS = 1023;  // + 1 "none" bucket
-constexpr int SHRINK_ROWS = 16;
-constexpr int EXP_TOK_PER_WAVE = 32;
-constexpr int EXP_HC = 128;         // H columns per expand pass (4 x 32 per wave)
 constexpr int MAX_TOPK = 32;
+constexpr int MAX_EXPERTS = 512;
+constexpr int SLOT_BUDGET = 1024;   // slots per tile (TT * top_k)
+constexpr int NT_DELTA = 256;       // threads of the shrink and expand workgroups
 
-struct Item {  // a run of sorted entries
-  int start, count, key, pad;
+struct Tile {
+  int bucket, start, count, pad;
 };
 
+__device__ __forceinline__ Tile load_tile(const Tile* t) {
+  return __builtin_bit_cast(Tile, gld<u32x4>(t));
+}
+__device__ __forceinline__ void store_tile(Tile* t, const Tile& v) {
+  gst<u32x4>(t, __builtin_bit_cast(u32x4, v));
+}
+
 struct Layout {
-  size_t u, slot_list, tok_list, shrink_items, expand_items, counters, total;
+  size_t u2, tok_list, tiles, counters, blk_e, blk_tl, tinfo, total;
+  long cap;     // padded slot positions per tile
+  int maxblk;   // 16-slot blocks per tile, at most
 };
 
 __host__ __device__ inline size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-int expand_waves(int64_t top_k, int64_t rank) {
-  // LDS per token: top_k * rank * 4 bytes (bf16 hi + lo); budget 64 KiB
-  const int64_t per_tok = top_k * rank * 4;
-  int64_t w = (64 * 1024) / (EXP_TOK_PER_WAVE * per_tok);
-  if (w > 4) w = 4;
-  return static_cast<int>(w);
+int tile_tokens(int64_t top_k) {
+  int tt = 128;
+  while (tt * top_k > SLOT_BUDGET) tt >>= 1;
+  return tt;
+}
+
+int64_t max_tiles(int64_t T, int64_t top_k, int64_t L) { return T / tile_tokens(top_k) + L + 2; }
+
+// every expert's list is padded to whole 16-slot blocks
+long tile_capacity(int64_t top_k, int64_t E) {
+  const long slots = static_cast<long>(tile_tokens(top_k)) * top_k;
+  return slots + 15 * (E < slots ? E : slots);
+}
+
+// 16-rank chunks per slot, rounded up to 1, 2, 4 or 8
+int rank_chunks(int64_t rank) {
+  const int c = static_cast<int>((rank + 15) / 16);
+  return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 8;
 }
 
 Layout layout(int64_t T, int64_t top_k, int64_t E, int64_t L, int64_t rank) {
   Layout ly{};
-  const int64_t slots = T * top_k;
-  const int ew = expand_waves(top_k, rank);
-  const int64_t tt = (ew > 0 ? ew : 1) * EXP_TOK_PER_WAVE;
+  ly.cap = tile_capacity(top_k, E);
+  const long nb = rank_chunks(rank);
   size_t off = 0;
-  ly.u = off;
-  off = al256(off + static_cast<size_t>(slots * rank) * 4);
-  ly.slot_list = off;
-  off = al256(off + static_cast<size_t>(slots) * 4);
+  ly.u2 = off;
+  off = al256(off + static_cast<size_t>(max_tiles(T, top_k, L)) * ly.cap * nb * 64);
   ly.tok_list = off;
   off = al256(off + static_cast<size_t>(T) * 4);
-  ly.shrink_items = off;
-  off = al256(off + static_cast<size_t>(slots / SHRINK_ROWS + L * E + 1) * sizeof(Item));
-  ly.expand_items = off;
-  off = al256(off + static_cast<size_t>(T / tt + L + 2) * sizeof(Item));
+  ly.tiles = off;
+  off = al256(off + static_cast<size_t>(max_tiles(T, top_k, L)) * sizeof(Tile));
   ly.counters = off;
   off = al256(off + 64);
+  const size_t mt = static_cast<size_t>(max_tiles(T, top_k, L));
+  ly.maxblk = static_cast<int>(ly.cap / 16 + 1);
+  ly.blk_e = off;  // expert of each block
+  off = al256(off + mt * ly.maxblk * 4);
+  ly.blk_tl = off;  // token row (tile-local) of each of a block's 16 slots, 0xFF = empty
+  off = al256(off + mt * ly.maxblk * 16);
+  ly.tinfo = off;  // per tile: number of blocks, "a token repeats an expert" flag
+  off = al256(off + mt * 8);
   ly.total = off;
   return ly;
 }
 
 // ---------------------------------------------------------------------------
-// 1. plan
+// 1. plan: tokens by adapter, tiles
 // ---------------------------------------------------------------------------
 struct PlanArgs {
-  const int32_t* perm;
-  const int32_t* topk_ids;
   const int32_t* lora_ids;
-  int T, top_k, E, L, padded_rows, tok_tile;
-  int32_t* slot_list;
+  int T, L, tt;
   int32_t* tok_list;
-  Item* shrink_items;
-  Item* expand_items;
-  int32_t* counters;  // [0] shrink item count, [1] expand item count
+  Tile* tiles;
+  int32_t* counters;  // [0] = number of tiles
 };
 
-__device__ __forceinline__ int slot_key(const PlanArgs& p, int x) {
-  const int t = x / p.top_k;
-  const int l = p.lora_ids[t];
-  const int r = p.perm[x];
-  const int e = p.topk_ids[x];
-  if (l < 0 || l >= p.L || r < 0 || r >= p.padded_rows || e < 0 || e >= p.E) return -1;
-  return l * p.E + e;
-}
-
-// exclusive scan of n ints in LDS (in place), returns the total; all threads call
-__device__ int block_exclusive_scan(int* v, int n, int* s_part) {
-  const int tid = threadIdx.x;
-  const int per = (n + PLAN_THREADS - 1) / PLAN_THREADS;
-  const int b0 = tid * per;
-  int local = 0;
-  for (int i = 0; i < per; ++i)
-    if (b0 + i < n) local += v[b0 + i];
-  // wave inclusive scan
-  const int lane = tid & 63, wave = tid >> 6;
-  int incl = local;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) s_part[wave] = incl;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int w = 0; w < PLAN_THREADS / 64; ++w) {
-      const int c = s_part[w];
-      s_part[w] = run;
-      run += c;
-    }
-    s_part[PLAN_THREADS / 64] = run;
-  }
-  __syncthreads();
-  int run = s_part[wave] + incl - local;
-  for (int i = 0; i < per; ++i)
-    if (b0 + i < n) {
-      const int c = v[b0 + i];
-      v[b0 + i] = run;
-      run += c;
-    }
-  const int total = s_part[PLAN_THREADS / 64];
-  __syncthreads();
-  return total;
-}
-
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs p) {
-  __shared__ int s_cnt[MAX_KEYS];
-  __shared__ int s_off[MAX_KEYS];
-  __shared__ int s_blk[MAX_KEYS];
-  __shared__ int s_tcnt[MAX_ADAPTERS + 1];
-  __shared__ int s_toff[MAX_ADAPTERS + 1];
-  __shared__ int s_tblk[MAX_ADAPTERS + 1];
-  __shared__ int s_part[PLAN_THREADS / 64 + 1];
+  __shared__ int s_cnt[MAX_ADAPTERS + 1];
+  __shared__ int s_off[MAX_ADAPTERS + 1];
+  __shared__ int s_tile0[MAX_ADAPTERS + 2];
   const int tid = threadIdx.x;
-  const int nkeys = p.L * p.E;
   const int nb = p.L + 1;
-  const int slots = p.T * p.top_k;
-
-  for (int i = tid; i < nkeys; i += PLAN_THREADS) s_cnt[i] = 0;
-  for (int i = tid; i < nb; i += PLAN_THREADS) s_tcnt[i] = 0;
+  for (int i = tid; i < nb; i += PLAN_THREADS) s_cnt[i] = 0;
   __syncthreads();
-  for (int x = tid; x < slots; x += PLAN_THREADS) {
-    const int key = slot_key(p, x);
-    if (key >= 0) atomicAdd(&s_cnt[key], 1);
-  }
   for (int t = tid; t < p.T; t += PLAN_THREADS) {
-    const int l = p.lora_ids[t];
-    atomicAdd(&s_tcnt[(l >= 0 && l < p.L) ? l : p.L], 1);
+    const int l = gld<int>(p.lora_ids + t);
+    atomicAdd(&s_cnt[(l >= 0 && l < p.L) ? l : p.L], 1);
   }
   __syncthreads();
-  for (int i = tid; i < nkeys; i += PLAN_THREADS) {
-    s_off[i] = s_cnt[i];
-    s_blk[i] = (s_cnt[i] + SHRINK_ROWS - 1) / SHRINK_ROWS;
-  }
-  for (int i = tid; i < nb; i += PLAN_THREADS) {
-    s_toff[i] = s_tcnt[i];
-    s_tblk[i] = (s_tcnt[i] + p.tok_tile - 1) / p.tok_tile;
+  if (tid < 64) {  // one wavefront scans the (<= 1024) buckets
+    const int per = (nb + 63) / 64, b0 = tid * per;
+    int tok = 0, til = 0;
+    for (int i = 0; i < per; ++i)
+      if (b0 + i < nb) {
+        tok += s_cnt[b0 + i];
+        til += (s_cnt[b0 + i] + p.tt - 1) / p.tt;
+      }
+    int itok = tok, itil = til;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int a = __shfl_up(itok, o, 64), b = __shfl_up(itil, o, 64);
+      if (tid >= o) {
+        itok += a;
+        itil += b;
+      }
+    }
+    int rt = itok - tok, rl = itil - til;
+    for (int i = 0; i < per; ++i)
+      if (b0 + i < nb) {
+        s_off[b0 + i] = rt;
+        s_tile0[b0 + i] = rl;
+        rt += s_cnt[b0 + i];
+        rl += (s_cnt[b0 + i] + p.tt - 1) / p.tt;
+      }
+    if (tid == 63) {
+      s_tile0[nb] = itil;
+      gst<int>(p.counters, itil);
+    }
   }
   __syncthreads();
-  block_exclusive_scan(s_off, nkeys, s_part);
-  const int n_shrink = block_exclusive_scan(s_blk, nkeys, s_part);
-  block_exclusive_scan(s_toff, nb, s_part);
-  const int n_expand = block_exclusive_scan(s_tblk, nb, s_part);
-
-  for (int key = tid; key < nkeys; key += PLAN_THREADS) {
-    const int c = s_cnt[key];
-    for (int b = 0; b * SHRINK_ROWS < c; ++b)
-      p.shrink_items[s_blk[key] + b] = Item{s_off[key] + b * SHRINK_ROWS,
-                                            min(SHRINK_ROWS, c - b * SHRINK_ROWS), key, 0};
-  }
-  for (int bk = tid; bk < nb; bk += PLAN_THREADS) {
-    const int c = s_tcnt[bk];
-    for (int b = 0; b * p.tok_tile < c; ++b)
-      p.expand_items[s_tblk[bk] + b] =
-          Item{s_toff[bk] + b * p.tok_tile, min(p.tok_tile, c - b * p.tok_tile), bk, 0};
-  }
-  if (tid == 0) {
-    p.counters[0] = n_shrink;
-    p.counters[1] = n_expand;
+  for (int b = tid; b < nb; b += PLAN_THREADS) {
+    const int c = s_cnt[b];
+    for (int i = 0; i * p.tt < c; ++i)
+      store_tile(p.tiles + s_tile0[b] + i, Tile{b, s_off[b] + i * p.tt, min(p.tt, c - i * p.tt), 0});
   }
   __syncthreads();
-  // scatter (cursor = running offsets)
-  for (int x = tid; x < slots; x += PLAN_THREADS) {
-    const int key = slot_key(p, x);
-    if (key >= 0) p.slot_list[atomicAdd(&s_off[key], 1)] = x;
-  }
   for (int t = tid; t < p.T; t += PLAN_THREADS) {
-    const int l = p.lora_ids[t];
-    p.tok_list[atomicAdd(&s_toff[(l >= 0 && l < p.L) ? l : p.L], 1)] = t;
+    const int l = gld<int>(p.lora_ids + t);
+    gst<int>(p.tok_list + atomicAdd(&s_off[(l >= 0 && l < p.L) ? l : p.L], 1), t);
   }
+}
+
+// ---------------------------------------------------------------------------
+// the tile's active slots, by expert (shared by shrink and expand)
+// ---------------------------------------------------------------------------
+struct SlotSrc {
+  const int32_t* tok_list;
+  const int32_t* perm;
+  const int32_t* topk_ids;
+  int top_k, padded_rows, E;
+};
+
+struct SlotLists {
+  int cnt[MAX_EXPERTS];       // scratch: counts, then write cursors
+  int off[MAX_EXPERTS + 1];   // start of each expert in `list`
+  int poff[MAX_EXPERTS + 1];  // start in the padded (whole-block) position space
+  int list[SLOT_BUDGET];      // entries (t_local << 24 | x), ascending per expert
+  int row[SLOT_BUDGET];       // permuted activation row of each entry
+  int tmp[SLOT_BUDGET];       // scratch: unsorted entries
+};
+
+// All NT_DELTA threads call it.  Loads every slot of the tile once (two
+// dependent rounds of loads), counts per expert, scans, scatters, and sorts
+// each expert's list (one thread per expert) so that the order is the same
+// in every workgroup that lists this tile.
+__device__ void list_slots(const SlotSrc& s, const Tile& tile, SlotLists& L) {
+  constexpr int PER = SLOT_BUDGET / NT_DELTA;
+  const int tid = threadIdx.x;
+  const int nslots = tile.count * s.top_k;
+  int xs[PER], es[PER], rs[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = tid + k * NT_DELTA;
+    xs[k] = -1;
+    if (i < nslots) {
+      const int tl = i / s.top_k;
+      xs[k] = gld<int>(s.tok_list + tile.start + tl) * s.top_k + (i - tl * s.top_k);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    es[k] = -1;
+    rs[k] = 0;
+    if (xs[k] >= 0) {
+      const int e = gld<int>(s.topk_ids + xs[k]), r = gld<int>(s.perm + xs[k]);
+      if (e >= 0 && e < s.E && r >= 0 && r < s.padded_rows) es[k] = e;
+      rs[k] = r;
+    }
+  }
+  for (int i = tid; i < s.E; i += NT_DELTA) L.cnt[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    if (es[k] >= 0) atomicAdd(&L.cnt[es[k]], 1);
+  __syncthreads();
+  if (tid < 64) {
+    const int per = (s.E + 63) / 64, b0 = tid * per;
+    int loc = 0, ploc = 0;
+    for (int i = 0; i < per; ++i)
+      if (b0 + i < s.E) {
+        loc += L.cnt[b0 + i];
+        ploc += (L.cnt[b0 + i] + 15) & ~15;
+      }
+    int inc = loc, pinc = ploc;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int a = __shfl_up(inc, o, 64), b = __shfl_up(pinc, o, 64);
+      if (tid >= o) {
+        inc += a;
+        pinc += b;
+      }
+    }
+    int run = inc - loc, prun = pinc - ploc;
+    for (int i = 0; i < per; ++i)
+      if (b0 + i < s.E) {
+        const int c = L.cnt[b0 + i];
+        L.off[b0 + i] = run;
+        L.poff[b0 + i] = prun;
+        L.cnt[b0 + i] = run;  // write cursor
+        run += c;
+        prun += (c + 15) & ~15;
+      }
+    if (tid == 63) {
+      L.off[s.E] = inc;
+      L.poff[s.E] = pinc;
+    }
+  }
+  __syncthreads();
+  int pos[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    pos[k] = -1;
+    if (es[k] >= 0) {
+      const uint32_t tl = static_cast<uint32_t>((tid + k * NT_DELTA) / s.top_k);
+      xs[k] = static_cast<int>((tl << 24) | static_cast<uint32_t>(xs[k]));  // the entry
+      pos[k] = atomicAdd(&L.cnt[es[k]], 1);
+      L.tmp[pos[k]] = xs[k];
+    }
+  }
+  __syncthreads();
+  // rank of each entry inside its expert's list (entries are distinct)
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    if (pos[k] >= 0) {
+      const int b = L.off[es[k]], n = L.off[es[k] + 1] - b;
+      const uint32_t v = static_cast<uint32_t>(xs[k]);
+      int rank = 0;
+      for (int i = 0; i < n; ++i) rank += static_cast<uint32_t>(L.tmp[b + i]) < v ? 1 : 0;
+      L.list[b + rank] = xs[k];
+      L.row[b + rank] = rs[k];
+    }
+  __syncthreads();
+}
+
+// u2 record of one 16-slot block: NB chunks x [4 parts][16 slots][8 bf16];
+// parts 0, 1 = hi of the chunk's ranks 0-7 / 8-15, parts 2, 3 = lo.
+__device__ __forceinline__ int u2_elem(int c, int part, int slot, int r8) {
+  return c * 512 + part * 128 + slot * 8 + r8;
 }
 
 // ---------------------------------------------------------------------------
 // 2. shrink
 // ---------------------------------------------------------------------------
 struct ShrinkArgs {
+  SlotSrc src;
   const uint16_t* act;
-  const int32_t* perm;
   const int64_t* w_ptr_a;
   long stride_a;
   const float* topk_weights;
-  const int32_t* slot_list;
-  const Item* items;
+  const Tile* tiles;
   const int32_t* counters;
-  float* u;
-  int I, E, rank;
+  uint16_t* u2;
+  int32_t* blk_e;
+  uint32_t* blk_tl;
+  int32_t* tinfo;
+  long cap;
+  int I, L, rank, epg, maxblk;
   float scale;
 };
 
-template <int NB>  // number of 16-rank blocks
-__global__ __launch_bounds__(256) void shrink_kernel(ShrinkArgs p) {
-  const int lane = threadIdx.x & 63;
-  const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int nw = (gridDim.x * blockDim.x) >> 6;
-  const int n_items = p.counters[0];
-  const int row = lane & 15, kq = lane >> 4;  // k offset 8*kq inside a 32-wide step
-  for (int it = gw; it < n_items; it += nw) {
-    const Item item = p.items[it];
-    const int l = item.key / p.E, e = item.key % p.E;
-    const int x = p.slot_list[item.start + min(row, item.count - 1)];
-    const uint16_t* arow = p.act + static_cast<long>(p.perm[x]) * p.I + kq * 8;
-    const uint16_t* Ale = reinterpret_cast<const uint16_t*>(p.w_ptr_a[e]) +
-                          static_cast<long>(l) * p.stride_a;
-    const uint16_t* brow[NB];
-    bool bvalid[NB];
+// The block table of a tile, for the expand: blocks in expert order (the u2
+// record of block i is record i), each with its expert and the tile-local
+// token row of its 16 slots.  Also flags a token that routes to one expert
+// twice (a block would then hold that token twice).
+__device__ void write_block_table(const SlotLists& L, int E, int ti, const ShrinkArgs& p) {
+  int dup = 0;
+  int32_t* be = p.blk_e + static_cast<long>(ti) * p.maxblk;
+  uint32_t* bt = p.blk_tl + static_cast<long>(ti) * p.maxblk * 4;
+  for (int e = threadIdx.x; e < E; e += NT_DELTA) {
+    const int b0 = L.off[e], n = L.off[e + 1] - b0;
+    for (int i = 1; i < n; ++i)
+      dup |= (static_cast<uint32_t>(L.list[b0 + i]) >> 24) ==
+             (static_cast<uint32_t>(L.list[b0 + i - 1]) >> 24);
+    for (int b = 0; b * 16 < n; ++b) {
+      const int bi = (L.poff[e] >> 4) + b;
+      gst<int>(be + bi, e);
+      uint32_t w[4];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int rr = nb * 16 + row;
-      bvalid[nb] = rr < p.rank;
-      brow[nb] = Ale + static_cast<long>(bvalid[nb] ? rr : 0) * p.I + kq * 8;
+      for (int q = 0; q < 4; ++q) {
+        w[q] = 0;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const int k = 16 * b + 4 * q + s2;
+          const uint32_t tl = k < n ? static_cast<uint32_t>(L.list[b0 + k]) >> 24 : 0xFFu;
+          w[q] |= tl << (8 * s2);
+        }
+      }
+      gst<u32x4>(bt + bi * 4, u32x4{w[0], w[1], w[2], w[3]});
+    }
+  }
+  dup = __syncthreads_or(dup);
+  if (threadIdx.x == 0) {
+    gst<int>(p.tinfo + 2 * ti, L.poff[E] >> 4);
+    gst<int>(p.tinfo + 2 * ti + 1, dup);
+  }
+}
+
+template <int NB>  // 1, 2, 4 or 8
+__global__ __launch_bounds__(NT_DELTA) void shrink_kernel(ShrinkArgs p) {
+  static_assert(NB == 1 || NB == 2 || NB == 4 || NB == 8, "rank chunks");
+  constexpr int KC = (128 / NB) < 32 ? 32 : 128 / NB;  // K elements per LDS stage
+  constexpr int CPR = KC / 8;                          // 16-byte chunks per stage row
+  constexpr int RPI = 64 / CPR;                        // rows per coalesced load instruction
+  constexpr int NLA = 16 / RPI;                        // act loads per lane per stage
+  constexpr int NLB = 16 * NB / RPI;                   // A_le loads per lane per stage
+  constexpr int STAGE = 16 * (1 + NB) * KC;            // bf16 per wave stage
+  __shared__ SlotLists SL;
+  __shared__ const uint16_t* s_abase[MAX_EXPERTS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_stage[NT_DELTA / 64][STAGE];
+
+  const int ti = blockIdx.x;
+  if (ti >= gld<int>(p.counters)) return;
+  const Tile tile = load_tile(p.tiles + ti);
+  if (tile.bucket >= p.L) return;
+  const int E = p.src.E;
+  const int e0 = blockIdx.y * p.epg, e1 = min(e0 + p.epg, E);
+  if (e0 >= e1) return;
+  const int l = tile.bucket;
+  for (int i = threadIdx.x; i < e1 - e0; i += NT_DELTA)
+    s_abase[i] = reinterpret_cast<const uint16_t*>(gld<int64_t>(p.w_ptr_a + e0 + i)) +
+                 static_cast<long>(l) * p.stride_a;
+  list_slots(p.src, tile, SL);
+  if (blockIdx.y == 0) write_block_table(SL, E, ti, p);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, kq = lane >> 4;   // MFMA fragment roles
+  const int lrow = lane / CPR, lch = lane % CPR;  // coalesced-load roles
+  uint16_t* stA = s_stage[wave];     // [16][KC]
+  uint16_t* stB = stA + 16 * KC;     // [16*NB][KC]
+  uint16_t* u2t = p.u2 + static_cast<long>(ti) * p.cap * NB * 32;
+
+  int nblk = 0;
+  for (int e = e0; e < e1; ++e) nblk += (SL.off[e + 1] - SL.off[e] + 15) >> 4;
+  for (int blk = wave; blk < nblk; blk += NT_DELTA / 64) {
+    int e = e0, b = blk;
+    while (true) {
+      const int c = (SL.off[e + 1] - SL.off[e] + 15) >> 4;
+      if (b < c) break;
+      b -= c;
+      ++e;
+    }
+    const int base = SL.off[e] + b * 16;
+    const int cnt = min(16, SL.off[e + 1] - base);
+    const uint16_t* Ale = s_abase[e - e0];
+    const uint16_t* asrc[NLA];
+    const uint16_t* bsrc[NLB];
+#pragma unroll
+    for (int j = 0; j < NLA; ++j) {
+      const int r = j * RPI + lrow;  // 0..15
+      asrc[j] = p.act + static_cast<long>(SL.row[base + min(r, cnt - 1)]) * p.I + lch * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < NLB; ++j) {
+      const int r = j * RPI + lrow;  // rank row 0 .. 16*NB-1 (clamped to real ranks)
+      bsrc[j] = Ale + static_cast<long>(min(r, p.rank - 1)) * p.I + lch * 8;
     }
     f32x4 acc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int I = p.I;
-    int k0 = 0;
-    constexpr int U = 4;
-    for (; k0 + 32 * U <= I; k0 += 32 * U) {
-      u32x4 fa[U], fb[U][NB];
+    const int nst = p.I / KC;  // full stages
+    // two register stages in flight: stage st + 2 is loaded while st feeds the MFMAs
+    u32x4 ra0[NLA], rb0[NLB], ra1[NLA], rb1[NLB];
+    auto gload = [&](u32x4 (&ra)[NLA], u32x4 (&rb)[NLB], int st) {
+      if (st < nst) {
+        const int k0 = st * KC;
 #pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        fa[uu] = *reinterpret_cast<const u32x4*>(arow + k0 + 32 * uu);
+        for (int j = 0; j < NLA; ++j) ra[j] = gld<u32x4>(asrc[j] + k0);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          fb[uu][nb] = bvalid[nb] ? *reinterpret_cast<const u32x4*>(brow[nb] + k0 + 32 * uu)
-                                  : u32x4{0, 0, 0, 0};
+        for (int j = 0; j < NLB; ++j) rb[j] = gld<u32x4>(bsrc[j] + k0);
+      }
+    };
+    auto consume = [&](u32x4 (&ra)[NLA], u32x4 (&rb)[NLB], int st) {
+      // registers -> LDS; chunk c of stage row r sits at chunk c ^ (r % CPR)
+#pragma unroll
+      for (int j = 0; j < NLA; ++j) {
+        const int r = j * RPI + lrow;
+        *reinterpret_cast<u32x4*>(stA + r * KC + ((lch ^ (r % CPR)) << 3)) = ra[j];
       }
 #pragma unroll
-      for (int uu = 0; uu < U; ++uu)
+      for (int j = 0; j < NLB; ++j) {
+        const int r = j * RPI + lrow;
+        *reinterpret_cast<u32x4*>(stB + r * KC + ((lch ^ (r % CPR)) << 3)) = rb[j];
+      }
+      __builtin_amdgcn_wave_barrier();
+      gload(ra, rb, st + 2);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[uu]),
-                                                            __builtin_bit_cast(bf16x8, fb[uu][nb]),
-                                                            acc[nb], 0, 0, 0);
+      for (int s2 = 0; s2 < KC / 32; ++s2) {
+        const int c = 4 * s2 + kq;
+        const u32x4 fa =
+            *reinterpret_cast<const u32x4*>(stA + row * KC + ((c ^ (row % CPR)) << 3));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int rr = nb * 16 + row;
+          const u32x4 fb =
+              *reinterpret_cast<const u32x4*>(stB + rr * KC + ((c ^ (rr % CPR)) << 3));
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa),
+                                                            __builtin_bit_cast(bf16x8, fb), acc[nb],
+                                                            0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();  // this stage's reads precede the next stage's writes
+    };
+    gload(ra0, rb0, 0);
+    gload(ra1, rb1, 1);
+    for (int st = 0; st < nst; st += 2) {
+      consume(ra0, rb0, st);
+      if (st + 1 < nst) consume(ra1, rb1, st + 1);
     }
-    for (; k0 < I; k0 += 32) {
-      const bool kin = k0 + kq * 8 < I;  // I % 8 == 0
-      const u32x4 fa = kin ? *reinterpret_cast<const u32x4*>(arow + k0) : u32x4{0, 0, 0, 0};
+    // K tail (I % KC != 0): fragments straight from memory
+    for (int k0 = nst * KC; k0 < p.I; k0 += 32) {
+      const bool kin = k0 + kq * 8 < p.I;  // I % 8 == 0
+      const u32x4 fa =
+          kin ? gld<u32x4>(p.act + static_cast<long>(SL.row[base + min(row, cnt - 1)]) * p.I + k0 +
+                           kq * 8)
+              : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 fb = (kin && bvalid[nb]) ? *reinterpret_cast<const u32x4*>(brow[nb] + k0)
-                                             : u32x4{0, 0, 0, 0};
+        const int rr = nb * 16 + row;
+        const u32x4 fb = (kin && rr < p.rank)
+                             ? gld<u32x4>(Ale + static_cast<long>(rr) * p.I + k0 + kq * 8)
+                             : u32x4{0, 0, 0, 0};
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, fa), __builtin_bit_cast(bf16x8, fb), acc[nb], 0, 0, 0);
       }
     }
-    // acc[nb][q] = u_raw[slot row 4*kq + q][rank nb*16 + row]
+    // acc[nb][q] = (A_le @ act)[slot row 4*kq + q][rank nb*16 + row]; padded rows/ranks -> 0
+    uint16_t* rec = u2t + static_cast<long>((SL.poff[e] + b * 16) / 16) * NB * 512;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int srow = 4 * kq + q;
-      if (srow < item.count) {
-        const int xs = p.slot_list[item.start + srow];
-        const float f = p.scale * p.topk_weights[xs];
+      float f = 0.f;
+      if (srow < cnt)
+        f = p.scale * gld<float>(p.topk_weights + (SL.list[base + srow] & 0xffffff));
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int rr = nb * 16 + row;
-          if (rr < p.rank) p.u[static_cast<long>(xs) * p.rank + rr] = acc[nb][q] * f;
-        }
+      for (int nb = 0; nb < NB; ++nb) {
+        const float v = nb * 16 + row < p.rank ? acc[nb][q] * f : 0.f;
+        const uint32_t hi = f32_to_bf16_rne(v);
+        const uint32_t lo = f32_to_bf16_rne(v - bf16_bits_to_f32(hi));
+        gst<uint16_t>(rec + u2_elem(nb, row >> 3, srow, row & 7), static_cast<uint16_t>(hi));
+        gst<uint16_t>(rec + u2_elem(nb, 2 + (row >> 3), srow, row & 7),
+                      static_cast<uint16_t>(lo));
       }
     }
   }
@@ -306,193 +512,175 @@ __global__ __launch_bounds__(256) void shrink_kernel(ShrinkArgs p) {
 // ---------------------------------------------------------------------------
 // 3. expand
 // ---------------------------------------------------------------------------
+constexpr int EXP_CW = 128;  // output columns per workgroup: 4 wavefronts x 2 x 16
+constexpr int MAX_BLOCKS = SLOT_BUDGET / 16 + MAX_EXPERTS;
+
 struct ExpandArgs {
-  const int32_t* perm;
-  const int32_t* topk_ids;
+  const int32_t* tok_list;
   const int64_t* w_ptr_b;
   long stride_b;
-  const int32_t* tok_list;
-  const Item* items;
+  const Tile* tiles;
   const int32_t* counters;
-  const float* u;
+  const uint16_t* u2;
+  const int32_t* blk_e;
+  const uint32_t* blk_tl;
+  const int32_t* tinfo;
   void* out;
-  int T, top_k, E, L, H, rank, padded_rows;
+  long cap;
+  int L, H, rank, maxblk, max_tiles, nch;
   int out_f32;
-  int h_splits;  // H ranges per item
 };
 
-__device__ __forceinline__ void split_hi_lo(float v, uint32_t& hi, uint32_t& lo) {
-  hi = f32_to_bf16_rne(v);
-  lo = f32_to_bf16_rne(v - bf16_bits_to_f32(hi));
+// accumulator rows of EXP_CW floats; 16-byte chunk c of row tl sits at c ^ (tl & 31)
+__device__ __forceinline__ int acc_chunk(int tl, int c) {
+  return tl * (EXP_CW / 4) + (c ^ (tl & 31));
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void expand_kernel(ExpandArgs p) {
-  constexpr int TT = NW * EXP_TOK_PER_WAVE;
-  extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
-  // [TT][top_k] sorted expert ids (int32), [TT][top_k][2][rank] bf16 hi/lo u,
-  // 2 x [EXP_HC][rank] bf16 B stage
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = p.top_k, R = p.rank;
-  int32_t* s_eid = reinterpret_cast<int32_t*>(dsmem);
-  uint16_t* s_u = reinterpret_cast<uint16_t*>(dsmem + al256(TT * K * 4));
-  uint16_t* s_b = s_u + static_cast<long>(TT) * K * 2 * R;
-  __shared__ int s_ntok;
+template <int NB>
+struct Ring {  // operands of one 16-slot block, loaded D blocks ahead
+  u32x4 fu[NB];     // u_hi / u_lo fragment
+  u32x4 fb[2][NB];  // B_le fragments of this wavefront's two 16-column groups
+  uint32_t tw;      // the 4 token-row bytes around this lane's slot
+};
 
-  const int n_items = p.counters[1];
-  const long total = static_cast<long>(n_items) * p.h_splits;
-  const int hrange = p.H / p.h_splits;  // multiple of EXP_HC or the whole H
-  for (long w = blockIdx.x; w < total; w += gridDim.x) {
-    const Item item = p.items[w / p.h_splits];
-    const int hs = static_cast<int>(w % p.h_splits);
-    const int h_begin = hs * hrange, h_end = h_begin + hrange;
-    __syncthreads();  // LDS reuse across iterations
+template <int NB>
+__global__ __launch_bounds__(NT_DELTA) void expand_kernel(ExpandArgs p) {
+  constexpr int D = NB == 1 ? 8 : (NB == 2 ? 4 : (NB == 4 ? 2 : 1));  // ring depth
+  __shared__ __attribute__((aligned(16))) float s_acc[128 * EXP_CW];
+  __shared__ const uint16_t* s_bp[MAX_BLOCKS];  // B_le of each block
 
-    if (item.key >= p.L) {  // no adapter: +0 rows
-      for (int i = wave; i < item.count; i += NW) {
-        const int t = p.tok_list[item.start + i];
-        for (int h = h_begin + lane * 4; h < h_end; h += 256) {
-          if (p.out_f32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + static_cast<long>(t) * p.H + h) =
-                f32x4{0.f, 0.f, 0.f, 0.f};
+  // XCD-aware order: workgroup id -> (XCD = id % 8, k-th on it); each XCD owns
+  // a contiguous run of (column chunk, tile) pairs, tiles fastest, so the
+  // tiles of one adapter that read the same B columns share that XCD's L2.
+  const int per = gridDim.x >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int ti = lin % p.max_tiles, ch = lin / p.max_tiles;
+  if (ch >= p.nch || ti >= gld<int>(p.counters)) return;
+  const Tile tile = load_tile(p.tiles + ti);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h0 = ch * EXP_CW;
+
+  if (tile.bucket >= p.L) {  // no adapter: +0 rows
+    for (int i = tid; i < tile.count * (EXP_CW / 4); i += NT_DELTA) {
+      const int tl = i / (EXP_CW / 4), c = (i % (EXP_CW / 4)) * 4;
+      const long o = static_cast<long>(gld<int>(p.tok_list + tile.start + tl)) * p.H + h0 + c;
+      if (p.out_f32)
+        gst<f32x4>(static_cast<float*>(p.out) + o, f32x4{0.f, 0.f, 0.f, 0.f});
+      else
+        gst<uint64_t>(static_cast<uint16_t*>(p.out) + o, 0ull);
+    }
+    return;
+  }
+  const int l = tile.bucket;
+  const int nblk = gld<int>(p.tinfo + 2 * ti);
+  const bool dup = gld<int>(p.tinfo + 2 * ti + 1) != 0;
+  const int32_t* be = p.blk_e + static_cast<long>(ti) * p.maxblk;
+  for (int i = tid; i < nblk; i += NT_DELTA)
+    s_bp[i] = reinterpret_cast<const uint16_t*>(gld<int64_t>(p.w_ptr_b + gld<int>(be + i))) +
+              static_cast<long>(l) * p.stride_b;
+  for (int i = tid * 4; i < tile.count * EXP_CW; i += NT_DELTA * 4)
+    *reinterpret_cast<f32x4*>(s_acc + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  if (nblk > 0) {
+    const int R = p.rank;
+    const int col = lane & 15, kq = lane >> 4;
+    // B_le is [hidden, rank]: this lane reads 8 ranks of column h0 + 32*wave + 16*g + col
+    const long hoff = static_cast<long>(h0 + 32 * wave + col) * R;
+    int roff[NB];
+    bool rin[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      const int r8 = c * 16 + (kq & 1) * 8;
+      rin[c] = r8 < R;
+      roff[c] = rin[c] ? r8 : R - 8;  // clamped: stays inside the column, masked below
+    }
+    const uint16_t* u2t = p.u2 + static_cast<long>(ti) * p.cap * NB * 32 + lane * 8;
+    const uint32_t* tlt = p.blk_tl + static_cast<long>(ti) * p.maxblk * 4 + (col >> 2);
+    const int tsh = (col & 3) * 8;
+
+    // every block index is clamped to the last block, so each ring step issues
+    // the same loads and the counter-based waits stay exact
+    auto load = [&](Ring<NB>& r, int i) {
+      const int ic = min(i, nblk - 1);
+      const uint16_t* rec = u2t + static_cast<long>(ic) * NB * 512;
+#pragma unroll
+      for (int c = 0; c < NB; ++c) r.fu[c] = gld<u32x4>(rec + c * 512);  // coalesced 1 KiB
+      const uint16_t* bp = s_bp[ic] + hoff;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int c = 0; c < NB; ++c) r.fb[g][c] = gld<u32x4>(bp + g * 16 * R + roff[c]);
+      r.tw = gld<uint32_t>(tlt + ic * 4);
+    };
+    auto consume = [&](const Ring<NB>& r, bool valid) {
+      f32x4 acc[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+          const u32x4 fb = rin[c] ? r.fb[g][c] : u32x4{0, 0, 0, 0};
+          // [B | B] (16 columns x 32) times [u_hi ; u_lo] (32 x 16 slots)
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb),
+                                                           __builtin_bit_cast(bf16x8, r.fu[c]),
+                                                           acc[g], 0, 0, 0);
+        }
+      }
+      // lane: slot `col` of the block, columns 32*wave + 16*g + 4*kq .. +3
+      const uint32_t tl = (r.tw >> tsh) & 0xFFu;
+      if (valid && tl != 0xFFu) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          f32x4* a = reinterpret_cast<f32x4*>(s_acc) + acc_chunk(tl, 8 * wave + 4 * g + kq);
+          if (!dup) {
+            f32x4 v = *a;
+            v.x += acc[g].x;
+            v.y += acc[g].y;
+            v.z += acc[g].z;
+            v.w += acc[g].w;
+            *a = v;
           } else {
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + static_cast<long>(t) * p.H +
-                                      h) = make_uint2(0u, 0u);
+            float* fp = reinterpret_cast<float*>(a);
+            atomicAdd(fp + 0, acc[g].x);
+            atomicAdd(fp + 1, acc[g].y);
+            atomicAdd(fp + 2, acc[g].z);
+            atomicAdd(fp + 3, acc[g].w);
           }
         }
       }
-      continue;
+    };
+
+    Ring<NB> ring[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(ring[d], d);
+    for (int i0 = 0; i0 < nblk; i0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        consume(ring[d], i0 + d < nblk);
+        load(ring[d], i0 + d + D);
+      }
     }
-    const int l = item.key;
-
-    // ---- setup: per token, its active slots sorted by expert, u as bf16 hi/lo ----
-    for (int i = tid; i < TT; i += 64 * NW) {
-      int32_t* te = s_eid + i * K;
-      uint16_t* tu = s_u + static_cast<long>(i) * K * 2 * R;
-      int n = 0;
-      if (i < item.count) {
-        const int t = p.tok_list[item.start + i];
-        for (int j = 0; j < K; ++j) {  // insertion sort of (expert, slot) keys
-          const int x = t * K + j;
-          const int e = p.topk_ids[x], r = p.perm[x];
-          if (r < 0 || r >= p.padded_rows || e < 0 || e >= p.E) continue;
-          const int key = (e << 5) | j;
-          int pos = n++;
-          while (pos > 0 && te[pos - 1] > key) {
-            te[pos] = te[pos - 1];
-            --pos;
-          }
-          te[pos] = key;
-        }
-        // merge slots of the same expert (their u are summed), store hi/lo
-        int m = 0;
-        for (int a = 0; a < n; ++a) {
-          const int key = te[a];
-          const int e = key >> 5, j = key & 31;
-          const float* us = p.u + static_cast<long>(t * K + j) * R;
-          if (m > 0 && te[m - 1] == e) {
-            uint16_t* dst = tu + (m - 1) * 2 * R;
-            for (int rr = 0; rr < R; ++rr) {
-              const float prev = bf16_bits_to_f32(dst[rr]) + bf16_bits_to_f32(dst[R + rr]);
-              uint32_t hi, lo;
-              split_hi_lo(prev + us[rr], hi, lo);
-              dst[rr] = static_cast<uint16_t>(hi);
-              dst[R + rr] = static_cast<uint16_t>(lo);
-            }
-            continue;
-          }
-          te[m] = e;  // m <= a: entry a was read above
-          uint16_t* dst = tu + m * 2 * R;
-          for (int rr = 0; rr < R; ++rr) {
-            uint32_t hi, lo;
-            split_hi_lo(us[rr], hi, lo);
-            dst[rr] = static_cast<uint16_t>(hi);
-            dst[R + rr] = static_cast<uint16_t>(lo);
-          }
-          ++m;
-        }
-        n = m;
-      }
-      for (int a = n; a < K; ++a) te[a] = 0x7fffffff;  // sentinel
-    }
-    __syncthreads();
-
-    // ---- per wave: 32 tokens; lane -> token lane%32, rank half kl ----
-    const int tl = wave * EXP_TOK_PER_WAVE + (lane & 31);
-    const int kl = lane >> 5;
-    const int32_t* my_e = s_eid + tl * K;
-    const uint16_t* my_u = s_u + static_cast<long>(tl) * K * 2 * R;
-
-    for (int h0 = h_begin; h0 < h_end; h0 += EXP_HC) {
-      f32x16 acc[EXP_HC / 32];
-#pragma unroll
-      for (int hb = 0; hb < EXP_HC / 32; ++hb)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[hb][q] = 0.f;
-      int ptr = 0;
-      int next_e = my_e[0];
-
-      const long bchunk = static_cast<long>(EXP_HC) * R;  // elements per expert chunk
-      // stage expert 0
-      auto stage = [&](int e, int buf) {
-        const uint16_t* src = reinterpret_cast<const uint16_t*>(p.w_ptr_b[e]) +
-                              static_cast<long>(l) * p.stride_b + static_cast<long>(h0) * R;
-        uint16_t* dst = s_b + buf * bchunk;
-        for (long c = tid * 8; c < bchunk; c += 64 * NW * 8)
-          *reinterpret_cast<u32x4*>(dst + c) = *reinterpret_cast<const u32x4*>(src + c);
-      };
-      __syncthreads();
-      stage(0, 0);
-      __syncthreads();
-      for (int e = 0; e < p.E; ++e) {
-        const int buf = e & 1;
-        if (e + 1 < p.E) stage(e + 1, buf ^ 1);
-        const bool has = (next_e == e);
-        const uint16_t* ub = my_u + ptr * 2 * R;
-        const uint16_t* sb = s_b + buf * bchunk;
-        for (int r0 = 0; r0 < R; r0 += 16) {
-          u32x4 hi = {0, 0, 0, 0}, lo = {0, 0, 0, 0};
-          const bool kin = r0 + kl * 8 < R;
-          if (has && kin) {
-            hi = *reinterpret_cast<const u32x4*>(ub + r0 + kl * 8);
-            lo = *reinterpret_cast<const u32x4*>(ub + R + r0 + kl * 8);
-          }
-#pragma unroll
-          for (int hb = 0; hb < EXP_HC / 32; ++hb) {
-            u32x4 fb = {0, 0, 0, 0};
-            if (kin)
-              fb = *reinterpret_cast<const u32x4*>(sb + static_cast<long>(hb * 32 + (lane & 31)) * R +
-                                                   r0 + kl * 8);
-            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hi),
-                                                              __builtin_bit_cast(bf16x8, fb),
-                                                              acc[hb], 0, 0, 0);
-            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, lo),
-                                                              __builtin_bit_cast(bf16x8, fb),
-                                                              acc[hb], 0, 0, 0);
-          }
-        }
-        if (has) {
-          ++ptr;
-          next_e = ptr < K ? my_e[ptr] : 0x7fffffff;
-        }
-        __syncthreads();
-      }
-      // ---- store: token row = 8*(q/4) + 4*(lane/32) + q%4 of the wave, col lane%32 ----
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int tr = wave * EXP_TOK_PER_WAVE + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        if (tr < item.count) {
-          const int t = p.tok_list[item.start + tr];
-#pragma unroll
-          for (int hb = 0; hb < EXP_HC / 32; ++hb) {
-            const long o = static_cast<long>(t) * p.H + h0 + hb * 32 + (lane & 31);
-            if (p.out_f32)
-              static_cast<float*>(p.out)[o] = acc[hb][q];
-            else
-              static_cast<uint16_t*>(p.out)[o] = static_cast<uint16_t>(f32_to_bf16_rne(acc[hb][q]));
-          }
-        }
-      }
+  }
+  __syncthreads();
+  // write out: 8 columns per thread-iteration
+  for (int i = tid; i < tile.count * (EXP_CW / 8); i += NT_DELTA) {
+    const int tl = i / (EXP_CW / 8), c = (i % (EXP_CW / 8)) * 8;
+    const f32x4* a = reinterpret_cast<const f32x4*>(s_acc);
+    const long o = static_cast<long>(gld<int>(p.tok_list + tile.start + tl)) * p.H + h0 + c;
+    const f32x4 v0 = a[acc_chunk(tl, c / 4)];
+    const f32x4 v1 = a[acc_chunk(tl, c / 4 + 1)];
+    if (p.out_f32) {
+      gst<f32x4>(static_cast<float*>(p.out) + o, v0);
+      gst<f32x4>(static_cast<float*>(p.out) + o + 4, v1);
+    } else {
+      u32x4 w;
+      w.x = pack_bf16x2(v0.x, v0.y);
+      w.y = pack_bf16x2(v0.z, v0.w);
+      w.z = pack_bf16x2(v1.x, v1.y);
+      w.w = pack_bf16x2(v1.z, v1.w);
+      gst<u32x4>(static_cast<uint16_t*>(p.out) + o, w);
     }
   }
 }
@@ -511,7 +699,9 @@ int num_cus() {
 extern "C" size_t mi_moe_fc2_lora_delta_workspace_size(int64_t num_tokens, int64_t top_k,
                                                        int64_t num_experts, int64_t num_adapters,
                                                        int64_t rank) {
-  if (num_tokens < 0 || top_k < 1 || num_experts < 1 || num_adapters < 0 || rank < 1) return 0;
+  if (num_tokens < 0 || top_k < 1 || top_k > mi::MAX_TOPK || num_experts < 1 ||
+      num_adapters < 0 || rank < 1)
+    return 0;
   return mi::layout(num_tokens, top_k, num_experts, num_adapters, rank).total;
 }
 
@@ -523,14 +713,14 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
     mi_dtype out_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   using namespace mi;
   clear_error();
-  MI_REQUIRE(T >= 0 && T < (1LL << 26), "bgmv_moe_gemm2_lora_delta: num_tokens out of range");
   MI_REQUIRE(top_k >= 1 && top_k <= MAX_TOPK, "bgmv_moe_gemm2_lora_delta: top_k must be in [1, %d]",
              MAX_TOPK);
-  MI_REQUIRE(E >= 1 && E <= 32767, "bgmv_moe_gemm2_lora_delta: num_experts must be in [1, 32767]");
+  MI_REQUIRE(T >= 0 && T * top_k < (1LL << 24),
+             "bgmv_moe_gemm2_lora_delta: num_tokens * top_k must be < 2^24");
+  MI_REQUIRE(E >= 1 && E <= MAX_EXPERTS,
+             "bgmv_moe_gemm2_lora_delta: num_experts must be in [1, %d]", MAX_EXPERTS);
   MI_REQUIRE(L >= 0 && L <= MAX_ADAPTERS,
              "bgmv_moe_gemm2_lora_delta: num_adapters must be in [0, %d]", MAX_ADAPTERS);
-  MI_REQUIRE(L * E <= MAX_KEYS,
-             "bgmv_moe_gemm2_lora_delta: num_adapters * num_experts must be <= %d", MAX_KEYS);
   MI_REQUIRE(rank >= 8 && rank <= 128 && rank % 8 == 0,
              "bgmv_moe_gemm2_lora_delta: rank must be a multiple of 8 in [8, 128] (got %lld)",
              (long long)rank);
@@ -538,9 +728,9 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
              "bgmv_moe_gemm2_lora_delta: I = gemm1_activation_output.shape[1] must be a positive "
              "multiple of 8 (got %lld)", (long long)inter_size);
   MI_REQUIRE(H >= 1 && H < (1 << 30), "bgmv_moe_gemm2_lora_delta: hidden_size out of range");
-  MI_REQUIRE_SUPPORTED(H % 128 == 0,
-                       "bgmv_moe_gemm2_lora_delta: hidden_size must be a multiple of 128 (got %lld)",
-                       (long long)H);
+  MI_REQUIRE_SUPPORTED(H % EXP_CW == 0,
+                       "bgmv_moe_gemm2_lora_delta: hidden_size must be a multiple of %d (got %lld)",
+                       EXP_CW, (long long)H);
   MI_REQUIRE(lora_stride_a >= 0 && lora_stride_a % 8 == 0 && lora_stride_b >= 0 &&
                  lora_stride_b % 8 == 0,
              "bgmv_moe_gemm2_lora_delta: lora strides must be non-negative multiples of 8 "
@@ -551,8 +741,6 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   MI_REQUIRE(out_dtype == MI_BF16 || out_dtype == MI_F32 || out_dtype == MI_F16,
              "bgmv_moe_gemm2_lora_delta: out_dtype must be bf16, fp16 or fp32");
   MI_REQUIRE_SUPPORTED(out_dtype != MI_F16, "bgmv_moe_gemm2_lora_delta: fp16 output not implemented");
-  const int ew = expand_waves(top_k, rank);
-  MI_REQUIRE_SUPPORTED(ew >= 1, "bgmv_moe_gemm2_lora_delta: top_k * rank must be <= 512");
   if (T == 0) return MI_OK;
   MI_REQUIRE(out != nullptr, "bgmv_moe_gemm2_lora_delta: out is null");
   MI_REQUIRE(aligned16(out), "bgmv_moe_gemm2_lora_delta: out must be 16-byte aligned");
@@ -572,67 +760,60 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* u = reinterpret_cast<float*>(ws + ly.u);
-  int32_t* slot_list = reinterpret_cast<int32_t*>(ws + ly.slot_list);
+  uint16_t* u2 = reinterpret_cast<uint16_t*>(ws + ly.u2);
   int32_t* tok_list = reinterpret_cast<int32_t*>(ws + ly.tok_list);
-  Item* shrink_items = reinterpret_cast<Item*>(ws + ly.shrink_items);
-  Item* expand_items = reinterpret_cast<Item*>(ws + ly.expand_items);
+  Tile* tiles = reinterpret_cast<Tile*>(ws + ly.tiles);
   int32_t* counters = reinterpret_cast<int32_t*>(ws + ly.counters);
-  const int tt = ew * EXP_TOK_PER_WAVE;
+  int32_t* blk_e = reinterpret_cast<int32_t*>(ws + ly.blk_e);
+  uint32_t* blk_tl = reinterpret_cast<uint32_t*>(ws + ly.blk_tl);
+  int32_t* tinfo = reinterpret_cast<int32_t*>(ws + ly.tinfo);
+  const int tt = tile_tokens(top_k);
+  const int ntiles = static_cast<int>(max_tiles(T, top_k, L));
 
-  PlanArgs pa{perm, topk_ids, lora_ids, static_cast<int>(T), static_cast<int>(top_k),
-              static_cast<int>(E), static_cast<int>(L), static_cast<int>(padded_rows), tt,
-              slot_list, tok_list, shrink_items, expand_items, counters};
+  PlanArgs pa{lora_ids, static_cast<int>(T), static_cast<int>(L), tt, tok_list, tiles, counters};
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, pa);
   mi_status st = launch_status("bgmv_moe_gemm2_lora_delta (plan)");
   if (st != MI_OK) return st;
 
+  const SlotSrc src{tok_list, perm, topk_ids, static_cast<int>(top_k),
+                    static_cast<int>(padded_rows), static_cast<int>(E)};
   const int cus = num_cus();
+  const int nb = rank_chunks(rank);
   if (L > 0) {
-    ShrinkArgs sa{static_cast<const uint16_t*>(act), perm, w_ptr_a, static_cast<long>(lora_stride_a),
-                  topk_weights, slot_list, shrink_items, counters, u, static_cast<int>(inter_size),
-                  static_cast<int>(E), static_cast<int>(rank), scale};
-    const dim3 sgrid(cus * 8), sblock(256);
-    switch ((rank + 15) / 16) {
+    // experts per shrink workgroup: enough workgroups to cover the chip ~4x
+    const int64_t est_tiles = T / tt + 1;
+    int64_t groups = (4 * cus + est_tiles - 1) / est_tiles;
+    if (groups > E) groups = E;
+    if (groups < 1) groups = 1;
+    const int epg = static_cast<int>((E + groups - 1) / groups);
+    const int ngroups = static_cast<int>((E + epg - 1) / epg);
+    ShrinkArgs sa{src, static_cast<const uint16_t*>(act), w_ptr_a, static_cast<long>(lora_stride_a),
+                  topk_weights, tiles, counters, u2, blk_e, blk_tl, tinfo, ly.cap,
+                  static_cast<int>(inter_size), static_cast<int>(L), static_cast<int>(rank), epg,
+                  ly.maxblk, scale};
+    const dim3 sgrid(ntiles, ngroups), sblock(NT_DELTA);
+    switch (nb) {
       case 1: hipLaunchKernelGGL(shrink_kernel<1>, sgrid, sblock, 0, s, sa); break;
       case 2: hipLaunchKernelGGL(shrink_kernel<2>, sgrid, sblock, 0, s, sa); break;
-      case 3: hipLaunchKernelGGL(shrink_kernel<3>, sgrid, sblock, 0, s, sa); break;
       case 4: hipLaunchKernelGGL(shrink_kernel<4>, sgrid, sblock, 0, s, sa); break;
-      case 5: hipLaunchKernelGGL(shrink_kernel<5>, sgrid, sblock, 0, s, sa); break;
-      case 6: hipLaunchKernelGGL(shrink_kernel<6>, sgrid, sblock, 0, s, sa); break;
-      case 7: hipLaunchKernelGGL(shrink_kernel<7>, sgrid, sblock, 0, s, sa); break;
       default: hipLaunchKernelGGL(shrink_kernel<8>, sgrid, sblock, 0, s, sa); break;
     }
     st = launch_status("bgmv_moe_gemm2_lora_delta (shrink)");
     if (st != MI_OK) return st;
   }
 
-  // H split: enough workgroups to cover the chip
-  int h_splits = 1;
-  const int64_t est_items = T / tt + 1;
-  while (H % (EXP_HC * h_splits * 2) == 0 && est_items * h_splits < 2 * cus) h_splits *= 2;
-  ExpandArgs ea{perm, topk_ids, w_ptr_b, static_cast<long>(lora_stride_b), tok_list, expand_items,
-                counters, u, out, static_cast<int>(T), static_cast<int>(top_k), static_cast<int>(E),
-                static_cast<int>(L), static_cast<int>(H), static_cast<int>(rank),
-                static_cast<int>(padded_rows), out_dtype == MI_F32 ? 1 : 0, h_splits};
-  const size_t lds = al256(tt * top_k * 4) + static_cast<size_t>(tt) * top_k * 2 * rank * 2 +
-                     2 * static_cast<size_t>(EXP_HC) * rank * 2;
-  const dim3 egrid(cus * 2);
-  static bool lds_attr_set[4] = {false, false, false, false};
-  if (!lds_attr_set[ew - 1]) {
-    const void* fn = ew == 1 ? reinterpret_cast<const void*>(expand_kernel<1>)
-                   : ew == 2 ? reinterpret_cast<const void*>(expand_kernel<2>)
-                   : ew == 3 ? reinterpret_cast<const void*>(expand_kernel<3>)
-                             : reinterpret_cast<const void*>(expand_kernel<4>);
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) ==
-        hipSuccess)
-      lds_attr_set[ew - 1] = true;
-  }
-  switch (ew) {
-    case 1: hipLaunchKernelGGL(expand_kernel<1>, egrid, dim3(64), lds, s, ea); break;
-    case 2: hipLaunchKernelGGL(expand_kernel<2>, egrid, dim3(128), lds, s, ea); break;
-    case 3: hipLaunchKernelGGL(expand_kernel<3>, egrid, dim3(192), lds, s, ea); break;
-    default: hipLaunchKernelGGL(expand_kernel<4>, egrid, dim3(256), lds, s, ea); break;
+  const int nch = static_cast<int>(H / EXP_CW);
+  ExpandArgs ea{tok_list, w_ptr_b, static_cast<long>(lora_stride_b), tiles, counters, u2, blk_e,
+                blk_tl, tinfo, out, ly.cap, static_cast<int>(L), static_cast<int>(H),
+                static_cast<int>(rank), ly.maxblk, ntiles, nch, out_dtype == MI_F32 ? 1 : 0};
+  const long ewg = (static_cast<long>(ntiles) * nch + 7) & ~7L;  // a multiple of the 8 XCDs
+  MI_REQUIRE(ewg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
+  const dim3 egrid(static_cast<unsigned>(ewg)), eblock(NT_DELTA);
+  switch (nb) {
+    case 1: hipLaunchKernelGGL(expand_kernel<1>, egrid, eblock, 0, s, ea); break;
+    case 2: hipLaunchKernelGGL(expand_kernel<2>, egrid, eblock, 0, s, ea); break;
+    case 4: hipLaunchKernelGGL(expand_kernel<4>, egrid, eblock, 0, s, ea); break;
+    default: hipLaunchKernelGGL(expand_kernel<8>, egrid, eblock, 0, s, ea); break;
   }
   return launch_status("bgmv_moe_gemm2_lora_delta (expand)");
 }
