@@ -67,7 +67,7 @@ __device__ __forceinline__ void store_tile(Tile* t, const Tile& v) {
 }
 
 struct Layout {
-  size_t u2, tok_list, tiles, counters, blk_e, blk_tl, tinfo, total;
+  size_t u2, tok_list, tiles, counters, blk_b, blk_tl, tinfo, total;
   long cap;     // padded slot positions per tile
   int maxblk;   // 16-slot blocks per tile, at most
 };
@@ -109,8 +109,8 @@ Layout layout(int64_t T, int64_t top_k, int64_t E, int64_t L, int64_t rank) {
   off = al256(off + 64);
   const size_t mt = static_cast<size_t>(max_tiles(T, top_k, L));
   ly.maxblk = static_cast<int>(ly.cap / 16 + 1);
-  ly.blk_e = off;  // expert of each block
-  off = al256(off + mt * ly.maxblk * 4);
+  ly.blk_b = off;  // address of each block's B_le
+  off = al256(off + mt * ly.maxblk * 8);
   ly.blk_tl = off;  // token row (tile-local) of each of a block's 16 slots, 0xFF = empty
   off = al256(off + mt * ly.maxblk * 16);
   ly.tinfo = off;  // per tile: number of blocks, "a token repeats an expert" flag
@@ -296,10 +296,11 @@ __device__ void list_slots(const SlotSrc& s, const Tile& tile, SlotLists& L) {
   __syncthreads();
 }
 
-// u2 record of one 16-slot block: NB chunks x [4 parts][16 slots][8 bf16];
-// parts 0, 1 = hi of the chunk's ranks 0-7 / 8-15, parts 2, 3 = lo.
-__device__ __forceinline__ int u2_elem(int c, int part, int slot, int r8) {
-  return c * 512 + part * 128 + slot * 8 + r8;
+// u2 record of one 16-slot block: NB chunks of 16 ranks, each 64 lane groups
+// of 8 bf16 -- the MFMA operand of lane (slot, q) = slot + 16 q, which holds
+// hi then lo of ranks 4q .. 4q+3 of the chunk (part 0 = hi, 1 = lo).
+__device__ __forceinline__ int u2_elem(int c, int part, int slot, int rr) {
+  return c * 512 + ((rr >> 2) * 16 + slot) * 8 + part * 4 + (rr & 3);
 }
 
 // ---------------------------------------------------------------------------
@@ -314,7 +315,9 @@ struct ShrinkArgs {
   const Tile* tiles;
   const int32_t* counters;
   uint16_t* u2;
-  int32_t* blk_e;
+  const int64_t* w_ptr_b;
+  long stride_b;
+  int64_t* blk_b;
   uint32_t* blk_tl;
   int32_t* tinfo;
   long cap;
@@ -323,21 +326,23 @@ struct ShrinkArgs {
 };
 
 // The block table of a tile, for the expand: blocks in expert order (the u2
-// record of block i is record i), each with its expert and the tile-local
-// token row of its 16 slots.  Also flags a token that routes to one expert
+// record of block i is record i), each with the address of its B_le and the
+// tile-local token row of its 16 slots.  Also flags a token that routes to one expert
 // twice (a block would then hold that token twice).
 __device__ void write_block_table(const SlotLists& L, int E, int ti, const ShrinkArgs& p) {
   int dup = 0;
-  int32_t* be = p.blk_e + static_cast<long>(ti) * p.maxblk;
+  int64_t* bb = p.blk_b + static_cast<long>(ti) * p.maxblk;
+  const int l = load_tile(p.tiles + ti).bucket;
   uint32_t* bt = p.blk_tl + static_cast<long>(ti) * p.maxblk * 4;
   for (int e = threadIdx.x; e < E; e += NT_DELTA) {
     const int b0 = L.off[e], n = L.off[e + 1] - b0;
     for (int i = 1; i < n; ++i)
       dup |= (static_cast<uint32_t>(L.list[b0 + i]) >> 24) ==
              (static_cast<uint32_t>(L.list[b0 + i - 1]) >> 24);
+    const int64_t ble = n > 0 ? gld<int64_t>(p.w_ptr_b + e) + 2 * p.stride_b * l : 0;
     for (int b = 0; b * 16 < n; ++b) {
       const int bi = (L.poff[e] >> 4) + b;
-      gst<int>(be + bi, e);
+      gst<int64_t>(bb + bi, ble);
       uint32_t w[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -501,9 +506,8 @@ __global__ __launch_bounds__(NT_DELTA) void shrink_kernel(ShrinkArgs p) {
         const float v = nb * 16 + row < p.rank ? acc[nb][q] * f : 0.f;
         const uint32_t hi = f32_to_bf16_rne(v);
         const uint32_t lo = f32_to_bf16_rne(v - bf16_bits_to_f32(hi));
-        gst<uint16_t>(rec + u2_elem(nb, row >> 3, srow, row & 7), static_cast<uint16_t>(hi));
-        gst<uint16_t>(rec + u2_elem(nb, 2 + (row >> 3), srow, row & 7),
-                      static_cast<uint16_t>(lo));
+        gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), static_cast<uint16_t>(hi));
+        gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), static_cast<uint16_t>(lo));
       }
     }
   }
@@ -512,17 +516,19 @@ __global__ __launch_bounds__(NT_DELTA) void shrink_kernel(ShrinkArgs p) {
 // ---------------------------------------------------------------------------
 // 3. expand
 // ---------------------------------------------------------------------------
-constexpr int EXP_CW = 128;  // output columns per workgroup: 4 wavefronts x 2 x 16
+constexpr int EXP_CW = 128;   // output columns per workgroup
+constexpr int NT_EXP = 256;   // expand workgroup: 4 wavefronts x 2 groups of 16 columns
+constexpr int EXP_NCG = EXP_CW / 16 / (NT_EXP / 64);  // 16-column groups per wavefront
+constexpr int EXP_TT = 128;   // accumulator rows (tokens per tile, at most)
 constexpr int MAX_BLOCKS = SLOT_BUDGET / 16 + MAX_EXPERTS;
+static_assert(EXP_CW == 16 * EXP_NCG * (NT_EXP / 64), "column groups");
 
 struct ExpandArgs {
   const int32_t* tok_list;
-  const int64_t* w_ptr_b;
-  long stride_b;
   const Tile* tiles;
   const int32_t* counters;
   const uint16_t* u2;
-  const int32_t* blk_e;
+  const int64_t* blk_b;
   const uint32_t* blk_tl;
   const int32_t* tinfo;
   void* out;
@@ -536,33 +542,183 @@ __device__ __forceinline__ int acc_chunk(int tl, int c) {
   return tl * (EXP_CW / 4) + (c ^ (tl & 31));
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int NB>
 struct Ring {  // operands of one 16-slot block, loaded D blocks ahead
-  u32x4 fu[NB];     // u_hi / u_lo fragment
-  u32x4 fb[2][NB];  // B_le fragments of this wavefront's two 16-column groups
-  uint32_t tw;      // the 4 token-row bytes around this lane's slot
+  u32x4 fu[NB];  // u fragment: hi and lo of 4 ranks
+  u32x2 fb[EXP_NCG][NB];  // B_le: the same 4 ranks of each of the wavefront's column groups
+  uint32_t tw;   // the 4 token-row bytes around this lane's slot
 };
 
-template <int NB>
-__global__ __launch_bounds__(NT_DELTA) void expand_kernel(ExpandArgs p) {
+// raw buffer resource (gfx9 layout: dword 3 = 0x00020000) over `bytes` bytes
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 buf_ld64(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                             uint32_t soff) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// The block loop of one wavefront.  PART: 16 * NB > rank, so some rank
+// chunks are partly or wholly past the rank (those ranks are masked to zero in
+// B, which may hold anything there; u is zero there).
+// DUP: a block may hold a token twice, so accumulate with LDS atomics.
+template <int NB, bool PART, bool DUP>
+__device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* const* s_bp,
+                                              const char* u2t, const char* tlt, int nblk,
+                                              int R, int H, int h0) {
   constexpr int D = NB == 1 ? 8 : (NB == 2 ? 4 : (NB == 4 ? 2 : 1));  // ring depth
-  __shared__ __attribute__((aligned(16))) float s_acc[128 * EXP_CW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kq = lane >> 4;
+  // byte offsets of this lane inside a block's u record, B_le, token-row table
+  const uint32_t uoff = lane * 16;
+  uint32_t boff[EXP_NCG][NB];
+  bool rin[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    const int r4 = c * 16 + kq * 4;  // rank % 8 == 0: ranks r4 .. r4+3 are all in or all out
+    rin[c] = r4 < R;
+#pragma unroll
+    for (int g = 0; g < EXP_NCG; ++g)
+      // B_le is [hidden, rank]; column h0 + 16*(EXP_NCG*wave + g) + col, ranks r4 .. r4+3
+      // (clamped into the column when past the rank; masked below)
+      boff[g][c] = 2u * (static_cast<uint32_t>(h0 + 16 * (EXP_NCG * wave + g) + col) * R +
+                         (rin[c] ? r4 : R - 4));
+  }
+  const uint32_t toff = (col >> 2) * 4;
+  const int tsh = (col & 3) * 8;
+  const int ca = 4 * EXP_NCG * wave + kq;  // accumulator chunk of group 0 (group g: + 4g)
+  f32x4* acc4 = reinterpret_cast<f32x4*>(s_acc);
+
+  // every block index is clamped to the last block, so each ring step issues
+  // the same loads and the counter-based waits stay exact.  Buffer loads: the
+  // per-lane offsets are constants, the block offset is a scalar.
+  const __amdgpu_buffer_rsrc_t ursrc = buf_rsrc(u2t, static_cast<uint32_t>(nblk) * NB * 1024);
+  const __amdgpu_buffer_rsrc_t trsrc = buf_rsrc(tlt, static_cast<uint32_t>(nblk) * 16);
+  const uint32_t bbytes = static_cast<uint32_t>(H) * R * 2;  // one B_le
+  auto bptr = [&](int i) { return s_bp[min(i, nblk - 1)]; };
+  auto load = [&](Ring<NB>& r, int i, const uint16_t* bsrc) {
+    const uint32_t ic = static_cast<uint32_t>(min(i, nblk - 1));
+#pragma unroll
+    for (int c = 0; c < NB; ++c) r.fu[c] = buf_ld128(ursrc, c * 1024 + uoff, ic * NB * 1024);
+    const __amdgpu_buffer_rsrc_t brsrc = buf_rsrc(uniform_ptr(bsrc), bbytes);
+#pragma unroll
+    for (int g = 0; g < EXP_NCG; ++g)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) r.fb[g][c] = buf_ld64(brsrc, boff[g][c], 0);  // 512 B rows
+    r.tw = buf_ld32(trsrc, toff, ic * 16);
+  };
+  auto mma = [&](const Ring<NB>& r, f32x4 (&acc)[EXP_NCG]) {
+#pragma unroll
+    for (int g = 0; g < EXP_NCG; ++g) {
+      acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        u32x2 b4 = r.fb[g][c];
+        if (PART && !rin[c]) b4 = u32x2{0, 0};
+        const u32x4 fb = u32x4{b4.x, b4.y, b4.x, b4.y};
+        // K = 32 runs over (4 ranks, hi|lo) of every lane group q: [B | B]
+        // (16 columns x 32) times [u_hi ; u_lo] (32 x 16 slots)
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb),
+                                                         __builtin_bit_cast(bf16x8, r.fu[c]),
+                                                         acc[g], 0, 0, 0);
+      }
+    }
+  };
+  // token row of this lane's slot; an empty slot or a block past the end goes
+  // to spare row EXP_TT + col (written, never read back)
+  auto row_of = [&](const Ring<NB>& r, bool valid) {
+    const uint32_t tl = (r.tw >> tsh) & 0xFFu;
+    return (valid && tl != 0xFFu) ? static_cast<int>(tl) : EXP_TT + col;
+  };
+
+  // Software pipeline, one block per step: the accumulator rows of block i
+  // are read, block i+1 goes through the MFMAs and its ring slot is refilled
+  // with block i+1+D, then block i is added and written back.  (Blocks i and
+  // i+1 may share a token, so block i+1's rows are read only after block i's
+  // writes.)  The B_le addresses of a round of D refills are read from LDS
+  // together at its start.
+  Ring<NB> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(ring[d], d, bptr(d));
+  f32x4 acc[EXP_NCG];
+  mma(ring[0], acc);
+  int tl = row_of(ring[0], true);  // nblk > 0
+  load(ring[0], D, bptr(D));
+  for (int i0 = 0; i0 < nblk; i0 += D) {
+    const uint16_t* bpr[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) bpr[d] = bptr(i0 + d + 1 + D);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = i0 + d;
+      f32x4* a[EXP_NCG];
+      f32x4 v[EXP_NCG];
+#pragma unroll
+      for (int g = 0; g < EXP_NCG; ++g) a[g] = acc4 + acc_chunk(tl, ca + 4 * g);
+      if (!DUP) {
+#pragma unroll
+        for (int g = 0; g < EXP_NCG; ++g) v[g] = *a[g];
+      }
+      Ring<NB>& rn = ring[(d + 1) % D];  // holds block i+1
+      f32x4 accn[EXP_NCG];
+      mma(rn, accn);
+      const int tln = row_of(rn, i + 1 < nblk);
+      load(rn, i + 1 + D, bpr[d]);
+#pragma unroll
+      for (int g = 0; g < EXP_NCG; ++g) {
+        if (!DUP) {
+          *a[g] = v[g] + acc[g];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) atomicAdd(reinterpret_cast<float*>(a[g]) + q, acc[g][q]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < EXP_NCG; ++g) acc[g] = accn[g];
+      tl = tln;
+    }
+  }
+}
+
+// 2 workgroups per CU (LDS) = 2 wavefronts per SIMD
+template <int NB, bool PART>
+__global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
+  __shared__ __attribute__((aligned(16))) float s_acc[(EXP_TT + 16) * EXP_CW];  // + spare rows
   __shared__ const uint16_t* s_bp[MAX_BLOCKS];  // B_le of each block
 
-  // XCD-aware order: workgroup id -> (XCD = id % 8, k-th on it); each XCD owns
-  // a contiguous run of (column chunk, tile) pairs, tiles fastest, so the
-  // tiles of one adapter that read the same B columns share that XCD's L2.
+  // Workgroup order: the (column chunk, tile) pairs are taken in runs of
+  // TB tiles -- all chunks of a run, tiles fastest -- and every XCD gets a
+  // contiguous range of that order (the dispatcher deals workgroup ids to
+  // the 8 XCDs in turn).  The u records of a run's tiles then stay in one
+  // L2 while its chunks go by, and the run's tiles (mostly one adapter)
+  // read each chunk of B_l together.
+  constexpr int TB = 8;
   const int per = gridDim.x >> 3;
   const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  const int ti = lin % p.max_tiles, ch = lin / p.max_tiles;
-  if (ch >= p.nch || ti >= gld<int>(p.counters)) return;
+  const int run = lin / (TB * p.nch), rem = lin % (TB * p.nch);
+  const int ch = rem / TB, ti = run * TB + rem % TB;
+  if (ti >= p.max_tiles || ti >= gld<int>(p.counters)) return;
   const Tile tile = load_tile(p.tiles + ti);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   const int h0 = ch * EXP_CW;
 
   if (tile.bucket >= p.L) {  // no adapter: +0 rows
-    for (int i = tid; i < tile.count * (EXP_CW / 4); i += NT_DELTA) {
+    for (int i = tid; i < tile.count * (EXP_CW / 4); i += NT_EXP) {
       const int tl = i / (EXP_CW / 4), c = (i % (EXP_CW / 4)) * 4;
       const long o = static_cast<long>(gld<int>(p.tok_list + tile.start + tl)) * p.H + h0 + c;
       if (p.out_f32)
@@ -572,100 +728,26 @@ __global__ __launch_bounds__(NT_DELTA) void expand_kernel(ExpandArgs p) {
     }
     return;
   }
-  const int l = tile.bucket;
   const int nblk = gld<int>(p.tinfo + 2 * ti);
   const bool dup = gld<int>(p.tinfo + 2 * ti + 1) != 0;
-  const int32_t* be = p.blk_e + static_cast<long>(ti) * p.maxblk;
-  for (int i = tid; i < nblk; i += NT_DELTA)
-    s_bp[i] = reinterpret_cast<const uint16_t*>(gld<int64_t>(p.w_ptr_b + gld<int>(be + i))) +
-              static_cast<long>(l) * p.stride_b;
-  for (int i = tid * 4; i < tile.count * EXP_CW; i += NT_DELTA * 4)
+  const int64_t* bb = p.blk_b + static_cast<long>(ti) * p.maxblk;
+  for (int i = tid; i < nblk; i += NT_EXP)
+    s_bp[i] = reinterpret_cast<const uint16_t*>(gld<int64_t>(bb + i));
+  for (int i = tid * 4; i < tile.count * EXP_CW; i += NT_EXP * 4)
     *reinterpret_cast<f32x4*>(s_acc + i) = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
   if (nblk > 0) {
-    const int R = p.rank;
-    const int col = lane & 15, kq = lane >> 4;
-    // B_le is [hidden, rank]: this lane reads 8 ranks of column h0 + 32*wave + 16*g + col
-    const long hoff = static_cast<long>(h0 + 32 * wave + col) * R;
-    int roff[NB];
-    bool rin[NB];
-#pragma unroll
-    for (int c = 0; c < NB; ++c) {
-      const int r8 = c * 16 + (kq & 1) * 8;
-      rin[c] = r8 < R;
-      roff[c] = rin[c] ? r8 : R - 8;  // clamped: stays inside the column, masked below
-    }
-    const uint16_t* u2t = p.u2 + static_cast<long>(ti) * p.cap * NB * 32 + lane * 8;
-    const uint32_t* tlt = p.blk_tl + static_cast<long>(ti) * p.maxblk * 4 + (col >> 2);
-    const int tsh = (col & 3) * 8;
-
-    // every block index is clamped to the last block, so each ring step issues
-    // the same loads and the counter-based waits stay exact
-    auto load = [&](Ring<NB>& r, int i) {
-      const int ic = min(i, nblk - 1);
-      const uint16_t* rec = u2t + static_cast<long>(ic) * NB * 512;
-#pragma unroll
-      for (int c = 0; c < NB; ++c) r.fu[c] = gld<u32x4>(rec + c * 512);  // coalesced 1 KiB
-      const uint16_t* bp = s_bp[ic] + hoff;
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int c = 0; c < NB; ++c) r.fb[g][c] = gld<u32x4>(bp + g * 16 * R + roff[c]);
-      r.tw = gld<uint32_t>(tlt + ic * 4);
-    };
-    auto consume = [&](const Ring<NB>& r, bool valid) {
-      f32x4 acc[2];
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          const u32x4 fb = rin[c] ? r.fb[g][c] : u32x4{0, 0, 0, 0};
-          // [B | B] (16 columns x 32) times [u_hi ; u_lo] (32 x 16 slots)
-          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb),
-                                                           __builtin_bit_cast(bf16x8, r.fu[c]),
-                                                           acc[g], 0, 0, 0);
-        }
-      }
-      // lane: slot `col` of the block, columns 32*wave + 16*g + 4*kq .. +3
-      const uint32_t tl = (r.tw >> tsh) & 0xFFu;
-      if (valid && tl != 0xFFu) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          f32x4* a = reinterpret_cast<f32x4*>(s_acc) + acc_chunk(tl, 8 * wave + 4 * g + kq);
-          if (!dup) {
-            f32x4 v = *a;
-            v.x += acc[g].x;
-            v.y += acc[g].y;
-            v.z += acc[g].z;
-            v.w += acc[g].w;
-            *a = v;
-          } else {
-            float* fp = reinterpret_cast<float*>(a);
-            atomicAdd(fp + 0, acc[g].x);
-            atomicAdd(fp + 1, acc[g].y);
-            atomicAdd(fp + 2, acc[g].z);
-            atomicAdd(fp + 3, acc[g].w);
-          }
-        }
-      }
-    };
-
-    Ring<NB> ring[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) load(ring[d], d);
-    for (int i0 = 0; i0 < nblk; i0 += D) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        consume(ring[d], i0 + d < nblk);
-        load(ring[d], i0 + d + D);
-      }
-    }
+    const char* u2t = reinterpret_cast<const char*>(p.u2 + static_cast<long>(ti) * p.cap * NB * 32);
+    const char* tlt = reinterpret_cast<const char*>(p.blk_tl + static_cast<long>(ti) * p.maxblk * 4);
+    if (dup)
+      expand_blocks<NB, PART, true>(s_acc, s_bp, u2t, tlt, nblk, p.rank, p.H, h0);
+    else
+      expand_blocks<NB, PART, false>(s_acc, s_bp, u2t, tlt, nblk, p.rank, p.H, h0);
   }
   __syncthreads();
   // write out: 8 columns per thread-iteration
-  for (int i = tid; i < tile.count * (EXP_CW / 8); i += NT_DELTA) {
+  for (int i = tid; i < tile.count * (EXP_CW / 8); i += NT_EXP) {
     const int tl = i / (EXP_CW / 8), c = (i % (EXP_CW / 8)) * 8;
     const f32x4* a = reinterpret_cast<const f32x4*>(s_acc);
     const long o = static_cast<long>(gld<int>(p.tok_list + tile.start + tl)) * p.H + h0 + c;
@@ -764,7 +846,7 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   int32_t* tok_list = reinterpret_cast<int32_t*>(ws + ly.tok_list);
   Tile* tiles = reinterpret_cast<Tile*>(ws + ly.tiles);
   int32_t* counters = reinterpret_cast<int32_t*>(ws + ly.counters);
-  int32_t* blk_e = reinterpret_cast<int32_t*>(ws + ly.blk_e);
+  int64_t* blk_b = reinterpret_cast<int64_t*>(ws + ly.blk_b);
   uint32_t* blk_tl = reinterpret_cast<uint32_t*>(ws + ly.blk_tl);
   int32_t* tinfo = reinterpret_cast<int32_t*>(ws + ly.tinfo);
   const int tt = tile_tokens(top_k);
@@ -788,7 +870,8 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
     const int epg = static_cast<int>((E + groups - 1) / groups);
     const int ngroups = static_cast<int>((E + epg - 1) / epg);
     ShrinkArgs sa{src, static_cast<const uint16_t*>(act), w_ptr_a, static_cast<long>(lora_stride_a),
-                  topk_weights, tiles, counters, u2, blk_e, blk_tl, tinfo, ly.cap,
+                  topk_weights, tiles, counters, u2, w_ptr_b, static_cast<long>(lora_stride_b),
+                  blk_b, blk_tl, tinfo, ly.cap,
                   static_cast<int>(inter_size), static_cast<int>(L), static_cast<int>(rank), epg,
                   ly.maxblk, scale};
     const dim3 sgrid(ntiles, ngroups), sblock(NT_DELTA);
@@ -803,17 +886,23 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   }
 
   const int nch = static_cast<int>(H / EXP_CW);
-  ExpandArgs ea{tok_list, w_ptr_b, static_cast<long>(lora_stride_b), tiles, counters, u2, blk_e,
-                blk_tl, tinfo, out, ly.cap, static_cast<int>(L), static_cast<int>(H),
-                static_cast<int>(rank), ly.maxblk, ntiles, nch, out_dtype == MI_F32 ? 1 : 0};
-  const long ewg = (static_cast<long>(ntiles) * nch + 7) & ~7L;  // a multiple of the 8 XCDs
+  ExpandArgs ea{tok_list, tiles, counters, u2, blk_b, blk_tl, tinfo, out, ly.cap,
+                static_cast<int>(L), static_cast<int>(H), static_cast<int>(rank), ly.maxblk,
+                ntiles, nch, out_dtype == MI_F32 ? 1 : 0};
+  // whole runs of 8 tiles x nch chunks, rounded to a multiple of the 8 XCDs
+  const long ewg = ((static_cast<long>(ntiles) + 7) / 8 * 8 * nch + 7) & ~7L;
   MI_REQUIRE(ewg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
-  const dim3 egrid(static_cast<unsigned>(ewg)), eblock(NT_DELTA);
-  switch (nb) {
-    case 1: hipLaunchKernelGGL(expand_kernel<1>, egrid, eblock, 0, s, ea); break;
-    case 2: hipLaunchKernelGGL(expand_kernel<2>, egrid, eblock, 0, s, ea); break;
-    case 4: hipLaunchKernelGGL(expand_kernel<4>, egrid, eblock, 0, s, ea); break;
-    default: hipLaunchKernelGGL(expand_kernel<8>, egrid, eblock, 0, s, ea); break;
+  const dim3 egrid(static_cast<unsigned>(ewg)), eblock(NT_EXP);
+  const bool part = rank != 16 * nb;  // rank chunks past the rank are masked
+  switch (nb * 2 + (part ? 1 : 0)) {
+    case 2: hipLaunchKernelGGL((expand_kernel<1, false>), egrid, eblock, 0, s, ea); break;
+    case 3: hipLaunchKernelGGL((expand_kernel<1, true>), egrid, eblock, 0, s, ea); break;
+    case 4: hipLaunchKernelGGL((expand_kernel<2, false>), egrid, eblock, 0, s, ea); break;
+    case 5: hipLaunchKernelGGL((expand_kernel<2, true>), egrid, eblock, 0, s, ea); break;
+    case 8: hipLaunchKernelGGL((expand_kernel<4, false>), egrid, eblock, 0, s, ea); break;
+    case 9: hipLaunchKernelGGL((expand_kernel<4, true>), egrid, eblock, 0, s, ea); break;
+    case 16: hipLaunchKernelGGL((expand_kernel<8, false>), egrid, eblock, 0, s, ea); break;
+    default: hipLaunchKernelGGL((expand_kernel<8, true>), egrid, eblock, 0, s, ea); break;
   }
   return launch_status("bgmv_moe_gemm2_lora_delta (expand)");
 }

@@ -64,7 +64,8 @@ def test_tiny(gpu):
     assert not bits16(out)[no].any(), "tokens without adapter must be +0"
 
 
-@pytest.mark.parametrize("r,I,H", [(16, 64, 256), (8, 200, 128), (32, 96, 384), (24, 128, 256)])
+@pytest.mark.parametrize("r,I,H", [(16, 64, 256), (8, 200, 128), (32, 96, 384), (24, 128, 256),
+                                   (40, 64, 256), (48, 72, 128)])
 def test_integer_probe_bitwise_scattered_bank(gpu, r, I, H):
     case = to_dev(synth.delta_int_probe(r=r, I=I, H=H), gpu)
     tb = tables(case, scattered=True)
