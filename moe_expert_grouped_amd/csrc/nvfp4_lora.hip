@@ -13,8 +13,8 @@
 // lies in 2^-10 .. 2688, so it is exact in fp16.  Each byte of codes becomes
 // an fp16 pair with v_cvt_scalef32_pk_f16_fp4 at scale 1.0 (a pure format
 // conversion, exact), and one v_pk_mul_f16 by the block's scale (converted
-// exactly from its E4M3 byte) applies the scale -- exact as well.  The
-// decoded tile is written to LDS once per workgroup and feeds
+// exactly from its E4M3 byte) applies the scale -- exact as well.  Each lane
+// decodes its own MFMA operands in registers (no LDS) and feeds
 // v_mfma_f32_32x32x16_f16.  CDNA4's block-scaled MFMA takes power-of-two
 // (E8M0) scales on 32-wide blocks, so it cannot consume UE4M3 scales on
 // 16-wide blocks; this decode-to-fp16 route is exact instead.
@@ -34,12 +34,11 @@ namespace {
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int NV_BM = 256, NV_BN = 256, NV_BK = 64;  // BK in elements (32 code bytes)
-constexpr int NV_WM = 4, NV_WN = 2;
-constexpr int NV_NT = 64 * NV_WM * NV_WN;  // 512 threads
+constexpr int NV_BM = 256, NV_BN = 256;  // workgroup tile
+constexpr int NV_KC = 128;               // K elements per register stage (64 code bytes)
+constexpr int NV_WM = 2, NV_WN = 2;      // 4 wavefronts of 128 x 128
+constexpr int NV_NT = 64 * NV_WM * NV_WN;
 constexpr int NV_GROUP_M = 4;
-
-__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Byte offset of the UE4M3 scale of (row, scale column col) in the 128x4
 // tiled layout: 512-byte tiles of 128 rows x 4 columns, row-block major;
@@ -98,12 +97,35 @@ struct NvArgs {
   int mode;  // 0 off, 1 raw, 2 prepared
 };
 
-__global__ __launch_bounds__(NV_NT) void nvfp4_lora_kernel(NvArgs p) {
-  constexpr int WTM = NV_BM / NV_WM, WTN = NV_BN / NV_WN;  // 64 x 128
-  constexpr int FM = WTM / 32, FN = WTN / 32;               // 2 x 4
-  constexpr int STAGE = (NV_BM + NV_BN) * NV_BK;            // fp16 elements
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t nv_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 nv_ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t nv_ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                            uint32_t soff) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+// One register stage of a wavefront: for each of its 4 A and 4 B fragment
+// rows, this lane's 64 codes (32 bytes) and their 4 scale bytes.
+struct NvStage {
+  u32x4 a[4][2], b[4][2];
+  uint32_t sa[4], sb[4];
+};
+
+// One wavefront computes a 128 x 128 block as 4 x 4 v_mfma_f32_32x32x16_f16
+// tiles; the accumulators (256 floats a lane) live in AGPRs.  There is no LDS:
+// the sum over K is order-free, so inside every 128-wide K stage lane half h
+// (lane / 32) takes the 64 consecutive elements [64h, 64h + 64) and MFMA step
+// s (0..7) consumes elements 64h + 8s .. +7 from both halves -- A and B use
+// the same assignment.  Each lane therefore reads its row's codes as 32
+// contiguous bytes and decodes them straight into MFMA operands.  Every A and
+// B row is decoded by the two wavefronts that share it.
+__global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
+  constexpr int WTM = NV_BM / NV_WM, WTN = NV_BN / NV_WN;  // 128 x 128
+  constexpr int FM = WTM / 32, FN = WTN / 32;               // 4 x 4
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NV_WN, wn = wave % NV_WN;
@@ -121,20 +143,29 @@ __global__ __launch_bounds__(NV_NT) void nvfp4_lora_kernel(NvArgs p) {
   const int m0 = (first + in_grp % gsize) * NV_BM;
   const int n0 = (in_grp / gsize) * NV_BN;
 
-  // ---- per-thread load coordinates: thread t owns row t/2, code half t%2 ----
-  const int lrow = tid >> 1, half = tid & 1;
-  const int arow = min(m0 + lrow, p.m - 1);
-  const int brow = min(n0 + lrow, p.n - 1);
-  const long kb = p.k / 2;  // code bytes per row
-  const uint8_t* a_codes = p.a + static_cast<long>(arow) * kb + half * 16;
-  const uint8_t* b_codes = p.b + static_cast<long>(brow) * kb + half * 16;
-  const int n_col_tiles = (p.k / 16 + 3) / 4;
-  const uint8_t* a_sfw = p.a_sf + sf_tile_word(arow, 0, n_col_tiles);
-  const uint8_t* b_sfw = p.b_sf + sf_tile_word(brow, 0, n_col_tiles);
-  // LDS chunk positions of this thread's 4 chunks (k chunks half*4 .. half*4+3)
-  int lds_off[4];
+  // ---- per-lane byte offsets (codes and scales), rows clamped into range ----
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t kb = static_cast<uint32_t>(p.k) / 2;  // code bytes per row
+  const int nct = (p.k / 16 + 3) / 4;                   // 128x4 scale tiles along K
+  const __amdgpu_buffer_rsrc_t ra = nv_rsrc(p.a, static_cast<uint32_t>(p.m) * kb);
+  const __amdgpu_buffer_rsrc_t rb = nv_rsrc(p.b, static_cast<uint32_t>(p.n) * kb);
+  const __amdgpu_buffer_rsrc_t rsa =
+      nv_rsrc(p.a_sf, static_cast<uint32_t>((p.m + 127) / 128) * nct * 512);
+  const __amdgpu_buffer_rsrc_t rsb =
+      nv_rsrc(p.b_sf, static_cast<uint32_t>((p.n + 127) / 128) * nct * 512);
+  uint32_t oa[FM], ob[FN], osa[FM], osb[FN];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) lds_off[c] = lrow * NV_BK + (((half * 4 + c) ^ lds_swz(lrow)) << 3);
+  for (int i = 0; i < FM; ++i) {
+    const int row = min(m0 + wm * WTM + i * 32 + r32, p.m - 1);
+    oa[i] = static_cast<uint32_t>(row) * kb + h * 32;
+    osa[i] = static_cast<uint32_t>(sf_tile_word(row, h, nct));
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int row = min(n0 + wn * WTN + j * 32 + r32, p.n - 1);
+    ob[j] = static_cast<uint32_t>(row) * kb + h * 32;
+    osb[j] = static_cast<uint32_t>(sf_tile_word(row, h, nct));
+  }
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -144,65 +175,71 @@ __global__ __launch_bounds__(NV_NT) void nvfp4_lora_kernel(NvArgs p) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  u32x4 ca, cb;       // 32 codes of A / B
-  uint32_t sa, sb;    // the row's 4 scale bytes of this K step
-
-  auto gload = [&](int kt) {
-    ca = *reinterpret_cast<const u32x4*>(a_codes + kt * (NV_BK / 2));
-    cb = *reinterpret_cast<const u32x4*>(b_codes + kt * (NV_BK / 2));
-    sa = *reinterpret_cast<const uint32_t*>(a_sfw + static_cast<long>(kt) * 512);
-    sb = *reinterpret_cast<const uint32_t*>(b_sfw + static_cast<long>(kt) * 512);
-  };
-  auto decode_store = [&](int buf) {
-    uint16_t* sA = smem + buf * STAGE;
-    uint16_t* sB = sA + NV_BM * NV_BK;
-    // this half covers scale columns 2*half and 2*half+1 of the step
-    const f16x2 sa0 = scale_pair((sa >> (16 * half)) & 0xff);
-    const f16x2 sa1 = scale_pair((sa >> (16 * half + 8)) & 0xff);
-    const f16x2 sb0 = scale_pair((sb >> (16 * half)) & 0xff);
-    const f16x2 sb1 = scale_pair((sb >> (16 * half + 8)) & 0xff);
-    *reinterpret_cast<u32x4*>(sA + lds_off[0]) = decode8(ca.x, sa0);
-    *reinterpret_cast<u32x4*>(sA + lds_off[1]) = decode8(ca.y, sa0);
-    *reinterpret_cast<u32x4*>(sA + lds_off[2]) = decode8(ca.z, sa1);
-    *reinterpret_cast<u32x4*>(sA + lds_off[3]) = decode8(ca.w, sa1);
-    *reinterpret_cast<u32x4*>(sB + lds_off[0]) = decode8(cb.x, sb0);
-    *reinterpret_cast<u32x4*>(sB + lds_off[1]) = decode8(cb.y, sb0);
-    *reinterpret_cast<u32x4*>(sB + lds_off[2]) = decode8(cb.z, sb1);
-    *reinterpret_cast<u32x4*>(sB + lds_off[3]) = decode8(cb.w, sb1);
-  };
-
-  const int KT = p.k / NV_BK;
-  gload(0);
-  decode_store(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint16_t* sA = smem + cur * STAGE;
-    const uint16_t* sB = sA + NV_BM * NV_BK;
+  // stage kc: codes at byte kc*64 of the row, scales in scale tile 2*kc + h
+  auto load = [&](NvStage& st, int kc) {
+    const uint32_t co = static_cast<uint32_t>(kc) * (NV_KC / 2);
+    const uint32_t so = static_cast<uint32_t>(kc) * 1024;
 #pragma unroll
-    for (int s = 0; s < NV_BK / 16; ++s) {
-      const int kc = 2 * s + (lane >> 5);
-      f16x8 fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 32 + (lane & 31);
-        fa[i] = *reinterpret_cast<const f16x8*>(sA + r * NV_BK + ((kc ^ lds_swz(r)) << 3));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * WTN + j * 32 + (lane & 31);
-        fb[j] = *reinterpret_cast<const f16x8*>(sB + r * NV_BK + ((kc ^ lds_swz(r)) << 3));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < FM; ++i) {
+      st.a[i][0] = nv_ld128(ra, oa[i], co);
+      st.a[i][1] = nv_ld128(ra, oa[i] + 16, co);
+      st.sa[i] = nv_ld32(rsa, osa[i], so);
     }
-    if (kt + 1 < KT) decode_store(cur ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      st.b[j][0] = nv_ld128(rb, ob[j], co);
+      st.b[j][1] = nv_ld128(rb, ob[j] + 16, co);
+      st.sb[j] = nv_ld32(rsb, osb[j], so);
+    }
+  };
+  auto compute = [&](const NvStage& st) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {  // scale block t: MFMA steps 2t, 2t+1
+      f16x2 psa[FM], psb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) psa[i] = scale_pair((st.sa[i] >> (8 * t)) & 0xff);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) psb[j] = scale_pair((st.sb[j] >> (8 * t)) & 0xff);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int s = 2 * t + u;  // code word s of the lane's 8
+        u32x4 fa[FM], fb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[i] = decode8(st.a[i][s >> 2][s & 3], psa[i]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[j] = decode8(st.b[j][s >> 2][s & 3], psb[j]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, fa[i]), __builtin_bit_cast(f16x8, fb[j]), acc[i][j], 0,
+                0, 0);
+      }
+    }
+    // interleave: the decode of later steps runs while earlier MFMAs execute
+#pragma unroll
+    for (int g = 0; g < 8 * FM * FN; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU
+    }
+  };
+
+  // K / 128 is even (K % 256 == 0): two stages per trip, the refill index is
+  // clamped so every trip issues the same loads
+  const int NKC = p.k / NV_KC;
+  NvStage s0, s1;
+  load(s0, 0);
+  for (int kc = 0; kc < NKC; kc += 2) {
+    // the barriers keep each refill where it is issued: a whole stage ahead
+    load(s1, kc + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(s0, min(kc + 2, NKC - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue ----
@@ -350,6 +387,9 @@ extern "C" mi_status mi_mm_nvfp4_lora(const uint8_t* a, const uint8_t* b, const 
              "mm_nvfp4_lora: shape too large");
   MI_REQUIRE(a && b && a_sf && b_sf && alpha && out, "mm_nvfp4_lora: a, b, a_sf, b_sf, alpha and "
              "out must be non-null");
+  MI_REQUIRE_SUPPORTED(m * (k / 2) < (1LL << 32) && n * (k / 2) < (1LL << 32) &&
+                           sf_needed(m, k) < (1ULL << 32) && sf_needed(n, k) < (1ULL << 32),
+                       "mm_nvfp4_lora: each operand's codes and scales must stay below 4 GiB");
   MI_REQUIRE(a_sf_bytes >= sf_needed(m, k),
              "mm_nvfp4_lora: a_sf holds %zu bytes, the 128x4 layout needs %zu", a_sf_bytes,
              sf_needed(m, k));
