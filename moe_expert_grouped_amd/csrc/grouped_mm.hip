@@ -11,16 +11,17 @@
 // Kernel structure
 //   * tile BM x BN, K step 64; WM x WN waves, each owning a (BM/WM) x (BN/WN)
 //     sub-tile of 32x32 v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulators);
-//   * global -> registers -> LDS, double-buffered, one barrier per K step; the
-//     next stage's global loads are in flight while the current stage feeds
-//     the MFMAs;
+//   * global -> registers -> LDS, one barrier per K step; P K steps of global
+//     loads are in flight in registers (small-row groups are bound by
+//     streaming b from HBM, so the loads run well ahead) while the LDS copy
+//     of the current step feeds the MFMAs;
 //   * LDS rows are 128 bytes (64 bf16); the 16-byte chunk c of row r is stored
 //     at chunk c ^ ((r ^ (r >> 3)) & 7), so both the row-contiguous stores and
 //     the MFMA fragment loads (32 rows, same chunk) spread over all banks;
 //   * persistent grid: each workgroup loops over tiles; tile order is grouped
-//     (GROUP_M m-tiles share each n-panel) and remapped so that the
-//     workgroups of one XCD (workgroup id % 8) take a contiguous run of tiles
-//     per round, which keeps the shared a/b panels in that XCD's L2;
+//     (GROUP_M m-tiles share each n-panel) and cut into 8 contiguous runs,
+//     one per XCD (workgroup id % 8), which keeps the shared a/b panels in
+//     that XCD's L2;
 //   * rows past the expert's end are clamped on load and masked on store;
 //     waves whose rows all lie past the end skip their MFMAs.
 #include "common.hpp"
@@ -58,7 +59,7 @@ __device__ __forceinline__ void store_out<float>(float* p, float v) {
   *p = v;
 }
 
-template <int BM, int BN, int WM, int WN, typename OutT>
+template <int BM, int BN, int WM, int WN, int P, typename OutT>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
     const int32_t* __restrict__ m_indptr, OutT* __restrict__ out, int m_rows, int k, int n,
@@ -118,16 +119,18 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
   const int total_mt = s_tile0[E];
   const int nt = n / BN;
   const long total = static_cast<long>(total_mt) * nt;
-  const int G = gridDim.x;           // multiple of 8
-  const int per_xcd = G >> 3;
+  // The dispatcher deals workgroup ids to the 8 XCDs in turn.  The tiles
+  // (known only now) are cut into 8 contiguous runs, one per XCD, and the
+  // workgroups of an XCD stride through its run.
+  const int slots = gridDim.x >> 3;  // workgroups per XCD (grid is a multiple of 8)
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const long run = (total + 7) / 8;
+  const long run_end = min(total, (xcd + 1) * run);
 
   uint16_t* const ldsA0 = smem;
   uint16_t* const ldsB0 = smem + BM * GM_BK;
 
-  for (long round_base = 0; round_base < total; round_base += G) {
-    const long L = round_base + static_cast<long>(xcd) * per_xcd + slot;
-    if (L >= total) continue;  // later rounds may still hold tiles for this slot
+  for (long L = xcd * run + slot; L < run_end; L += slots) {
 
     // grouped order: GROUP_M consecutive m-tiles sweep each n-panel together
     const long span = static_cast<long>(GM_GROUP_M) * nt;
@@ -183,51 +186,64 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    u32x4 ra[CPT_A], rb[CPT_B];
-
     const int KT = k / GM_BK;
+    // P stages of global loads in flight in registers (indices clamped to the
+    // last stage so every step issues the same loads); LDS double-buffered.
+    u32x4 ra[P][CPT_A], rb[P][CPT_B];
     __syncthreads();  // previous tile's last LDS reads are done
-    gm_gload(ra, Ag, a_off, 0);
-    gm_gload(rb, Bg, b_off, 0);
-    gm_lstore(ldsA0, ra, a_lds);
-    gm_lstore(ldsB0, rb, b_lds);
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      gm_gload(ra[q], Ag, a_off, min(q, KT - 1) * GM_BK);
+      gm_gload(rb[q], Bg, b_off, min(q, KT - 1) * GM_BK);
+    }
+    gm_lstore(ldsA0, ra[0], a_lds);
+    gm_lstore(ldsB0, rb[0], b_lds);
+    gm_gload(ra[0], Ag, a_off, min(P, KT - 1) * GM_BK);
+    gm_gload(rb[0], Bg, b_off, min(P, KT - 1) * GM_BK);
     __syncthreads();
 
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) {
-        gm_gload(ra, Ag, a_off, (kt + 1) * GM_BK);
-        gm_gload(rb, Bg, b_off, (kt + 1) * GM_BK);
-      }
-      if (wave_active) {
-        const uint16_t* sA = ldsA0 + cur * STAGE;
-        const uint16_t* sB = ldsB0 + cur * STAGE;
+    for (int kt0 = 0; kt0 < KT; kt0 += P) {
 #pragma unroll
-        for (int s = 0; s < GM_BK / 16; ++s) {
-          const int kc = 2 * s + (lane >> 5);
-          bf16x8 fa[FM], fb[FN];
+      for (int q = 0; q < P; ++q) {
+        const int kt = kt0 + q;
+        const int cur = kt & 1;
+        {
+          // steps past the end only refill and copy (no MFMAs): every step
+          // issues the same loads
+          if (wave_active && kt < KT) {
+            const uint16_t* sA = ldsA0 + cur * STAGE;
+            const uint16_t* sB = ldsB0 + cur * STAGE;
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int r = wm * WTM + i * 32 + (lane & 31);
-            fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * GM_BK + ((kc ^ lds_swz(r)) << 3));
+            for (int s = 0; s < GM_BK / 16; ++s) {
+              const int kc = 2 * s + (lane >> 5);
+              bf16x8 fa[FM], fb[FN];
+#pragma unroll
+              for (int i = 0; i < FM; ++i) {
+                const int r = wm * WTM + i * 32 + (lane & 31);
+                fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * GM_BK + ((kc ^ lds_swz(r)) << 3));
+              }
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                const int r = wn * WTN + j * 32 + (lane & 31);
+                fb[j] = *reinterpret_cast<const bf16x8*>(sB + r * GM_BK + ((kc ^ lds_swz(r)) << 3));
+              }
+#pragma unroll
+              for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                  acc[i][j] =
+                      __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            }
           }
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int r = wn * WTN + j * 32 + (lane & 31);
-            fb[j] = *reinterpret_cast<const bf16x8*>(sB + r * GM_BK + ((kc ^ lds_swz(r)) << 3));
-          }
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          // stage kt+1 sits in register slot (q+1) % P; refill that slot with stage kt+1+P
+          const int nq = (q + 1) % P;
+          gm_lstore(ldsA0 + (cur ^ 1) * STAGE, ra[nq], a_lds);
+          gm_lstore(ldsB0 + (cur ^ 1) * STAGE, rb[nq], b_lds);
+          gm_gload(ra[nq], Ag, a_off, min(kt + 1 + P, KT - 1) * GM_BK);
+          gm_gload(rb[nq], Bg, b_off, min(kt + 1 + P, KT - 1) * GM_BK);
+          __syncthreads();
         }
       }
-      if (kt + 1 < KT) {
-        gm_lstore(ldsA0 + (cur ^ 1) * STAGE, ra, a_lds);
-        gm_lstore(ldsB0 + (cur ^ 1) * STAGE, rb, b_lds);
-      }
-      __syncthreads();
     }
 
     // ---- epilogue: C[row][col], row = 8*(q/4) + 4*(lane/32) + q%4, col = lane%32 ----
@@ -262,7 +278,7 @@ int num_cus() {
   return cached[dev];
 }
 
-template <int BM, int BN, int WM, int WN, typename OutT>
+template <int BM, int BN, int WM, int WN, int P, typename OutT>
 mi_status launch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b,
                          int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
                          hipStream_t stream, int occupancy) {
@@ -272,7 +288,7 @@ mi_status launch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b
   if (G > ub_tiles) G = ub_tiles;
   G = ((G + 7) / 8) * 8;
   if (G < 8) G = 8;
-  hipLaunchKernelGGL((grouped_mm_kernel<BM, BN, WM, WN, OutT>), dim3(G), dim3(64 * WM * WN), 0,
+  hipLaunchKernelGGL((grouped_mm_kernel<BM, BN, WM, WN, P, OutT>), dim3(G), dim3(64 * WM * WN), 0,
                      stream, static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
                      m_indptr, static_cast<OutT*>(out), static_cast<int>(m_rows),
                      static_cast<int>(k), static_cast<int>(n), static_cast<int>(batch));
@@ -284,14 +300,13 @@ mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void*
                            int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
                            hipStream_t stream) {
   // Tile shape from host-known sizes only (the counts live on the device):
-  // large average groups take 256x256 tiles, small ones narrower tiles so the
-  // grid still covers the chip.
+  // large average groups take 256x256 tiles; smaller groups stream b from HBM
+  // and take 64x64 tiles, two workgroups per CU, with 4 K steps in flight.
   const int64_t avg = m_rows / batch;
   if (avg >= 192)
-    return launch_grouped<256, 256, 4, 2, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 1);
-  if (avg >= 96)
-    return launch_grouped<128, 64, 2, 2, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
-  return launch_grouped<64, 64, 2, 2, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
+    return launch_grouped<256, 256, 4, 2, 1, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
+                                                   1);
+  return launch_grouped<64, 64, 2, 2, 4, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
 }
 
 }  // namespace

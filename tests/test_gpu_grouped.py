@@ -32,7 +32,7 @@ def test_tiny_moe_fc2(gpu):
 
 @pytest.mark.parametrize("counts,n,k", [
     ((0, 1, 17, 128, 0, 255), 256, 128),          # small groups: 64x64 tiles
-    ((100, 0, 150, 177, 0, 229), 512, 192),       # medium: 128x64 tiles
+    ((100, 0, 150, 177, 0, 229), 512, 192),       # medium: 64x64 tiles, several per group
     ((300, 0, 513, 1, 256, 0, 390), 256, 256),    # large: 256x256 tiles, ragged tails
 ])
 def test_integer_probe_bitwise(gpu, counts, n, k):
