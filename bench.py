@@ -43,7 +43,12 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", default="", help="comma list of ops to run (profiling aid)")
+    p.add_argument("--only", default="", help="comma list of ops to run (profiling aid); "
+                   "'copy_probe' (not part of the step) is a 512 MiB fp32 negation (read + write) used to "
+                   "calibrate the HBM byte counters")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                   "'--only nvfp4_raw,copy_probe' into the committed traffic summary")
     return p.parse_args()
 
 
@@ -69,8 +74,73 @@ def read_traffic():
         return None
 
 
+COPY_PROBE_BYTES = 512 << 20  # per direction
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _pmc_avg(rows, counter, pick):
+    vals = [float(r["Counter_Value"]) for r in rows
+            if r["Counter_Name"] == counter and pick(r["Kernel_Name"])]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for the requested kernel")
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the NVFP4 kernel, each
+    scaled by what the same counter reads for the copy probe of known size."""
+    is_nv = lambda k: "nvfp4_lora_kernel" in k
+    is_copy = lambda k: "at::native" in k and "neg_kernel" in k
+    fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    nv_f, n_nf = _pmc_avg(fr, "FETCH_SIZE", is_nv)
+    cp_f, n_cf = _pmc_avg(fr, "FETCH_SIZE", is_copy)
+    nv_w, n_nw = _pmc_avg(wr, "WRITE_SIZE", is_nv)
+    cp_w, n_cw = _pmc_avg(wr, "WRITE_SIZE", is_copy)
+    f_fac = COPY_PROBE_BYTES / (cp_f * 1024.0)
+    w_fac = COPY_PROBE_BYTES / (cp_w * 1024.0)
+    fetch_b = nv_f * 1024.0 * f_fac
+    write_b = nv_w * 1024.0 * w_fac
+    out = os.path.join(ROOT, "profiles", os.path.basename(TRAFFIC_FILE))
+    with open(out, "w") as fh:
+        fh.write("# HBM traffic of nvfp4_lora_kernel, M=4096 N=8192 K=8192 r=16 (raw path)\n"
+                 "# commands (repo root, one MI355X; each pass its own run):\n"
+                 "#   rocprofv3 --pmc FETCH_SIZE -d <FETCH_DIR> -o f --output-format csv -- "
+                 "python3 bench.py --only nvfp4_raw,copy_probe --steps 3 --warmup 1\n"
+                 "#   rocprofv3 --pmc WRITE_SIZE -d <WRITE_DIR> -o w --output-format csv -- "
+                 "python3 bench.py --only nvfp4_raw,copy_probe --steps 3 --warmup 1\n"
+                 "#   python3 bench.py --pmc-summary <FETCH_DIR> <WRITE_DIR>\n"
+                 "# Counters are KiB per dispatch; each is scaled by the factor that maps the\n"
+                 "# same counter on the copy probe (a 512 MiB fp32 read + 512 MiB write) to its\n"
+                 "# known size.  Algorithmic bytes per launch: 124141568.\n")
+        fh.write(f"kernel_source_sha256_16 = {src_hash()}\n")
+        fh.write(f"fetch_kib_per_dispatch = {nv_f:.1f}   # {n_nf} dispatches\n")
+        fh.write(f"write_kib_per_dispatch = {nv_w:.1f}   # {n_nw} dispatches\n")
+        fh.write(f"copy_probe_fetch_kib = {cp_f:.1f}   # {n_cf} dispatches\n")
+        fh.write(f"copy_probe_write_kib = {cp_w:.1f}   # {n_cw} dispatches\n")
+        fh.write(f"fetch_scale = {f_fac:.4f}\nwrite_scale = {w_fac:.4f}\n")
+        fh.write(f"hbm_fetch_bytes_per_launch = {fetch_b:.0f}\n")
+        fh.write(f"hbm_write_bytes_per_launch = {write_b:.0f}\n")
+        fh.write(f"hbm_bytes_per_launch = {fetch_b + write_b:.0f}\n")
+    print(f"wrote {out}: {(fetch_b + write_b) / 1e6:.1f} MB per launch "
+          f"(fetch scale {f_fac:.3f}, write scale {w_fac:.3f})")
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (the path is "
                                    "data-parallel per GPU, see the sharding notes)"}))
@@ -136,11 +206,15 @@ def main():
                                                    lora_adapter=adapter, bias=nc.bias,
                                                    out=nout_prep),
     }
+    if "copy_probe" in only:
+        cp_src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        cp_dst = torch.empty_like(cp_src)
+        ops["copy_probe"] = lambda: torch.neg(cp_src, out=cp_dst)
     if only:
         ops = {k: v for k, v in ops.items() if k in only}
     work = {"grouped_gemm": (gemm_flops, gemm_bytes), "lora_delta": (delta_flops, delta_bytes),
             "fold": (fold_flops, fold_bytes), "nvfp4_raw": (nv_flops, nv_bytes),
-            "nvfp4_prepared": (nv_flops, nv_bytes)}
+            "nvfp4_prepared": (nv_flops, nv_bytes), "copy_probe": (0.0, 2.0 * COPY_PROBE_BYTES)}
 
     def step(ev=None):
         for i, (name, fn) in enumerate(ops.items()):
@@ -255,8 +329,8 @@ def cpu_baseline(g2, dc, nc, wa, wb, sa, sb):
     grouped_mm(a, b, mi_)
     t_total += time.perf_counter() - t
     flops += 2.0 * g2.a.shape[0] * g2.a.shape[1] * g2.b.shape[1]
-    # LoRA delta: 2048 of the 8192 tokens
-    toks = list(range(0, dc.T, dc.T // 2048))
+    # LoRA delta: every token
+    toks = list(range(dc.T))
     act = bits(dc.act)
     ba, bb = Bank(bits(dc.A.reshape(-1)), dc.A.data_ptr()), Bank(bits(dc.B.reshape(-1)),
                                                                  dc.B.data_ptr())
@@ -270,8 +344,8 @@ def cpu_baseline(g2, dc, nc, wa, wb, sa, sb):
     pr = perm.reshape(dc.T, dc.top_k)
     n_act = int(((pr[toks] >= 0) & (lids[toks][:, None] >= 0)).sum())
     flops += n_act * (2.0 * dc.rank * dc.I + 2.0 * dc.H * dc.rank)
-    # NVFP4 raw: 512 of the 4096 rows, all columns
-    rows = np.arange(0, nc.M, nc.M // 512)
+    # NVFP4 raw: 1024 of the 4096 rows, all columns
+    rows = np.arange(0, nc.M, nc.M // 1024)
     a_c = nc.a.cpu().numpy()[rows]
     b_c, asf, bsf = nc.b.cpu().numpy(), nc.a_sf.cpu().numpy(), nc.b_sf.cpu().numpy()
     t = time.perf_counter()
@@ -282,8 +356,8 @@ def cpu_baseline(g2, dc, nc, wa, wb, sa, sb):
     flops += 2.0 * len(rows) * nc.N * nc.K + 2.0 * len(rows) * nc.N * nc.rank
     return {"value": round(flops / t_total / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(t_total, 2),
-            "sample": "whole grouped GEMM workload + LoRA delta on 2048 of 8192 tokens + NVFP4 "
-                      "raw on 512 of 4096 rows (all columns); flops of the sample / oracle time"}
+            "sample": "whole grouped GEMM workload + whole LoRA delta workload + NVFP4 raw on "
+                      "1024 of 4096 rows (all columns); flops of the sample / oracle time"}
 
 
 if __name__ == "__main__":
