@@ -29,11 +29,12 @@
 namespace mi {
 namespace {
 
-constexpr int GM_BK = 64;
 constexpr int GM_MAX_EXPERTS = 1024;
 constexpr int GM_GROUP_M = 8;
 
-__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte chunk c of LDS row r sits at c ^ swz(r): consecutive rows spread over all banks
+template <int CPR>  // chunks per row
+__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row / CPR)) & (CPR - 1); }
 
 template <int C>
 __device__ __forceinline__ void gm_gload(u32x4 (&r)[C], const uint16_t* __restrict__ base,
@@ -59,7 +60,7 @@ __device__ __forceinline__ void store_out<float>(float* p, float v) {
   *p = v;
 }
 
-template <int BM, int BN, int WM, int WN, int P, typename OutT>
+template <int BM, int BN, int BK, int WM, int WN, int P, typename OutT>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
     const int32_t* __restrict__ m_indptr, OutT* __restrict__ out, int m_rows, int k, int n,
@@ -67,10 +68,11 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int CPT_A = BM * GM_BK / 8 / NT;  // 16-byte chunks per thread per stage
-  constexpr int CPT_B = BN * GM_BK / 8 / NT;
-  constexpr int STAGE = (BM + BN) * GM_BK;   // bf16 elements per stage
-  static_assert(CPT_A * NT == BM * GM_BK / 8 && CPT_B * NT == BN * GM_BK / 8, "tile/threads");
+  constexpr int CPR = BK / 8;                // 16-byte chunks per LDS row
+  constexpr int CPT_A = BM * BK / 8 / NT;  // 16-byte chunks per thread per stage
+  constexpr int CPT_B = BN * BK / 8 / NT;
+  constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per stage
+  static_assert(CPT_A * NT == BM * BK / 8 && CPT_B * NT == BN * BK / 8, "tile/threads");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
 
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
   const long run_end = min(total, (xcd + 1) * run);
 
   uint16_t* const ldsA0 = smem;
-  uint16_t* const ldsB0 = smem + BM * GM_BK;
+  uint16_t* const ldsB0 = smem + BM * BK;
 
   for (long L = xcd * run + slot; L < run_end; L += slots) {
 
@@ -161,19 +163,19 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
 #pragma unroll
     for (int i = 0; i < CPT_A; ++i) {
       const int c = tid + i * NT;
-      const int r = c >> 3, kc = c & 7;
+      const int r = c / CPR, kc = c % CPR;
       const int gr = min(m0 + r, m_end - 1);
       a_off[i] = static_cast<long>(gr) * k + kc * 8;
-      a_lds[i] = r * GM_BK + ((kc ^ lds_swz(r)) << 3);
+      a_lds[i] = r * BK + ((kc ^ lds_swz<CPR>(r)) << 3);
     }
     long b_off[CPT_B];
     int b_lds[CPT_B];
 #pragma unroll
     for (int i = 0; i < CPT_B; ++i) {
       const int c = tid + i * NT;
-      const int r = c >> 3, kc = c & 7;
+      const int r = c / CPR, kc = c % CPR;
       b_off[i] = static_cast<long>(r) * k + kc * 8;
-      b_lds[i] = r * GM_BK + ((kc ^ lds_swz(r)) << 3);
+      b_lds[i] = r * BK + ((kc ^ lds_swz<CPR>(r)) << 3);
     }
 
     const bool wave_active = (m0 + wm * WTM) < m_end;
@@ -186,20 +188,20 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    const int KT = k / GM_BK;
+    const int KT = k / BK;
     // P stages of global loads in flight in registers (indices clamped to the
     // last stage so every step issues the same loads); LDS double-buffered.
     u32x4 ra[P][CPT_A], rb[P][CPT_B];
     __syncthreads();  // previous tile's last LDS reads are done
 #pragma unroll
     for (int q = 0; q < P; ++q) {
-      gm_gload(ra[q], Ag, a_off, min(q, KT - 1) * GM_BK);
-      gm_gload(rb[q], Bg, b_off, min(q, KT - 1) * GM_BK);
+      gm_gload(ra[q], Ag, a_off, min(q, KT - 1) * BK);
+      gm_gload(rb[q], Bg, b_off, min(q, KT - 1) * BK);
     }
     gm_lstore(ldsA0, ra[0], a_lds);
     gm_lstore(ldsB0, rb[0], b_lds);
-    gm_gload(ra[0], Ag, a_off, min(P, KT - 1) * GM_BK);
-    gm_gload(rb[0], Bg, b_off, min(P, KT - 1) * GM_BK);
+    gm_gload(ra[0], Ag, a_off, min(P, KT - 1) * BK);
+    gm_gload(rb[0], Bg, b_off, min(P, KT - 1) * BK);
     __syncthreads();
 
     for (int kt0 = 0; kt0 < KT; kt0 += P) {
@@ -214,18 +216,18 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
             const uint16_t* sA = ldsA0 + cur * STAGE;
             const uint16_t* sB = ldsB0 + cur * STAGE;
 #pragma unroll
-            for (int s = 0; s < GM_BK / 16; ++s) {
+            for (int s = 0; s < BK / 16; ++s) {
               const int kc = 2 * s + (lane >> 5);
               bf16x8 fa[FM], fb[FN];
 #pragma unroll
               for (int i = 0; i < FM; ++i) {
                 const int r = wm * WTM + i * 32 + (lane & 31);
-                fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * GM_BK + ((kc ^ lds_swz(r)) << 3));
+                fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * BK + ((kc ^ lds_swz<CPR>(r)) << 3));
               }
 #pragma unroll
               for (int j = 0; j < FN; ++j) {
                 const int r = wn * WTN + j * 32 + (lane & 31);
-                fb[j] = *reinterpret_cast<const bf16x8*>(sB + r * GM_BK + ((kc ^ lds_swz(r)) << 3));
+                fb[j] = *reinterpret_cast<const bf16x8*>(sB + r * BK + ((kc ^ lds_swz<CPR>(r)) << 3));
               }
 #pragma unroll
               for (int i = 0; i < FM; ++i)
@@ -239,8 +241,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
           const int nq = (q + 1) % P;
           gm_lstore(ldsA0 + (cur ^ 1) * STAGE, ra[nq], a_lds);
           gm_lstore(ldsB0 + (cur ^ 1) * STAGE, rb[nq], b_lds);
-          gm_gload(ra[nq], Ag, a_off, min(kt + 1 + P, KT - 1) * GM_BK);
-          gm_gload(rb[nq], Bg, b_off, min(kt + 1 + P, KT - 1) * GM_BK);
+          gm_gload(ra[nq], Ag, a_off, min(kt + 1 + P, KT - 1) * BK);
+          gm_gload(rb[nq], Bg, b_off, min(kt + 1 + P, KT - 1) * BK);
           __syncthreads();
         }
       }
@@ -278,7 +280,7 @@ int num_cus() {
   return cached[dev];
 }
 
-template <int BM, int BN, int WM, int WN, int P, typename OutT>
+template <int BM, int BN, int BK, int WM, int WN, int P, typename OutT>
 mi_status launch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b,
                          int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
                          hipStream_t stream, int occupancy) {
@@ -288,7 +290,7 @@ mi_status launch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b
   if (G > ub_tiles) G = ub_tiles;
   G = ((G + 7) / 8) * 8;
   if (G < 8) G = 8;
-  hipLaunchKernelGGL((grouped_mm_kernel<BM, BN, WM, WN, P, OutT>), dim3(G), dim3(64 * WM * WN), 0,
+  hipLaunchKernelGGL((grouped_mm_kernel<BM, BN, BK, WM, WN, P, OutT>), dim3(G), dim3(64 * WM * WN), 0,
                      stream, static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
                      m_indptr, static_cast<OutT*>(out), static_cast<int>(m_rows),
                      static_cast<int>(k), static_cast<int>(n), static_cast<int>(batch));
@@ -304,9 +306,9 @@ mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void*
   // and take 64x64 tiles, two workgroups per CU, with 4 K steps in flight.
   const int64_t avg = m_rows / batch;
   if (avg >= 192)
-    return launch_grouped<256, 256, 4, 2, 1, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
+    return launch_grouped<256, 256, 64, 4, 2, 1, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
                                                    1);
-  return launch_grouped<64, 64, 2, 2, 4, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
+  return launch_grouped<64, 64, 64, 2, 2, 4, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
 }
 
 }  // namespace

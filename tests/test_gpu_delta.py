@@ -135,3 +135,25 @@ def test_at_scale_sampled(gpu):
     check_close(to_f64(out.index_select(0, idx)), ref, "delta at scale (sampled tokens)")
     out2 = run_gpu(case, tb)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_workspace_contents_do_not_matter(gpu):
+    """Every workspace byte the kernels read is written earlier in the same
+    call: a workspace full of garbage gives the same bits as a zeroed one."""
+    from moe_expert_grouped_amd import delta_workspace_bytes
+    case = to_dev(synth.delta_int_probe(seed=107, r=24, I=128, H=256), gpu)
+    tb = tables(case, scattered=True)
+    fa, wa, sa, fb, wb, sb = tb
+    nbytes = delta_workspace_bytes(case.T, case.topk_ids.shape[1], case.A.shape[1], case.L,
+                                   case.rank)
+    outs = []
+    for fill in (0, 0xFF, 0x5A):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=gpu)
+        outs.append(bgmv_moe_gemm2_lora_delta(case.act, case.perm, wa.to(gpu), sa, wb.to(gpu), sb,
+                                              case.topk_ids, case.topk_weights, case.lora_ids,
+                                              case.rank, case.H, num_adapters=case.L,
+                                              scale=case.scale, workspace=ws))
+    torch.cuda.synchronize()
+    ref = run_oracle(case, tb)
+    for o in outs:
+        assert np.array_equal(bits16(o), f64_to_bf16_bits(ref))
