@@ -67,7 +67,7 @@ __device__ __forceinline__ void store_tile(Tile* t, const Tile& v) {
 }
 
 struct Layout {
-  size_t u2, tok_list, tiles, counters, blk_b, blk_tl, tinfo, total;
+  size_t u2, tok_list, tiles, counters, blk_a, blk_b, blk_tl, blk_row, blk_w, tinfo, total;
   long cap;     // padded slot positions per tile
   int maxblk;   // 16-slot blocks per tile, at most
 };
@@ -109,8 +109,14 @@ Layout layout(int64_t T, int64_t top_k, int64_t E, int64_t L, int64_t rank) {
   off = al256(off + 64);
   const size_t mt = static_cast<size_t>(max_tiles(T, top_k, L));
   ly.maxblk = static_cast<int>(ly.cap / 16 + 1);
+  ly.blk_a = off;  // address of each block's A_le
+  off = al256(off + mt * ly.maxblk * 8);
   ly.blk_b = off;  // address of each block's B_le
   off = al256(off + mt * ly.maxblk * 8);
+  ly.blk_row = off;  // activation row of each slot (a valid row when the slot is empty)
+  off = al256(off + mt * ly.maxblk * 64);
+  ly.blk_w = off;  // scale * w of each slot (0 when empty)
+  off = al256(off + mt * ly.maxblk * 64);
   ly.blk_tl = off;  // token row (tile-local) of each of a block's 16 slots, 0xFF = empty
   off = al256(off + mt * ly.maxblk * 16);
   ly.tinfo = off;  // per tile: number of blocks, "a token repeats an expert" flag
@@ -192,6 +198,7 @@ struct SlotSrc {
   const int32_t* tok_list;
   const int32_t* perm;
   const int32_t* topk_ids;
+  const float* topk_weights;
   int top_k, padded_rows, E;
 };
 
@@ -201,6 +208,7 @@ struct SlotLists {
   int poff[MAX_EXPERTS + 1];  // start in the padded (whole-block) position space
   int list[SLOT_BUDGET];      // entries (t_local << 24 | x), ascending per expert
   int row[SLOT_BUDGET];       // permuted activation row of each entry
+  float wgt[SLOT_BUDGET];     // routing weight of each entry
   int tmp[SLOT_BUDGET];       // scratch: unsorted entries
 };
 
@@ -213,6 +221,7 @@ __device__ void list_slots(const SlotSrc& s, const Tile& tile, SlotLists& L) {
   const int tid = threadIdx.x;
   const int nslots = tile.count * s.top_k;
   int xs[PER], es[PER], rs[PER];
+  float ws[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int i = tid + k * NT_DELTA;
@@ -226,8 +235,10 @@ __device__ void list_slots(const SlotSrc& s, const Tile& tile, SlotLists& L) {
   for (int k = 0; k < PER; ++k) {
     es[k] = -1;
     rs[k] = 0;
+    ws[k] = 0.f;
     if (xs[k] >= 0) {
       const int e = gld<int>(s.topk_ids + xs[k]), r = gld<int>(s.perm + xs[k]);
+      ws[k] = gld<float>(s.topk_weights + xs[k]);
       if (e >= 0 && e < s.E && r >= 0 && r < s.padded_rows) es[k] = e;
       rs[k] = r;
     }
@@ -292,80 +303,133 @@ __device__ void list_slots(const SlotSrc& s, const Tile& tile, SlotLists& L) {
       for (int i = 0; i < n; ++i) rank += static_cast<uint32_t>(L.tmp[b + i]) < v ? 1 : 0;
       L.list[b + rank] = xs[k];
       L.row[b + rank] = rs[k];
+      L.wgt[b + rank] = ws[k];
     }
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// 2. list: the tile's slots by expert, cut into 16-slot blocks (block table)
+// ---------------------------------------------------------------------------
+struct ListArgs {
+  SlotSrc src;
+  const Tile* tiles;
+  const int32_t* counters;
+  const float* topk_weights;
+  const int64_t* w_ptr_a;
+  long stride_a;
+  const int64_t* w_ptr_b;
+  long stride_b;
+  int64_t* blk_a;     // per block: address of its A_le
+  int64_t* blk_b;     // per block: address of its B_le
+  uint32_t* blk_tl;   // per block: tile-local token row of each slot, 0xFF = empty
+  int32_t* blk_row;   // per block: activation row of each slot (a valid row when empty)
+  float* blk_w;       // per block: scale * w of each slot, 0 when empty
+  int32_t* tinfo;     // per tile: number of blocks, "a token repeats an expert" flag
+  int L, maxblk;
+  float scale;
+};
+
+// One workgroup per tile.  Blocks are numbered in expert order (the u2
+// record of block i is record i); every table entry a later kernel reads is
+// written here, tiles without adapter included (zero blocks).
+__global__ __launch_bounds__(NT_DELTA) void list_kernel(ListArgs p) {
+  __shared__ SlotLists SL;
+  __shared__ int64_t s_pa[MAX_EXPERTS], s_pb[MAX_EXPERTS];  // A_le, B_le of each expert
+  const int ti = blockIdx.x;
+  if (ti >= gld<int>(p.counters)) return;
+  const Tile tile = load_tile(p.tiles + ti);
+  if (tile.bucket >= p.L) {
+    if (threadIdx.x == 0) gst<uint64_t>(p.tinfo + 2 * ti, 0ull);
+    return;
+  }
+  const int l = tile.bucket;
+  const int E = p.src.E;
+  for (int e = threadIdx.x; e < E; e += NT_DELTA) {  // in flight with the slot loads
+    s_pa[e] = gld<int64_t>(p.w_ptr_a + e) + 2 * p.stride_a * l;
+    s_pb[e] = gld<int64_t>(p.w_ptr_b + e) + 2 * p.stride_b * l;
+  }
+  list_slots(p.src, tile, SL);  // starts and ends with barriers
+  const long tb = static_cast<long>(ti) * p.maxblk;
+
+  // per block: its A_le and B_le (one thread per expert, ~1 block each)
+  for (int e = threadIdx.x; e < E; e += NT_DELTA) {
+    const int n = SL.off[e + 1] - SL.off[e];
+    if (n == 0) continue;
+    const int64_t ale = s_pa[e], ble = s_pb[e];
+    for (int b = 0; b * 16 < n; ++b) {
+      gst<int64_t>(p.blk_a + tb + (SL.poff[e] >> 4) + b, ale);
+      gst<int64_t>(p.blk_b + tb + (SL.poff[e] >> 4) + b, ble);
+    }
+  }
+  // per 4-slot word of the padded position space: token rows, act rows, weights
+  const int npos = SL.poff[E];
+  int dup = 0;
+  for (int w = threadIdx.x; w < npos / 4; w += NT_DELTA) {
+    const int p0 = 4 * w;
+    int lo = 0, hi = E;  // the expert owning p0: last e with poff[e] <= p0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (SL.poff[mid] <= p0) lo = mid; else hi = mid;
+    }
+    const int e = lo, b0 = SL.off[e], n = SL.off[e + 1] - b0, k0 = p0 - SL.poff[e];
+    uint32_t tlw = 0;
+    u32x4 rows, ws;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int k = k0 + s2;
+      const int entry = SL.list[b0 + min(k, n - 1)];  // empty slots repeat a valid row
+      const uint32_t tl = static_cast<uint32_t>(entry) >> 24;
+      tlw |= (k < n ? tl : 0xFFu) << (8 * s2);
+      rows[s2] = static_cast<uint32_t>(SL.row[b0 + min(k, n - 1)]);
+      ws[s2] = __float_as_uint(k < n ? p.scale * SL.wgt[b0 + k] : 0.f);
+      if (k > 0 && k < n)  // the list is sorted by token: a repeat is adjacent
+        dup |= (static_cast<uint32_t>(SL.list[b0 + k - 1]) >> 24) == tl;
+    }
+    gst<uint32_t>(p.blk_tl + tb * 4 + w, tlw);
+    gst<u32x4>(p.blk_row + tb * 16 + p0, rows);
+    gst<u32x4>(p.blk_w + tb * 16 + p0, ws);
+  }
+  dup = __syncthreads_or(dup);
+  if (threadIdx.x == 0) {
+    gst<int>(p.tinfo + 2 * ti, npos >> 4);
+    gst<int>(p.tinfo + 2 * ti + 1, dup);
+  }
+}
+
 // u2 record of one 16-slot block: NB chunks of 16 ranks, each 64 lane groups
-// of 8 bf16 -- the MFMA operand of lane (slot, q) = slot + 16 q, which holds
-// hi then lo of ranks 4q .. 4q+3 of the chunk (part 0 = hi, 1 = lo).
+// of 8 bf16 -- the expand's MFMA operand of lane (slot, q) = slot + 16 q,
+// which holds hi then lo of ranks 4q .. 4q+3 of the chunk (part 0 hi, 1 lo).
 __device__ __forceinline__ int u2_elem(int c, int part, int slot, int rr) {
   return c * 512 + ((rr >> 2) * 16 + slot) * 8 + part * 4 + (rr & 3);
 }
 
 // ---------------------------------------------------------------------------
-// 2. shrink
+// 3. shrink: u = (scale * w) * A_le @ act[row], one wavefront per block
 // ---------------------------------------------------------------------------
+constexpr int SHR_WAVES = 4;  // wavefronts (blocks) per workgroup
+
 struct ShrinkArgs {
-  SlotSrc src;
   const uint16_t* act;
-  const int64_t* w_ptr_a;
-  long stride_a;
-  const float* topk_weights;
   const Tile* tiles;
   const int32_t* counters;
+  const int64_t* blk_a;
+  const int32_t* blk_row;
+  const float* blk_w;
+  const int32_t* tinfo;
   uint16_t* u2;
-  const int64_t* w_ptr_b;
-  long stride_b;
-  int64_t* blk_b;
-  uint32_t* blk_tl;
-  int32_t* tinfo;
   long cap;
-  int I, L, rank, epg, maxblk;
-  float scale;
+  int I, L, rank, maxblk, bpt;  // bpt: workgroups per tile
 };
 
-// The block table of a tile, for the expand: blocks in expert order (the u2
-// record of block i is record i), each with the address of its B_le and the
-// tile-local token row of its 16 slots.  Also flags a token that routes to one expert
-// twice (a block would then hold that token twice).
-__device__ void write_block_table(const SlotLists& L, int E, int ti, const ShrinkArgs& p) {
-  int dup = 0;
-  int64_t* bb = p.blk_b + static_cast<long>(ti) * p.maxblk;
-  const int l = load_tile(p.tiles + ti).bucket;
-  uint32_t* bt = p.blk_tl + static_cast<long>(ti) * p.maxblk * 4;
-  for (int e = threadIdx.x; e < E; e += NT_DELTA) {
-    const int b0 = L.off[e], n = L.off[e + 1] - b0;
-    for (int i = 1; i < n; ++i)
-      dup |= (static_cast<uint32_t>(L.list[b0 + i]) >> 24) ==
-             (static_cast<uint32_t>(L.list[b0 + i - 1]) >> 24);
-    const int64_t ble = n > 0 ? gld<int64_t>(p.w_ptr_b + e) + 2 * p.stride_b * l : 0;
-    for (int b = 0; b * 16 < n; ++b) {
-      const int bi = (L.poff[e] >> 4) + b;
-      gst<int64_t>(bb + bi, ble);
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        w[q] = 0;
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          const int k = 16 * b + 4 * q + s2;
-          const uint32_t tl = k < n ? static_cast<uint32_t>(L.list[b0 + k]) >> 24 : 0xFFu;
-          w[q] |= tl << (8 * s2);
-        }
-      }
-      gst<u32x4>(bt + bi * 4, u32x4{w[0], w[1], w[2], w[3]});
-    }
-  }
-  dup = __syncthreads_or(dup);
-  if (threadIdx.x == 0) {
-    gst<int>(p.tinfo + 2 * ti, L.poff[E] >> 4);
-    gst<int>(p.tinfo + 2 * ti + 1, dup);
-  }
-}
-
+// The block's 16 activation rows and A_le are streamed with coalesced 16-byte
+// loads (two K stages in flight in registers) into a wave-private, swizzled
+// LDS stage and read back as v_mfma_f32_16x16x32_bf16 fragments.  (A fragment
+// puts neighbouring lanes on different rows; loading it straight from memory
+// costs more address work per byte.)  Waves never synchronise with each
+// other, so a wave without a block just leaves.
 template <int NB>  // 1, 2, 4 or 8
-__global__ __launch_bounds__(NT_DELTA) void shrink_kernel(ShrinkArgs p) {
+__global__ __launch_bounds__(64 * SHR_WAVES) void shrink_kernel(ShrinkArgs p) {
   static_assert(NB == 1 || NB == 2 || NB == 4 || NB == 8, "rank chunks");
   constexpr int KC = (128 / NB) < 32 ? 32 : 128 / NB;  // K elements per LDS stage
   constexpr int CPR = KC / 8;                          // 16-byte chunks per stage row
@@ -373,148 +437,123 @@ __global__ __launch_bounds__(NT_DELTA) void shrink_kernel(ShrinkArgs p) {
   constexpr int NLA = 16 / RPI;                        // act loads per lane per stage
   constexpr int NLB = 16 * NB / RPI;                   // A_le loads per lane per stage
   constexpr int STAGE = 16 * (1 + NB) * KC;            // bf16 per wave stage
-  __shared__ SlotLists SL;
-  __shared__ const uint16_t* s_abase[MAX_EXPERTS];
-  __shared__ __attribute__((aligned(16))) uint16_t s_stage[NT_DELTA / 64][STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_stage[SHR_WAVES][STAGE];
 
-  const int ti = blockIdx.x;
-  if (ti >= gld<int>(p.counters)) return;
-  const Tile tile = load_tile(p.tiles + ti);
-  if (tile.bucket >= p.L) return;
-  const int E = p.src.E;
-  const int e0 = blockIdx.y * p.epg, e1 = min(e0 + p.epg, E);
-  if (e0 >= e1) return;
-  const int l = tile.bucket;
-  for (int i = threadIdx.x; i < e1 - e0; i += NT_DELTA)
-    s_abase[i] = reinterpret_cast<const uint16_t*>(gld<int64_t>(p.w_ptr_a + e0 + i)) +
-                 static_cast<long>(l) * p.stride_a;
-  list_slots(p.src, tile, SL);
-  if (blockIdx.y == 0) write_block_table(SL, E, ti, p);
-
+  const int ti = blockIdx.x / p.bpt;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = lane & 15, kq = lane >> 4;   // MFMA fragment roles
-  const int lrow = lane / CPR, lch = lane % CPR;  // coalesced-load roles
-  uint16_t* stA = s_stage[wave];     // [16][KC]
-  uint16_t* stB = stA + 16 * KC;     // [16*NB][KC]
-  uint16_t* u2t = p.u2 + static_cast<long>(ti) * p.cap * NB * 32;
+  const int bi = (blockIdx.x % p.bpt) * SHR_WAVES + wave;
+  if (ti >= gld<int>(p.counters)) return;
+  if (load_tile(p.tiles + ti).bucket >= p.L) return;  // no adapter, no blocks
+  if (bi >= gld<int>(p.tinfo + 2 * ti)) return;
+  const long tb = static_cast<long>(ti) * p.maxblk + bi;
 
-  int nblk = 0;
-  for (int e = e0; e < e1; ++e) nblk += (SL.off[e + 1] - SL.off[e] + 15) >> 4;
-  for (int blk = wave; blk < nblk; blk += NT_DELTA / 64) {
-    int e = e0, b = blk;
-    while (true) {
-      const int c = (SL.off[e + 1] - SL.off[e] + 15) >> 4;
-      if (b < c) break;
-      b -= c;
-      ++e;
+  const int row = lane & 15, kq = lane >> 4;      // MFMA fragment roles
+  const int lrow = lane / CPR, lch = lane % CPR;  // coalesced-load roles
+  uint16_t* stA = s_stage[wave];  // [16][KC]
+  uint16_t* stB = stA + 16 * KC;  // [16*NB][KC]
+  const uint16_t* Ale = reinterpret_cast<const uint16_t*>(gld<int64_t>(p.blk_a + tb));
+
+  const uint16_t* asrc[NLA];
+  const uint16_t* bsrc[NLB];
+#pragma unroll
+  for (int j = 0; j < NLA; ++j) {
+    const int r = j * RPI + lrow;  // 0..15
+    asrc[j] = p.act + static_cast<long>(gld<int>(p.blk_row + tb * 16 + r)) * p.I + lch * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < NLB; ++j) {
+    const int r = j * RPI + lrow;  // rank row 0 .. 16*NB-1 (clamped to real ranks)
+    bsrc[j] = Ale + static_cast<long>(min(r, p.rank - 1)) * p.I + lch * 8;
+  }
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nst = p.I / KC;  // full stages
+  // two register stages in flight: stage st + 2 is loaded while st feeds the MFMAs
+  u32x4 ra0[NLA], rb0[NLB], ra1[NLA], rb1[NLB];
+  auto gload = [&](u32x4 (&ra)[NLA], u32x4 (&rb)[NLB], int st) {
+    if (st < nst) {
+      const int k0 = st * KC;
+#pragma unroll
+      for (int j = 0; j < NLA; ++j) ra[j] = gld<u32x4>(asrc[j] + k0);
+#pragma unroll
+      for (int j = 0; j < NLB; ++j) rb[j] = gld<u32x4>(bsrc[j] + k0);
     }
-    const int base = SL.off[e] + b * 16;
-    const int cnt = min(16, SL.off[e + 1] - base);
-    const uint16_t* Ale = s_abase[e - e0];
-    const uint16_t* asrc[NLA];
-    const uint16_t* bsrc[NLB];
+  };
+  auto consume = [&](u32x4 (&ra)[NLA], u32x4 (&rb)[NLB], int st) {
+    // registers -> LDS; chunk c of stage row r sits at chunk c ^ (r % CPR)
 #pragma unroll
     for (int j = 0; j < NLA; ++j) {
-      const int r = j * RPI + lrow;  // 0..15
-      asrc[j] = p.act + static_cast<long>(SL.row[base + min(r, cnt - 1)]) * p.I + lch * 8;
+      const int r = j * RPI + lrow;
+      *reinterpret_cast<u32x4*>(stA + r * KC + ((lch ^ (r % CPR)) << 3)) = ra[j];
     }
 #pragma unroll
     for (int j = 0; j < NLB; ++j) {
-      const int r = j * RPI + lrow;  // rank row 0 .. 16*NB-1 (clamped to real ranks)
-      bsrc[j] = Ale + static_cast<long>(min(r, p.rank - 1)) * p.I + lch * 8;
+      const int r = j * RPI + lrow;
+      *reinterpret_cast<u32x4*>(stB + r * KC + ((lch ^ (r % CPR)) << 3)) = rb[j];
     }
-    f32x4 acc[NB];
+    __builtin_amdgcn_wave_barrier();
+    gload(ra, rb, st + 2);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nst = p.I / KC;  // full stages
-    // two register stages in flight: stage st + 2 is loaded while st feeds the MFMAs
-    u32x4 ra0[NLA], rb0[NLB], ra1[NLA], rb1[NLB];
-    auto gload = [&](u32x4 (&ra)[NLA], u32x4 (&rb)[NLB], int st) {
-      if (st < nst) {
-        const int k0 = st * KC;
-#pragma unroll
-        for (int j = 0; j < NLA; ++j) ra[j] = gld<u32x4>(asrc[j] + k0);
-#pragma unroll
-        for (int j = 0; j < NLB; ++j) rb[j] = gld<u32x4>(bsrc[j] + k0);
-      }
-    };
-    auto consume = [&](u32x4 (&ra)[NLA], u32x4 (&rb)[NLB], int st) {
-      // registers -> LDS; chunk c of stage row r sits at chunk c ^ (r % CPR)
-#pragma unroll
-      for (int j = 0; j < NLA; ++j) {
-        const int r = j * RPI + lrow;
-        *reinterpret_cast<u32x4*>(stA + r * KC + ((lch ^ (r % CPR)) << 3)) = ra[j];
-      }
-#pragma unroll
-      for (int j = 0; j < NLB; ++j) {
-        const int r = j * RPI + lrow;
-        *reinterpret_cast<u32x4*>(stB + r * KC + ((lch ^ (r % CPR)) << 3)) = rb[j];
-      }
-      __builtin_amdgcn_wave_barrier();
-      gload(ra, rb, st + 2);
-#pragma unroll
-      for (int s2 = 0; s2 < KC / 32; ++s2) {
-        const int c = 4 * s2 + kq;
-        const u32x4 fa =
-            *reinterpret_cast<const u32x4*>(stA + row * KC + ((c ^ (row % CPR)) << 3));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int rr = nb * 16 + row;
-          const u32x4 fb =
-              *reinterpret_cast<const u32x4*>(stB + rr * KC + ((c ^ (rr % CPR)) << 3));
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa),
-                                                            __builtin_bit_cast(bf16x8, fb), acc[nb],
-                                                            0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_wave_barrier();  // this stage's reads precede the next stage's writes
-    };
-    gload(ra0, rb0, 0);
-    gload(ra1, rb1, 1);
-    for (int st = 0; st < nst; st += 2) {
-      consume(ra0, rb0, st);
-      if (st + 1 < nst) consume(ra1, rb1, st + 1);
-    }
-    // K tail (I % KC != 0): fragments straight from memory
-    for (int k0 = nst * KC; k0 < p.I; k0 += 32) {
-      const bool kin = k0 + kq * 8 < p.I;  // I % 8 == 0
+    for (int s2 = 0; s2 < KC / 32; ++s2) {
+      const int c = 4 * s2 + kq;
       const u32x4 fa =
-          kin ? gld<u32x4>(p.act + static_cast<long>(SL.row[base + min(row, cnt - 1)]) * p.I + k0 +
-                           kq * 8)
-              : u32x4{0, 0, 0, 0};
+          *reinterpret_cast<const u32x4*>(stA + row * KC + ((c ^ (row % CPR)) << 3));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int rr = nb * 16 + row;
-        const u32x4 fb = (kin && rr < p.rank)
-                             ? gld<u32x4>(Ale + static_cast<long>(rr) * p.I + k0 + kq * 8)
-                             : u32x4{0, 0, 0, 0};
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, fa), __builtin_bit_cast(bf16x8, fb), acc[nb], 0, 0, 0);
+        const u32x4 fb =
+            *reinterpret_cast<const u32x4*>(stB + rr * KC + ((c ^ (rr % CPR)) << 3));
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa),
+                                                          __builtin_bit_cast(bf16x8, fb), acc[nb],
+                                                          0, 0, 0);
       }
     }
-    // acc[nb][q] = (A_le @ act)[slot row 4*kq + q][rank nb*16 + row]; padded rows/ranks -> 0
-    uint16_t* rec = u2t + static_cast<long>((SL.poff[e] + b * 16) / 16) * NB * 512;
+    __builtin_amdgcn_wave_barrier();  // this stage's reads precede the next stage's writes
+  };
+  gload(ra0, rb0, 0);
+  gload(ra1, rb1, 1);
+  for (int st = 0; st < nst; st += 2) {
+    consume(ra0, rb0, st);
+    if (st + 1 < nst) consume(ra1, rb1, st + 1);
+  }
+  // K tail (I % KC != 0): fragments straight from memory
+  for (int k0 = nst * KC; k0 < p.I; k0 += 32) {
+    const bool kin = k0 + kq * 8 < p.I;  // I % 8 == 0
+    const u32x4 fa =
+        kin ? gld<u32x4>(p.act + static_cast<long>(gld<int>(p.blk_row + tb * 16 + row)) * p.I +
+                         k0 + kq * 8)
+            : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int srow = 4 * kq + q;
-      float f = 0.f;
-      if (srow < cnt)
-        f = p.scale * gld<float>(p.topk_weights + (SL.list[base + srow] & 0xffffff));
+    for (int nb = 0; nb < NB; ++nb) {
+      const int rr = nb * 16 + row;
+      const u32x4 fb = (kin && rr < p.rank)
+                           ? gld<u32x4>(Ale + static_cast<long>(rr) * p.I + k0 + kq * 8)
+                           : u32x4{0, 0, 0, 0};
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, fa), __builtin_bit_cast(bf16x8, fb), acc[nb], 0, 0, 0);
+    }
+  }
+  // acc[nb][j] = (A_le @ act)[slot 4*kq + j][rank nb*16 + row]; empty slots have weight 0
+  uint16_t* rec = p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32;
+  const f32x4 wv = __builtin_bit_cast(f32x4, gld<u32x4>(p.blk_w + tb * 16 + 4 * kq));
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float v = nb * 16 + row < p.rank ? acc[nb][q] * f : 0.f;
-        const uint32_t hi = f32_to_bf16_rne(v);
-        const uint32_t lo = f32_to_bf16_rne(v - bf16_bits_to_f32(hi));
-        gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), static_cast<uint16_t>(hi));
-        gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), static_cast<uint16_t>(lo));
-      }
+  for (int j = 0; j < 4; ++j) {
+    const int srow = 4 * kq + j;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float v = nb * 16 + row < p.rank ? acc[nb][j] * wv[j] : 0.f;
+      const uint32_t hi = f32_to_bf16_rne(v);
+      const uint32_t lo = f32_to_bf16_rne(v - bf16_bits_to_f32(hi));
+      gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), static_cast<uint16_t>(hi));
+      gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), static_cast<uint16_t>(lo));
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. expand
+// 4. expand
 // ---------------------------------------------------------------------------
 constexpr int EXP_CW = 128;   // output columns per workgroup
 constexpr int NT_EXP = 256;   // expand workgroup: 4 wavefronts x 2 groups of 16 columns
@@ -846,7 +885,10 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   int32_t* tok_list = reinterpret_cast<int32_t*>(ws + ly.tok_list);
   Tile* tiles = reinterpret_cast<Tile*>(ws + ly.tiles);
   int32_t* counters = reinterpret_cast<int32_t*>(ws + ly.counters);
+  int64_t* blk_a = reinterpret_cast<int64_t*>(ws + ly.blk_a);
   int64_t* blk_b = reinterpret_cast<int64_t*>(ws + ly.blk_b);
+  int32_t* blk_row = reinterpret_cast<int32_t*>(ws + ly.blk_row);
+  float* blk_w = reinterpret_cast<float*>(ws + ly.blk_w);
   uint32_t* blk_tl = reinterpret_cast<uint32_t*>(ws + ly.blk_tl);
   int32_t* tinfo = reinterpret_cast<int32_t*>(ws + ly.tinfo);
   const int tt = tile_tokens(top_k);
@@ -857,24 +899,24 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   mi_status st = launch_status("bgmv_moe_gemm2_lora_delta (plan)");
   if (st != MI_OK) return st;
 
-  const SlotSrc src{tok_list, perm, topk_ids, static_cast<int>(top_k),
+  const SlotSrc src{tok_list, perm, topk_ids, topk_weights, static_cast<int>(top_k),
                     static_cast<int>(padded_rows), static_cast<int>(E)};
-  const int cus = num_cus();
   const int nb = rank_chunks(rank);
   if (L > 0) {
-    // experts per shrink workgroup: enough workgroups to cover the chip ~4x
-    const int64_t est_tiles = T / tt + 1;
-    int64_t groups = (4 * cus + est_tiles - 1) / est_tiles;
-    if (groups > E) groups = E;
-    if (groups < 1) groups = 1;
-    const int epg = static_cast<int>((E + groups - 1) / groups);
-    const int ngroups = static_cast<int>((E + epg - 1) / epg);
-    ShrinkArgs sa{src, static_cast<const uint16_t*>(act), w_ptr_a, static_cast<long>(lora_stride_a),
-                  topk_weights, tiles, counters, u2, w_ptr_b, static_cast<long>(lora_stride_b),
-                  blk_b, blk_tl, tinfo, ly.cap,
-                  static_cast<int>(inter_size), static_cast<int>(L), static_cast<int>(rank), epg,
-                  ly.maxblk, scale};
-    const dim3 sgrid(ntiles, ngroups), sblock(NT_DELTA);
+    ListArgs la{src, tiles, counters, topk_weights, w_ptr_a, static_cast<long>(lora_stride_a),
+                w_ptr_b, static_cast<long>(lora_stride_b), blk_a, blk_b, blk_tl, blk_row, blk_w,
+                tinfo, static_cast<int>(L), ly.maxblk, scale};
+    hipLaunchKernelGGL(list_kernel, dim3(ntiles), dim3(NT_DELTA), 0, s, la);
+    st = launch_status("bgmv_moe_gemm2_lora_delta (list)");
+    if (st != MI_OK) return st;
+
+    const int bpt = (ly.maxblk + SHR_WAVES - 1) / SHR_WAVES;  // shrink workgroups per tile
+    const long swg = static_cast<long>(ntiles) * bpt;
+    MI_REQUIRE(swg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
+    ShrinkArgs sa{static_cast<const uint16_t*>(act), tiles, counters, blk_a, blk_row, blk_w, tinfo,
+                  u2, ly.cap, static_cast<int>(inter_size), static_cast<int>(L),
+                  static_cast<int>(rank), ly.maxblk, bpt};
+    const dim3 sgrid(static_cast<unsigned>(swg)), sblock(64 * SHR_WAVES);
     switch (nb) {
       case 1: hipLaunchKernelGGL(shrink_kernel<1>, sgrid, sblock, 0, s, sa); break;
       case 2: hipLaunchKernelGGL(shrink_kernel<2>, sgrid, sblock, 0, s, sa); break;

@@ -157,3 +157,20 @@ def test_workspace_contents_do_not_matter(gpu):
     ref = run_oracle(case, tb)
     for o in outs:
         assert np.array_equal(bits16(o), f64_to_bf16_bits(ref))
+
+
+def test_token_routed_twice_to_one_expert(gpu):
+    """Routing that repeats an expert for a token: both slots count (the
+    formula sums over j); such tiles accumulate with LDS atomics."""
+    case = synth.delta_int_probe(seed=109, T=40, top_k=4, E=6, I=64, H=256, L=2, r=16)
+    ids = case.topk_ids.clone()
+    ids[::3, 1] = ids[::3, 0]      # every third token: slot 1 repeats slot 0's expert
+    ids[5, 2] = ids[5, 3] = ids[5, 0]
+    case = to_dev(synth.DeltaCase(case.name, case.act, case.perm, case.A, case.B, ids,
+                                  case.topk_weights, case.lora_ids, case.scale, case.extra), gpu)
+    tb = tables(case, scattered=True)
+    out = run_gpu(case, tb)
+    ref = run_oracle(case, tb)
+    assert np.array_equal(bits16(out), f64_to_bf16_bits(ref))
+    out2 = run_gpu(case, tb)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
