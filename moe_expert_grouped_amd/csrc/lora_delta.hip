@@ -4,29 +4,26 @@
 // (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta, formula and parameters).
 //
 // Work is organised around token tiles: up to TT tokens of one adapter.
-// Three launches on the caller's stream, no host reads:
+// Four launches on the caller's stream, no host reads:
 //
 //  1. plan    (one workgroup) -- buckets the T tokens by adapter (bucket
 //             num_adapters collects tokens without a valid adapter) and cuts
 //             every bucket into tiles of <= TT tokens.
-//  2. shrink  -- one workgroup per (tile, group of experts).  Every workgroup
-//             lists the tile's active slots (permuted row in [0, padded_rows),
-//             expert in [0, num_experts)) by expert in LDS, each expert's list
-//             sorted by slot, and cuts every expert's list into 16-slot
-//             blocks; the workgroup of expert group 0 stores the tile's block
-//             table (expert and token rows of each block) for the expand.  A
-//             wavefront turns one block into u = (scale*w) * A_le @ act[row]
-//             with v_mfma_f32_16x16x32_bf16: the activation rows and A_le are
-//             streamed with coalesced 16-byte loads (two stages in flight in
-//             registers) into a wave-private, swizzled LDS stage and read back
-//             as MFMA fragments.  (An MFMA fragment puts neighbouring lanes on
-//             different rows; loading fragments straight from memory would
-//             split every instruction into 64 scattered requests.)  u is
-//             written as bf16 hi = bf16(u) and lo = bf16(u - hi) (~16
-//             significand bits together), directly in the fragment order the
-//             expand consumes: one contiguous 1 KiB record per block and 16
-//             ranks; record i belongs to block i of the table.
-//  3. expand  -- one workgroup per (tile, 128 output columns), in an order
+//  2. list    (one workgroup per tile) -- lists the tile's active slots
+//             (permuted row in [0, padded_rows), expert in [0, num_experts))
+//             by expert, each expert's list sorted by slot, and cuts every
+//             list into 16-slot blocks.  Per block it stores the A_le and
+//             B_le addresses and, per slot, the token row, activation row and
+//             scale*w -- the block table both later kernels read.
+//  3. shrink  (one wavefront per block) -- u = (scale*w) * A_le @ act[row]
+//             with v_mfma_f32_16x16x32_bf16: the block's activation rows and
+//             A_le are streamed with coalesced 16-byte loads (two K stages in
+//             flight in registers) into a wave-private, swizzled LDS stage
+//             and read back as MFMA fragments.  u is written as bf16 hi =
+//             bf16(u) and lo = bf16(u - hi) (~16 significand bits together)
+//             in the fragment order the expand consumes: one contiguous 1 KiB
+//             record per block and 16 ranks; record i belongs to block i.
+//  4. expand  -- one workgroup per (tile, 128 output columns), in an order
 //             that keeps the tiles of one column chunk on one XCD (they share
 //             B columns through its L2).  An fp32 accumulator [TT tokens x 128
 //             columns] lives in LDS.  Each of 4 wavefronts owns 32 columns and
@@ -35,14 +32,15 @@
 //             B_le] (16 columns x 32) and [u_hi ; u_lo] (32 x 16 slots) and
 //             adds the 4 consecutive columns each lane holds into the slot's
 //             token row with one 16-byte LDS read-modify-write.  The u record,
-//             the B_le fragments (16 columns x 16 ranks are 512 contiguous
-//             bytes) and the token rows of a block are loaded several blocks
-//             ahead in a register ring.  The wavefront owns its columns and a
-//             block never holds one token twice (unless the routing repeats an
-//             expert for a token; such a tile uses LDS float atomics), so
-//             every accumulator element is updated by one wavefront in block
-//             order: the summation order per token is fixed and the result is
-//             bitwise repeatable.  Tokens without adapter get +0 rows.
+//             the B_le fragments (16 columns x 4 ranks per lane, 512 contiguous
+//             bytes per wave) and the token rows of a block are loaded several
+//             blocks ahead in a register ring.  The wavefront owns its columns
+//             and a block never holds one token twice (unless the routing
+//             repeats an expert for a token; such a tile uses LDS float
+//             atomics), so every accumulator element is updated by one
+//             wavefront in block order: the summation order per token is fixed
+//             and the result is bitwise repeatable.  Tokens without adapter
+//             get +0 rows.
 #include "common.hpp"
 
 namespace mi {

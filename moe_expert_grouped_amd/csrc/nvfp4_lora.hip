@@ -193,13 +193,26 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
     }
   };
   auto compute = [&](const NvStage& st) {
+    // the 4 UE4M3 scale bytes of each row as fp16, two per conversion (exact)
+    f16x2 sa01[FM], sa23[FM], sb01[FN], sb23[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      sa01[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.sa[i], 1.0f, false);
+      sa23[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.sa[i], 1.0f, true);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      sb01[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.sb[j], 1.0f, false);
+      sb23[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.sb[j], 1.0f, true);
+    }
+    auto splat = [](f16x2 v, int hi) { return hi ? f16x2{v.y, v.y} : f16x2{v.x, v.x}; };
 #pragma unroll
     for (int t = 0; t < 4; ++t) {  // scale block t: MFMA steps 2t, 2t+1
       f16x2 psa[FM], psb[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) psa[i] = scale_pair((st.sa[i] >> (8 * t)) & 0xff);
+      for (int i = 0; i < FM; ++i) psa[i] = splat(t < 2 ? sa01[i] : sa23[i], t & 1);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) psb[j] = scale_pair((st.sb[j] >> (8 * t)) & 0xff);
+      for (int j = 0; j < FN; ++j) psb[j] = splat(t < 2 ? sb01[j] : sb23[j], t & 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int s = 2 * t + u;  // code word s of the lane's 8
