@@ -1,6 +1,9 @@
 """Number formats used by the pages, decoded exactly into float64.
 
 - bf16: the 16 high bits of an IEEE binary32.
+- fp16: IEEE binary16 (1 sign, 5 exponent bits with bias 15, 10 mantissa
+  bits; subnormals at exponent 0) -- the other input and output type the
+  grouped_mm_bf16 page lists.
 - E2M1 (the NVFP4 element code, ``flashinfer.gemm.mm_nvfp4_lora`` --
   "E2M1 codes packed two per byte"): 1 sign, 2 exponent (bias 1), 1 mantissa
   bit; magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.  The pages only name the
@@ -49,6 +52,56 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     bits = bits | (np.signbit(x).astype(np.uint16) << np.uint16(15))
     bits = np.where(np.isnan(x), np.uint16(0x7FC0), bits)
     return bits.astype(np.uint16)
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    """fp16 bit patterns (uint16) -> float64, from the field definition."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(u >> 15, -1.0, 1.0)
+    E = (u >> 10) & 0x1F
+    M = u & 0x3FF
+    mag = np.where(E == 0, M * 2.0 ** -24, (1.0 + M / 1024.0) * np.ldexp(1.0, E - 15))
+    val = sign * mag
+    val = np.where((E == 31) & (M == 0), sign * np.inf, val)
+    return np.where((E == 31) & (M != 0), np.nan, val)
+
+
+def f64_to_f16_bits(x) -> np.ndarray:
+    """Round float64 values to fp16 once, to nearest with ties to even.
+
+    Same construction as :func:`f64_to_bf16_bits`: 11 significant bits,
+    subnormal spacing 2**-24, overflow past 65504 gives +-Inf, NaN gives
+    0x7E00.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    finite = np.isfinite(x)
+    axf = np.where(finite, ax, 0.0)
+    _, e = np.frexp(axf)
+    q = np.maximum(e - 11, -24)
+    y = np.ldexp(np.rint(np.ldexp(axf, -q)), q)
+    overflow = y > 65504.0
+    y = np.where(overflow, 0.0, y)
+    # y is now an exact fp16 magnitude: encode its fields
+    _, ey = np.frexp(np.where(y > 0, y, 1.0))
+    normal = y >= 2.0 ** -14
+    E = np.where(normal, ey - 1 + 15, 0)
+    M = np.where(normal, np.ldexp(y, -(ey - 1)) * 1024.0 - 1024.0, y * 2.0 ** 24)
+    bits = ((E.astype(np.int64) << 10) | np.rint(M).astype(np.int64)).astype(np.uint16)
+    bits = np.where(y == 0, np.uint16(0), bits)
+    bits = np.where(overflow | np.isinf(x), np.uint16(0x7C00), bits)
+    bits = bits | (np.signbit(x).astype(np.uint16) << np.uint16(15))
+    bits = np.where(np.isnan(x), np.uint16(0x7E00), bits)
+    return bits.astype(np.uint16)
+
+
+def to_f64(bits, dtype: str) -> np.ndarray:
+    """Decode 16-bit patterns of the named type ("bf16" or "f16")."""
+    if dtype == "bf16":
+        return bf16_to_f64(bits)
+    if dtype == "f16":
+        return f16_to_f64(bits)
+    raise ValueError(dtype)
 
 
 def e2m1_to_f64(codes) -> np.ndarray:

@@ -10,24 +10,26 @@ Readings where the page is silent:
 - the output has ``a.shape[0]`` rows; rows outside
   ``[m_indptr[0], m_indptr[-1])`` are not defined by the formula and are
   reported as not written;
-- the value is the exact product of the bf16 inputs (computed in float64);
-  the GPU rounds it once to the output dtype.
+- the value is the exact product of the bf16 (or fp16) inputs, computed in
+  float64; the GPU rounds it once to the output dtype.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .formats import bf16_to_f64
+from .formats import bf16_to_f64, to_f64
 
 
-def grouped_mm(a_bits: np.ndarray, b_bits: np.ndarray, m_indptr: np.ndarray):
+def grouped_mm(a_bits: np.ndarray, b_bits: np.ndarray, m_indptr: np.ndarray,
+               dtype: str = "bf16"):
     """Return ``(out, written)``: float64 ``[cum_m, n]`` and a bool row mask.
 
-    ``a_bits`` uint16 ``[cum_m, k]``, ``b_bits`` uint16 ``[E, n, k]``,
-    ``m_indptr`` int ``[E+1]`` (non-decreasing).
+    ``a_bits`` uint16 ``[cum_m, k]``, ``b_bits`` uint16 ``[E, n, k]`` (bit
+    patterns of ``dtype``, "bf16" or "f16"), ``m_indptr`` int ``[E+1]``
+    (non-decreasing).
     """
-    A = bf16_to_f64(a_bits)
-    B = bf16_to_f64(b_bits)
+    A = to_f64(a_bits, dtype)
+    B = to_f64(b_bits, dtype)
     m_indptr = np.asarray(m_indptr, dtype=np.int64)
     cum_m = A.shape[0]
     E, n, k = B.shape

@@ -83,3 +83,31 @@ def test_e2m1_times_ue4m3_is_exact_in_bf16():
     prod = (v[:, None] * s[None, :]).ravel()
     back = F.bf16_to_f64(F.f64_to_bf16_bits(prod))
     assert np.array_equal(back, prod)
+
+
+def test_f16_decode_matches_numpy_on_all_patterns():
+    from oracle.formats import f16_to_f64
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = bits.view(np.float16).astype(np.float64)
+    got = f16_to_f64(bits)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_f16_rounding_matches_numpy_and_hand_cases():
+    from oracle.formats import f64_to_f16_bits
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.normal(0, 1, 20000), rng.normal(0, 1e4, 5000),
+                        rng.normal(0, 1e-6, 5000), [0.0, -0.0, 65504.0, 65520.0, 1e6, -1e6]])
+    want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(f64_to_f16_bits(x), want)
+    # ties to even: 1 + 2**-11 lies halfway between 1 and 1 + 2**-10 -> 1 (even)
+    assert f64_to_f16_bits(np.array([1 + 2.0 ** -11]))[0] == 0x3C00
+    # 1 + 3*2**-11 lies halfway between 1 + 2**-10 and 1 + 2**-9 -> the even one
+    assert f64_to_f16_bits(np.array([1 + 3 * 2.0 ** -11]))[0] == 0x3C02
+    # smallest subnormal and the halfway point below it
+    assert f64_to_f16_bits(np.array([2.0 ** -24]))[0] == 0x0001
+    assert f64_to_f16_bits(np.array([2.0 ** -25]))[0] == 0x0000
+    assert f64_to_f16_bits(np.array([np.nan]))[0] == 0x7E00

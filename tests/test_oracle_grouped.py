@@ -81,3 +81,20 @@ def test_selected_rows_match_full():
     cols = [1, 4]
     sel = grouped_mm_rows(a[rows], lambda e, c: b[e][c], mi, rows, cols)
     assert np.array_equal(sel, full[np.ix_(rows, cols)])
+
+
+def test_fp16_inputs_decode_as_fp16():
+    # small integers are exact in both types: the fp16 reading of the fp16 bits
+    # and the bf16 reading of the bf16 bits of the same values agree
+    from oracle.formats import f64_to_bf16_bits, f64_to_f16_bits
+    rng = np.random.default_rng(3)
+    a = rng.integers(-4, 5, (20, 32)).astype(np.float64)
+    b = rng.integers(-4, 5, (3, 16, 32)).astype(np.float64)
+    mi = np.array([0, 7, 7, 20])
+    o16, w16 = grouped_mm(f64_to_f16_bits(a), f64_to_f16_bits(b), mi, "f16")
+    ob, wb = grouped_mm(f64_to_bf16_bits(a), f64_to_bf16_bits(b), mi)
+    assert np.array_equal(o16, ob) and np.array_equal(w16, wb)
+    # a value bf16 cannot hold: 1 + 2**-10 is exact in fp16 only
+    one = f64_to_f16_bits(np.array([[1 + 2.0 ** -10]]))
+    o, _ = grouped_mm(one, one.reshape(1, 1, 1), np.array([0, 1]), "f16")
+    assert o[0, 0] == (1 + 2.0 ** -10) ** 2
