@@ -65,18 +65,19 @@ MI_API int mi_abi_version(void);
  *     out[s:t, :] = a[s:t, :] @ b[e]^T
  * accumulated in fp32 and rounded once to out_dtype.
  *
- *   a         bf16 [m_rows, k]
- *   b         bf16 [batch, n, k]    (K-major: row j of b[e] is output column j)
+ *   a         [m_rows, k] of ab_dtype (MI_BF16 or MI_F16: "bf16 or fp16" in the
+ *             parameter list)
+ *   b         [batch, n, k] of ab_dtype  (K-major: row j of b[e] is output column j)
  *   m_indptr  int32 [batch + 1], device, non-decreasing, 0 <= values <= m_rows;
  *             read on the device only -- empty groups are skipped, no padding
- *   out       [m_rows, n] of out_dtype (MI_BF16 or MI_F32); only rows
+ *   out       [m_rows, n] of out_dtype (MI_BF16, MI_F16 or MI_F32); only rows
  *             [m_indptr[0], m_indptr[batch]) are written, the rest untouched
  * Requirements: m_rows >= 0, batch >= 1, n % 256 == 0, k % 64 == 0 (the
  * device-walk backend's shape rule on the page), k >= 64.
  */
 MI_API mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k,
-                             const void* b, int64_t batch, int64_t n,
-                             const int32_t* m_indptr,
+                             mi_dtype ab_dtype, const void* b, int64_t batch,
+                             int64_t n, const int32_t* m_indptr,
                              void* out, mi_dtype out_dtype, void* stream);
 
 /*
@@ -101,7 +102,7 @@ MI_API mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k,
  *   workspace    device scratch of at least mi_moe_fc2_lora_delta_workspace_size()
  *                bytes, 256-byte aligned; contents need no initialisation
  * The intermediate A_down @ act stays fp32; the result is rounded once.
- * Requirements: lora_dtype MI_BF16; out_dtype MI_BF16 or MI_F32; rank % 8 == 0,
+ * Requirements: lora_dtype MI_BF16; out_dtype MI_BF16, MI_F16 or MI_F32; rank % 8 == 0,
  * 8 <= rank <= 128; inter_size % 8 == 0; hidden % 128 == 0; 1 <= top_k <= 32;
  * lora strides multiples of 8; num_experts <= 512.
  */

@@ -69,8 +69,8 @@ def grouped_mm_bf16(a: torch.Tensor, b: torch.Tensor, m_indptr: torch.Tensor,
     signature compatibility; there is one program and ``tactic`` must be -1.
     """
     _need(tactic == -1, "grouped_mm_bf16: tactic must be -1 (single program)")
-    _need(a.dtype == torch.bfloat16 and b.dtype == torch.bfloat16,
-          "grouped_mm_bf16: a and b must be bfloat16")
+    _need(a.dtype in (torch.bfloat16, torch.float16) and b.dtype == a.dtype,
+          "grouped_mm_bf16: a and b must both be bfloat16 or both float16")
     _need(a.dim() == 2 and b.dim() == 3 and b.shape[2] == a.shape[1],
           "grouped_mm_bf16: a must be (cum_m, k) and b (batch_size, n, k)")
     _need(m_indptr.dtype == torch.int32 and m_indptr.shape == (b.shape[0] + 1,),
@@ -83,9 +83,9 @@ def grouped_mm_bf16(a: torch.Tensor, b: torch.Tensor, m_indptr: torch.Tensor,
         out = torch.zeros((a.shape[0], b.shape[1]), dtype=out_dtype, device=a.device)
     _need(out.shape == (a.shape[0], b.shape[1]) and out.dtype == out_dtype and out.is_contiguous(),
           "grouped_mm_bf16: out must be a contiguous (cum_m, n) tensor of out_dtype")
-    check(_lib.lib().mi_grouped_mm_bf16(_ptr(a), a.shape[0], a.shape[1], _ptr(b), b.shape[0],
-                                        b.shape[1], _ptr(m_indptr), _ptr(out), _DT[out_dtype],
-                                        _stream(a.device)))
+    check(_lib.lib().mi_grouped_mm_bf16(_ptr(a), a.shape[0], a.shape[1], _DT[a.dtype], _ptr(b),
+                                        b.shape[0], b.shape[1], _ptr(m_indptr), _ptr(out),
+                                        _DT[out_dtype], _stream(a.device)))
     return out
 
 

@@ -49,18 +49,35 @@ __device__ __forceinline__ void gm_lstore(uint16_t* lds, const u32x4 (&r)[C], co
   for (int i = 0; i < C; ++i) *reinterpret_cast<u32x4*>(lds + off[i]) = r[i];
 }
 
+// output element types: bf16 bits, fp16, fp32; one rounding to nearest even
+struct Bf16Out { uint16_t bits; };
 template <typename OutT>
 __device__ __forceinline__ void store_out(OutT* p, float v);
 template <>
-__device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
-  *p = static_cast<uint16_t>(f32_to_bf16_rne(v));
+__device__ __forceinline__ void store_out<Bf16Out>(Bf16Out* p, float v) {
+  p->bits = static_cast<uint16_t>(f32_to_bf16_rne(v));
+}
+template <>
+__device__ __forceinline__ void store_out<_Float16>(_Float16* p, float v) {
+  *p = static_cast<_Float16>(v);  // IEEE conversion, round to nearest even
 }
 template <>
 __device__ __forceinline__ void store_out<float>(float* p, float v) {
   *p = v;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int P, typename OutT>
+// the MFMA for the input type: bf16 or fp16 operands, fp32 accumulation
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int P, bool F16, typename OutT>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
     const int32_t* __restrict__ m_indptr, OutT* __restrict__ out, int m_rows, int k, int n,
@@ -218,23 +235,21 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
 #pragma unroll
             for (int s = 0; s < BK / 16; ++s) {
               const int kc = 2 * s + (lane >> 5);
-              bf16x8 fa[FM], fb[FN];
+              u32x4 fa[FM], fb[FN];
 #pragma unroll
               for (int i = 0; i < FM; ++i) {
                 const int r = wm * WTM + i * 32 + (lane & 31);
-                fa[i] = *reinterpret_cast<const bf16x8*>(sA + r * BK + ((kc ^ lds_swz<CPR>(r)) << 3));
+                fa[i] = *reinterpret_cast<const u32x4*>(sA + r * BK + ((kc ^ lds_swz<CPR>(r)) << 3));
               }
 #pragma unroll
               for (int j = 0; j < FN; ++j) {
                 const int r = wn * WTN + j * 32 + (lane & 31);
-                fb[j] = *reinterpret_cast<const bf16x8*>(sB + r * BK + ((kc ^ lds_swz<CPR>(r)) << 3));
+                fb[j] = *reinterpret_cast<const u32x4*>(sB + r * BK + ((kc ^ lds_swz<CPR>(r)) << 3));
               }
 #pragma unroll
               for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                  acc[i][j] =
-                      __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<F16>(fa[i], fb[j], acc[i][j]);
             }
           }
           // stage kt+1 sits in register slot (q+1) % P; refill that slot with stage kt+1+P
@@ -280,7 +295,7 @@ int num_cus() {
   return cached[dev];
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int P, typename OutT>
+template <int BM, int BN, int BK, int WM, int WN, int P, bool F16, typename OutT>
 mi_status launch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b,
                          int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
                          hipStream_t stream, int occupancy) {
@@ -290,14 +305,14 @@ mi_status launch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b
   if (G > ub_tiles) G = ub_tiles;
   G = ((G + 7) / 8) * 8;
   if (G < 8) G = 8;
-  hipLaunchKernelGGL((grouped_mm_kernel<BM, BN, BK, WM, WN, P, OutT>), dim3(G), dim3(64 * WM * WN), 0,
+  hipLaunchKernelGGL((grouped_mm_kernel<BM, BN, BK, WM, WN, P, F16, OutT>), dim3(G), dim3(64 * WM * WN), 0,
                      stream, static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
                      m_indptr, static_cast<OutT*>(out), static_cast<int>(m_rows),
                      static_cast<int>(k), static_cast<int>(n), static_cast<int>(batch));
   return launch_status("grouped_mm_bf16");
 }
 
-template <typename OutT>
+template <bool F16, typename OutT>
 mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b,
                            int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
                            hipStream_t stream) {
@@ -306,17 +321,18 @@ mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void*
   // and take 64x64 tiles, two workgroups per CU, with 4 K steps in flight.
   const int64_t avg = m_rows / batch;
   if (avg >= 192)
-    return launch_grouped<256, 256, 64, 4, 2, 1, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
+    return launch_grouped<256, 256, 64, 4, 2, 1, F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
                                                    1);
-  return launch_grouped<64, 64, 64, 2, 2, 4, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
+  return launch_grouped<64, 64, 64, 2, 2, 4, F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
 }
 
 }  // namespace
 }  // namespace mi
 
-extern "C" mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k, const void* b,
-                                        int64_t batch, int64_t n, const int32_t* m_indptr,
-                                        void* out, mi_dtype out_dtype, void* stream) {
+extern "C" mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k, mi_dtype ab_dtype,
+                                        const void* b, int64_t batch, int64_t n,
+                                        const int32_t* m_indptr, void* out, mi_dtype out_dtype,
+                                        void* stream) {
   using namespace mi;
   clear_error();
   MI_REQUIRE(batch >= 1, "grouped_mm_bf16: batch_size must be >= 1 (got %lld)", (long long)batch);
@@ -329,16 +345,23 @@ extern "C" mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k
   MI_REQUIRE(k > 0 && k % 64 == 0, "grouped_mm_bf16: k %% 64 == 0 required (got k=%lld)",
              (long long)k);
   MI_REQUIRE(n < (1LL << 31) && k < (1LL << 31), "grouped_mm_bf16: n or k too large");
+  MI_REQUIRE(ab_dtype == MI_BF16 || ab_dtype == MI_F16,
+             "grouped_mm_bf16: a and b must be bf16 or fp16");
   MI_REQUIRE(out_dtype == MI_BF16 || out_dtype == MI_F32 || out_dtype == MI_F16,
              "grouped_mm_bf16: out_dtype must be bf16, fp16 or fp32");
-  MI_REQUIRE_SUPPORTED(out_dtype != MI_F16, "grouped_mm_bf16: fp16 output is not implemented");
   MI_REQUIRE(m_indptr != nullptr, "grouped_mm_bf16: m_indptr is null");
   MI_REQUIRE(b != nullptr, "grouped_mm_bf16: b is null");
   if (m_rows == 0) return MI_OK;
   MI_REQUIRE(a != nullptr && out != nullptr, "grouped_mm_bf16: a/out is null");
   MI_REQUIRE(aligned16(a) && aligned16(b), "grouped_mm_bf16: a and b must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f16 = ab_dtype == MI_F16;
   if (out_dtype == MI_BF16)
-    return dispatch_grouped<uint16_t>(a, m_rows, k, b, batch, n, m_indptr, out, s);
-  return dispatch_grouped<float>(a, m_rows, k, b, batch, n, m_indptr, out, s);
+    return f16 ? dispatch_grouped<true, Bf16Out>(a, m_rows, k, b, batch, n, m_indptr, out, s)
+               : dispatch_grouped<false, Bf16Out>(a, m_rows, k, b, batch, n, m_indptr, out, s);
+  if (out_dtype == MI_F16)
+    return f16 ? dispatch_grouped<true, _Float16>(a, m_rows, k, b, batch, n, m_indptr, out, s)
+               : dispatch_grouped<false, _Float16>(a, m_rows, k, b, batch, n, m_indptr, out, s);
+  return f16 ? dispatch_grouped<true, float>(a, m_rows, k, b, batch, n, m_indptr, out, s)
+             : dispatch_grouped<false, float>(a, m_rows, k, b, batch, n, m_indptr, out, s);
 }

@@ -571,7 +571,7 @@ struct ExpandArgs {
   void* out;
   long cap;
   int L, H, rank, maxblk, max_tiles, nch;
-  int out_f32;
+  int out_kind;  // 0 bf16, 1 fp32, 2 fp16
 };
 
 // accumulator rows of EXP_CW floats; 16-byte chunk c of row tl sits at c ^ (tl & 31)
@@ -758,7 +758,7 @@ __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
     for (int i = tid; i < tile.count * (EXP_CW / 4); i += NT_EXP) {
       const int tl = i / (EXP_CW / 4), c = (i % (EXP_CW / 4)) * 4;
       const long o = static_cast<long>(gld<int>(p.tok_list + tile.start + tl)) * p.H + h0 + c;
-      if (p.out_f32)
+      if (p.out_kind == 1)
         gst<f32x4>(static_cast<float*>(p.out) + o, f32x4{0.f, 0.f, 0.f, 0.f});
       else
         gst<uint64_t>(static_cast<uint16_t*>(p.out) + o, 0ull);
@@ -790,9 +790,16 @@ __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
     const long o = static_cast<long>(gld<int>(p.tok_list + tile.start + tl)) * p.H + h0 + c;
     const f32x4 v0 = a[acc_chunk(tl, c / 4)];
     const f32x4 v1 = a[acc_chunk(tl, c / 4 + 1)];
-    if (p.out_f32) {
+    if (p.out_kind == 1) {
       gst<f32x4>(static_cast<float*>(p.out) + o, v0);
       gst<f32x4>(static_cast<float*>(p.out) + o + 4, v1);
+    } else if (p.out_kind == 2) {  // IEEE fp16, round to nearest even
+      typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+      const h8 h = {static_cast<_Float16>(v0.x), static_cast<_Float16>(v0.y),
+                    static_cast<_Float16>(v0.z), static_cast<_Float16>(v0.w),
+                    static_cast<_Float16>(v1.x), static_cast<_Float16>(v1.y),
+                    static_cast<_Float16>(v1.z), static_cast<_Float16>(v1.w)};
+      gst<u32x4>(static_cast<uint16_t*>(p.out) + o, __builtin_bit_cast(u32x4, h));
     } else {
       u32x4 w;
       w.x = pack_bf16x2(v0.x, v0.y);
@@ -859,7 +866,6 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   MI_REQUIRE_SUPPORTED(lora_dtype == MI_BF16, "bgmv_moe_gemm2_lora_delta: lora_dtype must be bf16");
   MI_REQUIRE(out_dtype == MI_BF16 || out_dtype == MI_F32 || out_dtype == MI_F16,
              "bgmv_moe_gemm2_lora_delta: out_dtype must be bf16, fp16 or fp32");
-  MI_REQUIRE_SUPPORTED(out_dtype != MI_F16, "bgmv_moe_gemm2_lora_delta: fp16 output not implemented");
   if (T == 0) return MI_OK;
   MI_REQUIRE(out != nullptr, "bgmv_moe_gemm2_lora_delta: out is null");
   MI_REQUIRE(aligned16(out), "bgmv_moe_gemm2_lora_delta: out must be 16-byte aligned");
@@ -928,7 +934,7 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   const int nch = static_cast<int>(H / EXP_CW);
   ExpandArgs ea{tok_list, tiles, counters, u2, blk_b, blk_tl, tinfo, out, ly.cap,
                 static_cast<int>(L), static_cast<int>(H), static_cast<int>(rank), ly.maxblk,
-                ntiles, nch, out_dtype == MI_F32 ? 1 : 0};
+                ntiles, nch, out_dtype == MI_F32 ? 1 : (out_dtype == MI_F16 ? 2 : 0)};
   // whole runs of 8 tiles x nch chunks, rounded to a multiple of the 8 XCDs
   const long ewg = ((static_cast<long>(ntiles) + 7) / 8 * 8 * nch + 7) & ~7L;
   MI_REQUIRE(ewg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");

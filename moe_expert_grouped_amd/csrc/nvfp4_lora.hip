@@ -32,7 +32,6 @@ namespace mi {
 namespace {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int NV_BM = 256, NV_BN = 256;  // workgroup tile
 constexpr int NV_KC = 128;               // K elements per register stage (64 code bytes)

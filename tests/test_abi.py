@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert syms == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(L, s), s
-    assert L.mi_abi_version() == 1
+    assert L.mi_abi_version() == 2
 
 
 def _err(status):
@@ -41,19 +41,19 @@ FAKE = 0x100000  # never dereferenced: validation fails before any launch
 
 def test_grouped_mm_validation():
     L = _lib.lib()
-    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, FAKE, 2, 100, FAKE, FAKE, _lib.MI_BF16, NULL))
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, _lib.MI_BF16, FAKE, 2, 100, FAKE, FAKE, _lib.MI_BF16, NULL))
     assert "n % 256" in msg
-    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 96, FAKE, 2, 256, FAKE, FAKE, _lib.MI_BF16, NULL))
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 96, _lib.MI_BF16, FAKE, 2, 256, FAKE, FAKE, _lib.MI_BF16, NULL))
     assert "k % 64" in msg
-    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, FAKE, 0, 256, FAKE, FAKE, _lib.MI_BF16, NULL))
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, _lib.MI_BF16, FAKE, 0, 256, FAKE, FAKE, _lib.MI_BF16, NULL))
     assert "batch_size" in msg
-    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, FAKE, 2, 256, NULL, FAKE, _lib.MI_BF16, NULL))
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, _lib.MI_BF16, FAKE, 2, 256, NULL, FAKE, _lib.MI_BF16, NULL))
     assert "m_indptr" in msg
-    with pytest.raises(NotImplementedError):
-        _lib.check(L.mi_grouped_mm_bf16(FAKE, 64, 64, FAKE, 2, 256, FAKE, FAKE, _lib.MI_F16,
-                                        NULL))
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, _lib.MI_F32, FAKE, 2, 256, FAKE, FAKE,
+                                    _lib.MI_BF16, NULL))
+    assert "bf16 or fp16" in msg
     # an empty a is a no-op that returns before touching the device
-    assert L.mi_grouped_mm_bf16(NULL, 0, 64, FAKE, 2, 256, FAKE, NULL, _lib.MI_BF16, NULL) == 0
+    assert L.mi_grouped_mm_bf16(NULL, 0, 64, _lib.MI_BF16, FAKE, 2, 256, FAKE, NULL, _lib.MI_BF16, NULL) == 0
 
 
 def _nv(**kw):

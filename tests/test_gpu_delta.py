@@ -174,3 +174,13 @@ def test_token_routed_twice_to_one_expert(gpu):
     assert np.array_equal(bits16(out), f64_to_bf16_bits(ref))
     out2 = run_gpu(case, tb)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_fp16_output_integer_probe_bitwise(gpu):
+    """out_dtype fp16 (the delta is added to an fp16 MoE output): the exact
+    value rounded once to fp16."""
+    from oracle.formats import f64_to_f16_bits
+    case = to_dev(synth.delta_int_probe(seed=113, r=16, I=64, H=256), gpu)
+    tb = tables(case, scattered=True)
+    out = run_gpu(case, tb, torch.float16)
+    assert np.array_equal(bits16(out), f64_to_f16_bits(run_oracle(case, tb)))

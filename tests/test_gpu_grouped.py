@@ -116,3 +116,41 @@ def test_deterministic(gpu):
     o1 = _run(case, gpu)
     o2 = _run(case, gpu)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("counts,n,k", [
+    ((0, 1, 17, 128, 0, 255), 256, 128),          # small groups: 64x64 tiles
+    ((300, 0, 513, 1, 256, 0, 390), 256, 256),    # large: 256x256 tiles
+])
+def test_fp16_inputs_integer_probe_bitwise_every_output(gpu, counts, n, k):
+    """fp16 a and b (the page's other input type) with bf16, fp16 and fp32
+    outputs; small-integer operands make every fp32 sum exact, so each output
+    is the oracle's exact value rounded once."""
+    from oracle.formats import f64_to_f16_bits
+    case = synth.grouped_int_probe(seed=111, counts=counts, n=n, k=k)
+    a16, b16 = case.a.float().half(), case.b.float().half()
+    mi = case.m_indptr
+    ref, written = grouped_mm(bits16(a16), bits16(b16), mi.numpy(), "f16")
+    for out_dtype, enc in ((torch.float16, f64_to_f16_bits), (torch.bfloat16, f64_to_bf16_bits)):
+        out = grouped_mm_bf16(a16.to(gpu), b16.to(gpu), mi.to(gpu), out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits16(out)[written], enc(ref[written])), out_dtype
+    out = grouped_mm_bf16(a16.to(gpu), b16.to(gpu), mi.to(gpu), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(out)[written], ref[written])
+
+
+def test_fp16_random_ragged_fp16_out(gpu):
+    g = np.random.default_rng(17)
+    for avg in (40, 400):
+        E = 7
+        counts = g.integers(0, 2 * avg, E)
+        mi = torch.zeros(E + 1, dtype=torch.int32)
+        mi[1:] = torch.from_numpy(np.cumsum(counts)).to(torch.int32)
+        gg = synth.gen(int(avg) + 5)
+        a = synth.bf16_normal((int(mi[-1]), 256), 1.0, gg).float().half()
+        b = synth.bf16_normal((E, 512, 256), 256 ** -0.5, gg).float().half()
+        ref, written = grouped_mm(bits16(a), bits16(b), mi.numpy(), "f16")
+        out = grouped_mm_bf16(a.to(gpu), b.to(gpu), mi.to(gpu), out_dtype=torch.float16)
+        torch.cuda.synchronize()
+        check_close(to_f64(out)[written], ref[written], f"fp16 ragged avg={avg}")
