@@ -239,6 +239,13 @@ class DeltaCase:
     def H(self):
         return self.B.shape[2]
 
+    def cast(self, dtype: torch.dtype) -> "DeltaCase":
+        """The same case with the activation and both banks stored as
+        ``dtype`` (torch's conversion; exact for the small-integer probes)."""
+        return DeltaCase(f"{self.name} {str(dtype).replace('torch.', '')}", self.act.to(dtype),
+                         self.perm, self.A.to(dtype), self.B.to(dtype), self.topk_ids,
+                         self.topk_weights, self.lora_ids, self.scale, dict(self.extra))
+
 
 def delta_tiny(seed: int = 1) -> DeltaCase:
     """Tiny MoE FC2 with LoRA delta: E=4, T=16, top_k=2, I=128, H=256,

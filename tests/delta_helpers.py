@@ -40,5 +40,8 @@ def scattered_bank(bank: torch.Tensor, seed: int, pad: int = 40):
     return flat, w_ptr, stride
 
 
+ORACLE_DTYPE = {torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
 def oracle_bank(t: torch.Tensor) -> Bank:
-    return Bank(bits16(t.reshape(-1)), t.data_ptr())
+    return Bank(bits16(t.reshape(-1)), t.data_ptr(), ORACLE_DTYPE[t.dtype])

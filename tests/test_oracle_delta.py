@@ -3,12 +3,13 @@ probe, invariants, a two-GEMM special case and the pointer semantics."""
 from fractions import Fraction
 
 import numpy as np
+import pytest
 import torch
 
 import synth
 from oracle import formats as F
 from oracle.lora_delta import moe_fc2_lora_delta
-from tests.delta_helpers import contiguous_tables, oracle_bank, scattered_bank
+from tests.delta_helpers import ORACLE_DTYPE, contiguous_tables, oracle_bank, scattered_bank
 from tests.parity import bits16
 
 
@@ -27,14 +28,23 @@ def run_oracle(case, A=None, B=None, tables=None, **over):
     kw.update(over)
     return moe_fc2_lora_delta(bits16(case.act), kw["perm"], ba, wa.numpy(), sa, bb, wb.numpy(),
                               sb, kw["topk_ids"], kw["topk_weights"], kw["lora_ids"],
-                              case.rank, case.H, kw["scale"])
+                              case.rank, case.H, kw["scale"],
+                              lora_dtype=ORACLE_DTYPE[case.act.dtype])
+
+
+def decode(t: torch.Tensor) -> np.ndarray:
+    """float64 values of a bf16 tensor (oracle decoder) or an fp16 tensor
+    (numpy's own IEEE half decoder, independent of the oracle's)."""
+    if t.dtype == torch.float16:
+        return bits16(t).view(np.float16).astype(np.float64)
+    return F.bf16_to_f64(bits16(t))
 
 
 def literal_loops(case):
     """The formula with plain Python floats and explicit index loops."""
-    act = F.bf16_to_f64(bits16(case.act))
-    A = F.bf16_to_f64(bits16(case.A))
-    B = F.bf16_to_f64(bits16(case.B))
+    act = decode(case.act)
+    A = decode(case.A)
+    B = decode(case.B)
     T, k = case.topk_ids.shape
     out = [[0.0] * case.H for _ in range(T)]
     for t in range(T):
@@ -73,8 +83,30 @@ def test_literal_loops():
     assert not ours[1].any()          # token 1 has no adapter
 
 
-def test_integer_probe_exact_with_fractions():
-    case = synth.delta_int_probe(T=8, top_k=3, E=4, I=16, H=8, L=3, r=4, pad_rows=5)
+def test_fp16_lora_dtype_literal_loops():
+    """lora_dtype fp16: activation and banks decode as IEEE half.  The case's
+    values are not all representable in bf16, so decoding them as bf16 fails."""
+    case = small_case(12).cast(torch.float16)
+    g = torch.Generator().manual_seed(3)
+    case.act += torch.randn(case.act.shape, generator=g).half() * 1e-3
+    assert not torch.equal(case.act.bfloat16().half(), case.act)
+    ours = run_oracle(case)
+    assert np.allclose(ours, literal_loops(case), rtol=1e-12, atol=1e-14)
+    # the same bits read as bf16 give other numbers (the pin can fail)
+    ba, bb = oracle_bank(case.A), oracle_bank(case.B)
+    ba.dtype = bb.dtype = "bf16"
+    (wa, sa), (wb, sb) = contiguous_tables(case.A), contiguous_tables(case.B)
+    wrong = moe_fc2_lora_delta(bits16(case.act), case.perm.numpy(), ba, wa.numpy(), sa, bb,
+                               wb.numpy(), sb, case.topk_ids.numpy(), case.topk_weights.numpy(),
+                               case.lora_ids.numpy(), case.rank, case.H, case.scale)
+    assert not np.allclose(wrong, ours)
+    with pytest.raises(AssertionError):  # banks and activation must agree on the dtype
+        run_oracle(case, tables=((ba, wa, sa), (oracle_bank(case.B), wb, sb)))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_integer_probe_exact_with_fractions(dtype):
+    case = synth.delta_int_probe(T=8, top_k=3, E=4, I=16, H=8, L=3, r=4, pad_rows=5).cast(dtype)
     ours = run_oracle(case)
     act = case.act.to(torch.int64).numpy()
     A = case.A.to(torch.int64).numpy()
