@@ -86,7 +86,9 @@ MI_API mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k,
  *     delta[t] = scale * sum_j w[t,j] * B_down[l,e] @ (A_down[l,e] @ act[perm[t*top_k+j]])
  * with e = topk_ids[t,j], w = topk_weights[t,j], l = lora_ids[t].
  *
- *   act          lora_dtype [padded_rows, inter_size]  permuted post-activation rows
+ *   act          lora_dtype [padded_rows, inter_size]  permuted post-activation rows;
+ *                lora_dtype (MI_BF16 or MI_F16, "bf16/fp16" in the parameter list) is
+ *                also the element type of both LoRA banks
  *   expanded_idx_to_permuted_idx  int32 [num_tokens * top_k]; < 0 = inactive slot
  *   w_ptr_a      int64 [num_experts]: byte address (16-byte aligned) of A_down[0,e], a [rank, inter_size]
  *                block; adapter l starts lora_stride_a ELEMENTS later
@@ -101,8 +103,10 @@ MI_API mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k,
  *                tokens without adapter or without an active slot)
  *   workspace    device scratch of at least mi_moe_fc2_lora_delta_workspace_size()
  *                bytes, 256-byte aligned; contents need no initialisation
- * The intermediate A_down @ act stays fp32; the result is rounded once.
- * Requirements: lora_dtype MI_BF16; out_dtype MI_BF16, MI_F16 or MI_F32; rank % 8 == 0,
+ * The intermediate A_down @ act is fp32 and reaches the second product with ~16
+ * (bf16) or ~22 (fp16, after a per-slot power-of-two scaling) significant bits;
+ * the result is rounded once.
+ * Requirements: lora_dtype MI_BF16 or MI_F16; out_dtype MI_BF16, MI_F16 or MI_F32; rank % 8 == 0,
  * 8 <= rank <= 128; inter_size % 8 == 0; hidden % 128 == 0; 1 <= top_k <= 32;
  * lora strides multiples of 8; num_experts <= 512.
  */

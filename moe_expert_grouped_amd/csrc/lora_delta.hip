@@ -23,6 +23,9 @@
 //             bf16(u) and lo = bf16(u - hi) (~16 significand bits together)
 //             in the fragment order the expand consumes: one contiguous 1 KiB
 //             record per block and 16 ranks; record i belongs to block i.
+//             With fp16 activations and weights (lora_dtype fp16) the MFMAs
+//             take fp16 and u, scaled per slot by a power of two, is carried
+//             as fp16 hi + lo (details at the kernel).
 //  4. expand  -- one workgroup per (tile, 128 output columns), in an order
 //             that keeps the tiles of one column chunk on one XCD (they share
 //             B columns through its L2).  An fp32 accumulator [TT tokens x 128
@@ -65,7 +68,8 @@ __device__ __forceinline__ void store_tile(Tile* t, const Tile& v) {
 }
 
 struct Layout {
-  size_t u2, tok_list, tiles, counters, blk_a, blk_b, blk_tl, blk_row, blk_w, tinfo, total;
+  size_t u2, tok_list, tiles, counters, blk_a, blk_b, blk_tl, blk_row, blk_w, blk_f, tinfo,
+      total;
   long cap;     // padded slot positions per tile
   int maxblk;   // 16-slot blocks per tile, at most
 };
@@ -114,6 +118,8 @@ Layout layout(int64_t T, int64_t top_k, int64_t E, int64_t L, int64_t rank) {
   ly.blk_row = off;  // activation row of each slot (a valid row when the slot is empty)
   off = al256(off + mt * ly.maxblk * 64);
   ly.blk_w = off;  // scale * w of each slot (0 when empty)
+  off = al256(off + mt * ly.maxblk * 64);
+  ly.blk_f = off;  // fp16 carrier: power-of-two factor that undoes each slot's u scaling
   off = al256(off + mt * ly.maxblk * 64);
   ly.blk_tl = off;  // token row (tile-local) of each of a block's 16 slots, 0xFF = empty
   off = al256(off + mt * ly.maxblk * 16);
@@ -416,9 +422,21 @@ struct ShrinkArgs {
   const float* blk_w;
   const int32_t* tinfo;
   uint16_t* u2;
+  float* blk_f;
   long cap;
   int I, L, rank, maxblk, bpt;  // bpt: workgroups per tile
 };
+
+// One 16x16x32 MFMA step of either input type (fp32 accumulation, exact products)
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 
 // The block's 16 activation rows and A_le are streamed with coalesced 16-byte
 // loads (two K stages in flight in registers) into a wave-private, swizzled
@@ -426,7 +444,14 @@ struct ShrinkArgs {
 // puts neighbouring lanes on different rows; loading it straight from memory
 // costs more address work per byte.)  Waves never synchronise with each
 // other, so a wave without a block just leaves.
-template <int NB>  // 1, 2, 4 or 8
+//
+// F16 (lora_dtype fp16): the MFMAs take fp16 and u is carried as fp16 hi + lo.
+// fp16 has a narrow exponent range, so each slot's u row is first multiplied
+// by 2^k, k chosen so that its largest magnitude lies in [2^14, 2^15); hi + lo
+// then keep ~22 significant bits of every rank relative to that maximum and
+// nothing overflows.  2^-k goes to blk_f and the expand multiplies it back
+// (both scalings by powers of two are exact).
+template <int NB, bool F16>  // NB: 1, 2, 4 or 8
 __global__ __launch_bounds__(64 * SHR_WAVES) void shrink_kernel(ShrinkArgs p) {
   static_assert(NB == 1 || NB == 2 || NB == 4 || NB == 8, "rank chunks");
   constexpr int KC = (128 / NB) < 32 ? 32 : 128 / NB;  // K elements per LDS stage
@@ -503,9 +528,7 @@ __global__ __launch_bounds__(64 * SHR_WAVES) void shrink_kernel(ShrinkArgs p) {
         const int rr = nb * 16 + row;
         const u32x4 fb =
             *reinterpret_cast<const u32x4*>(stB + rr * KC + ((c ^ (rr % CPR)) << 3));
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa),
-                                                          __builtin_bit_cast(bf16x8, fb), acc[nb],
-                                                          0, 0, 0);
+        acc[nb] = mfma16<F16>(fa, fb, acc[nb]);
       }
     }
     __builtin_amdgcn_wave_barrier();  // this stage's reads precede the next stage's writes
@@ -529,25 +552,49 @@ __global__ __launch_bounds__(64 * SHR_WAVES) void shrink_kernel(ShrinkArgs p) {
       const u32x4 fb = (kin && rr < p.rank)
                            ? gld<u32x4>(Ale + static_cast<long>(rr) * p.I + k0 + kq * 8)
                            : u32x4{0, 0, 0, 0};
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, fa), __builtin_bit_cast(bf16x8, fb), acc[nb], 0, 0, 0);
+      acc[nb] = mfma16<F16>(fa, fb, acc[nb]);
     }
   }
   // acc[nb][j] = (A_le @ act)[slot 4*kq + j][rank nb*16 + row]; empty slots have weight 0
   uint16_t* rec = p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32;
   const f32x4 wv = __builtin_bit_cast(f32x4, gld<u32x4>(p.blk_w + tb * 16 + 4 * kq));
+  f32x4 fac = f32x4{1.f, 1.f, 1.f, 1.f};  // F16: 2^-k of each of the lane group's 4 slots
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int srow = 4 * kq + j;
+    float v[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const float v = nb * 16 + row < p.rank ? acc[nb][j] * wv[j] : 0.f;
-      const uint32_t hi = f32_to_bf16_rne(v);
-      const uint32_t lo = f32_to_bf16_rne(v - bf16_bits_to_f32(hi));
-      gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), static_cast<uint16_t>(hi));
-      gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), static_cast<uint16_t>(lo));
+    for (int nb = 0; nb < NB; ++nb) v[nb] = nb * 16 + row < p.rank ? acc[nb][j] * wv[j] : 0.f;
+    if constexpr (F16) {
+      // slot maximum over the 16 lanes of this lane group (ranks row, row+16, ...)
+      float m = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) m = fmaxf(m, fabsf(v[nb]));
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, __shfl_xor(m, x));
+      // m in [2^(ex-1), 2^ex) -> m * 2^(15-ex) in [2^14, 2^15); the clamp keeps
+      // 2^-k a normal float (a slot that small stays scaled up by 2^112)
+      const int k = min(max(15 - __builtin_amdgcn_frexp_expf(m), -113), 112);
+      fac[j] = __builtin_amdgcn_ldexpf(1.f, -k);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float us = __builtin_amdgcn_ldexpf(v[nb], k);
+        const _Float16 hi = static_cast<_Float16>(us);
+        const _Float16 lo = static_cast<_Float16>(us - static_cast<float>(hi));
+        gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), __builtin_bit_cast(uint16_t, hi));
+        gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), __builtin_bit_cast(uint16_t, lo));
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t hi = f32_to_bf16_rne(v[nb]);
+        const uint32_t lo = f32_to_bf16_rne(v[nb] - bf16_bits_to_f32(hi));
+        gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), static_cast<uint16_t>(hi));
+        gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), static_cast<uint16_t>(lo));
+      }
     }
   }
+  if (F16 && row == 0) gst<f32x4>(p.blk_f + tb * 16 + 4 * kq, fac);
 }
 
 // ---------------------------------------------------------------------------
@@ -567,6 +614,7 @@ struct ExpandArgs {
   const uint16_t* u2;
   const int64_t* blk_b;
   const uint32_t* blk_tl;
+  const float* blk_f;
   const int32_t* tinfo;
   void* out;
   long cap;
@@ -586,6 +634,7 @@ struct Ring {  // operands of one 16-slot block, loaded D blocks ahead
   u32x4 fu[NB];  // u fragment: hi and lo of 4 ranks
   u32x2 fb[EXP_NCG][NB];  // B_le: the same 4 ranks of each of the wavefront's column groups
   uint32_t tw;   // the 4 token-row bytes around this lane's slot
+  float f;       // fp16 carrier: 2^-k of this lane's slot
 };
 
 // raw buffer resource (gfx9 layout: dword 3 = 0x00020000) over `bytes` bytes
@@ -614,10 +663,12 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
 // chunks are partly or wholly past the rank (those ranks are masked to zero in
 // B, which may hold anything there; u is zero there).
 // DUP: a block may hold a token twice, so accumulate with LDS atomics.
-template <int NB, bool PART, bool DUP>
+// F16: fp16 operands; each slot's products are multiplied by its 2^-k factor
+// (fused into the accumulation as one FMA).
+template <int NB, bool PART, bool DUP, bool F16>
 __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* const* s_bp,
-                                              const char* u2t, const char* tlt, int nblk,
-                                              int R, int H, int h0) {
+                                              const char* u2t, const char* tlt, const char* ft,
+                                              int nblk, int R, int H, int h0) {
   constexpr int D = NB == 1 ? 8 : (NB == 2 ? 4 : (NB == 4 ? 2 : 1));  // ring depth
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kq = lane >> 4;
@@ -646,6 +697,7 @@ __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* cons
   // per-lane offsets are constants, the block offset is a scalar.
   const __amdgpu_buffer_rsrc_t ursrc = buf_rsrc(u2t, static_cast<uint32_t>(nblk) * NB * 1024);
   const __amdgpu_buffer_rsrc_t trsrc = buf_rsrc(tlt, static_cast<uint32_t>(nblk) * 16);
+  const __amdgpu_buffer_rsrc_t frsrc = buf_rsrc(ft, F16 ? static_cast<uint32_t>(nblk) * 64 : 0);
   const uint32_t bbytes = static_cast<uint32_t>(H) * R * 2;  // one B_le
   auto bptr = [&](int i) { return s_bp[min(i, nblk - 1)]; };
   auto load = [&](Ring<NB>& r, int i, const uint16_t* bsrc) {
@@ -658,6 +710,7 @@ __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* cons
 #pragma unroll
       for (int c = 0; c < NB; ++c) r.fb[g][c] = buf_ld64(brsrc, boff[g][c], 0);  // 512 B rows
     r.tw = buf_ld32(trsrc, toff, ic * 16);
+    r.f = F16 ? __builtin_bit_cast(float, buf_ld32(frsrc, col * 4, ic * 64)) : 1.f;
   };
   auto mma = [&](const Ring<NB>& r, f32x4 (&acc)[EXP_NCG]) {
 #pragma unroll
@@ -670,9 +723,14 @@ __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* cons
         const u32x4 fb = u32x4{b4.x, b4.y, b4.x, b4.y};
         // K = 32 runs over (4 ranks, hi|lo) of every lane group q: [B | B]
         // (16 columns x 32) times [u_hi ; u_lo] (32 x 16 slots)
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb),
-                                                         __builtin_bit_cast(bf16x8, r.fu[c]),
-                                                         acc[g], 0, 0, 0);
+        if constexpr (F16)
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, fb),
+                                                          __builtin_bit_cast(f16x8, r.fu[c]),
+                                                          acc[g], 0, 0, 0);
+        else
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb),
+                                                           __builtin_bit_cast(bf16x8, r.fu[c]),
+                                                           acc[g], 0, 0, 0);
       }
     }
   };
@@ -695,6 +753,7 @@ __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* cons
   f32x4 acc[EXP_NCG];
   mma(ring[0], acc);
   int tl = row_of(ring[0], true);  // nblk > 0
+  float fs = ring[0].f;            // F16 only
   load(ring[0], D, bptr(D));
   for (int i0 = 0; i0 < nblk; i0 += D) {
     const uint16_t* bpr[D];
@@ -715,25 +774,31 @@ __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* cons
       f32x4 accn[EXP_NCG];
       mma(rn, accn);
       const int tln = row_of(rn, i + 1 < nblk);
+      const float fsn = rn.f;
       load(rn, i + 1 + D, bpr[d]);
 #pragma unroll
       for (int g = 0; g < EXP_NCG; ++g) {
         if (!DUP) {
-          *a[g] = v[g] + acc[g];
+          if (F16)
+            *a[g] = v[g] + acc[g] * fs;  // one FMA per element; the product is exact
+          else
+            *a[g] = v[g] + acc[g];
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) atomicAdd(reinterpret_cast<float*>(a[g]) + q, acc[g][q]);
+          for (int q = 0; q < 4; ++q)
+            atomicAdd(reinterpret_cast<float*>(a[g]) + q, F16 ? acc[g][q] * fs : acc[g][q]);
         }
       }
 #pragma unroll
       for (int g = 0; g < EXP_NCG; ++g) acc[g] = accn[g];
       tl = tln;
+      fs = fsn;
     }
   }
 }
 
 // 2 workgroups per CU (LDS) = 2 wavefronts per SIMD
-template <int NB, bool PART>
+template <int NB, bool PART, bool F16>
 __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
   __shared__ __attribute__((aligned(16))) float s_acc[(EXP_TT + 16) * EXP_CW];  // + spare rows
   __shared__ const uint16_t* s_bp[MAX_BLOCKS];  // B_le of each block
@@ -777,10 +842,11 @@ __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
   if (nblk > 0) {
     const char* u2t = reinterpret_cast<const char*>(p.u2 + static_cast<long>(ti) * p.cap * NB * 32);
     const char* tlt = reinterpret_cast<const char*>(p.blk_tl + static_cast<long>(ti) * p.maxblk * 4);
+    const char* ft = reinterpret_cast<const char*>(p.blk_f + static_cast<long>(ti) * p.maxblk * 16);
     if (dup)
-      expand_blocks<NB, PART, true>(s_acc, s_bp, u2t, tlt, nblk, p.rank, p.H, h0);
+      expand_blocks<NB, PART, true, F16>(s_acc, s_bp, u2t, tlt, ft, nblk, p.rank, p.H, h0);
     else
-      expand_blocks<NB, PART, false>(s_acc, s_bp, u2t, tlt, nblk, p.rank, p.H, h0);
+      expand_blocks<NB, PART, false, F16>(s_acc, s_bp, u2t, tlt, ft, nblk, p.rank, p.H, h0);
   }
   __syncthreads();
   // write out: 8 columns per thread-iteration
@@ -863,7 +929,8 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
              "elements (16-byte aligned adapter blocks)");
   MI_REQUIRE(padded_rows >= 0 && padded_rows < (1LL << 31),
              "bgmv_moe_gemm2_lora_delta: padded_rows out of range");
-  MI_REQUIRE_SUPPORTED(lora_dtype == MI_BF16, "bgmv_moe_gemm2_lora_delta: lora_dtype must be bf16");
+  MI_REQUIRE(lora_dtype == MI_BF16 || lora_dtype == MI_F16,
+             "bgmv_moe_gemm2_lora_delta: lora_dtype must be bf16 or fp16");
   MI_REQUIRE(out_dtype == MI_BF16 || out_dtype == MI_F32 || out_dtype == MI_F16,
              "bgmv_moe_gemm2_lora_delta: out_dtype must be bf16, fp16 or fp32");
   if (T == 0) return MI_OK;
@@ -893,6 +960,8 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   int64_t* blk_b = reinterpret_cast<int64_t*>(ws + ly.blk_b);
   int32_t* blk_row = reinterpret_cast<int32_t*>(ws + ly.blk_row);
   float* blk_w = reinterpret_cast<float*>(ws + ly.blk_w);
+  float* blk_f = reinterpret_cast<float*>(ws + ly.blk_f);
+  const bool f16 = lora_dtype == MI_F16;
   uint32_t* blk_tl = reinterpret_cast<uint32_t*>(ws + ly.blk_tl);
   int32_t* tinfo = reinterpret_cast<int32_t*>(ws + ly.tinfo);
   const int tt = tile_tokens(top_k);
@@ -918,21 +987,25 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
     const long swg = static_cast<long>(ntiles) * bpt;
     MI_REQUIRE(swg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
     ShrinkArgs sa{static_cast<const uint16_t*>(act), tiles, counters, blk_a, blk_row, blk_w, tinfo,
-                  u2, ly.cap, static_cast<int>(inter_size), static_cast<int>(L),
+                  u2, blk_f, ly.cap, static_cast<int>(inter_size), static_cast<int>(L),
                   static_cast<int>(rank), ly.maxblk, bpt};
     const dim3 sgrid(static_cast<unsigned>(swg)), sblock(64 * SHR_WAVES);
-    switch (nb) {
-      case 1: hipLaunchKernelGGL(shrink_kernel<1>, sgrid, sblock, 0, s, sa); break;
-      case 2: hipLaunchKernelGGL(shrink_kernel<2>, sgrid, sblock, 0, s, sa); break;
-      case 4: hipLaunchKernelGGL(shrink_kernel<4>, sgrid, sblock, 0, s, sa); break;
-      default: hipLaunchKernelGGL(shrink_kernel<8>, sgrid, sblock, 0, s, sa); break;
+    switch (nb * 2 + (f16 ? 1 : 0)) {
+      case 2: hipLaunchKernelGGL((shrink_kernel<1, false>), sgrid, sblock, 0, s, sa); break;
+      case 3: hipLaunchKernelGGL((shrink_kernel<1, true>), sgrid, sblock, 0, s, sa); break;
+      case 4: hipLaunchKernelGGL((shrink_kernel<2, false>), sgrid, sblock, 0, s, sa); break;
+      case 5: hipLaunchKernelGGL((shrink_kernel<2, true>), sgrid, sblock, 0, s, sa); break;
+      case 8: hipLaunchKernelGGL((shrink_kernel<4, false>), sgrid, sblock, 0, s, sa); break;
+      case 9: hipLaunchKernelGGL((shrink_kernel<4, true>), sgrid, sblock, 0, s, sa); break;
+      case 16: hipLaunchKernelGGL((shrink_kernel<8, false>), sgrid, sblock, 0, s, sa); break;
+      default: hipLaunchKernelGGL((shrink_kernel<8, true>), sgrid, sblock, 0, s, sa); break;
     }
     st = launch_status("bgmv_moe_gemm2_lora_delta (shrink)");
     if (st != MI_OK) return st;
   }
 
   const int nch = static_cast<int>(H / EXP_CW);
-  ExpandArgs ea{tok_list, tiles, counters, u2, blk_b, blk_tl, tinfo, out, ly.cap,
+  ExpandArgs ea{tok_list, tiles, counters, u2, blk_b, blk_tl, blk_f, tinfo, out, ly.cap,
                 static_cast<int>(L), static_cast<int>(H), static_cast<int>(rank), ly.maxblk,
                 ntiles, nch, out_dtype == MI_F32 ? 1 : (out_dtype == MI_F16 ? 2 : 0)};
   // whole runs of 8 tiles x nch chunks, rounded to a multiple of the 8 XCDs
@@ -940,15 +1013,21 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   MI_REQUIRE(ewg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
   const dim3 egrid(static_cast<unsigned>(ewg)), eblock(NT_EXP);
   const bool part = rank != 16 * nb;  // rank chunks past the rank are masked
-  switch (nb * 2 + (part ? 1 : 0)) {
-    case 2: hipLaunchKernelGGL((expand_kernel<1, false>), egrid, eblock, 0, s, ea); break;
-    case 3: hipLaunchKernelGGL((expand_kernel<1, true>), egrid, eblock, 0, s, ea); break;
-    case 4: hipLaunchKernelGGL((expand_kernel<2, false>), egrid, eblock, 0, s, ea); break;
-    case 5: hipLaunchKernelGGL((expand_kernel<2, true>), egrid, eblock, 0, s, ea); break;
-    case 8: hipLaunchKernelGGL((expand_kernel<4, false>), egrid, eblock, 0, s, ea); break;
-    case 9: hipLaunchKernelGGL((expand_kernel<4, true>), egrid, eblock, 0, s, ea); break;
-    case 16: hipLaunchKernelGGL((expand_kernel<8, false>), egrid, eblock, 0, s, ea); break;
-    default: hipLaunchKernelGGL((expand_kernel<8, true>), egrid, eblock, 0, s, ea); break;
+  switch (nb * 4 + (part ? 2 : 0) + (f16 ? 1 : 0)) {
+#define MI_EXPAND_CASE(NB_, PART_, F16_)                                                 \
+  case NB_ * 4 + (PART_ ? 2 : 0) + (F16_ ? 1 : 0):                                        \
+    hipLaunchKernelGGL((expand_kernel<NB_, PART_, F16_>), egrid, eblock, 0, s, ea); break;
+    MI_EXPAND_CASE(1, false, false) MI_EXPAND_CASE(1, false, true)
+    MI_EXPAND_CASE(1, true, false) MI_EXPAND_CASE(1, true, true)
+    MI_EXPAND_CASE(2, false, false) MI_EXPAND_CASE(2, false, true)
+    MI_EXPAND_CASE(2, true, false) MI_EXPAND_CASE(2, true, true)
+    MI_EXPAND_CASE(4, false, false) MI_EXPAND_CASE(4, false, true)
+    MI_EXPAND_CASE(4, true, false) MI_EXPAND_CASE(4, true, true)
+    MI_EXPAND_CASE(8, false, false) MI_EXPAND_CASE(8, false, true)
+    MI_EXPAND_CASE(8, true, false) MI_EXPAND_CASE(8, true, true)
+#undef MI_EXPAND_CASE
+    default: MI_REQUIRE(false, "bgmv_moe_gemm2_lora_delta: no expand variant (rank %lld)",
+                        (long long)rank);
   }
   return launch_status("bgmv_moe_gemm2_lora_delta (expand)");
 }

@@ -99,8 +99,7 @@ def test_delta_validation():
     assert "strides" in _err(_delta(sa=1001))
     with pytest.raises(NotImplementedError):
         _lib.check(_delta(H=200))
-    with pytest.raises(NotImplementedError):
-        _lib.check(_delta(ldt=_lib.MI_F16))
+    assert "lora_dtype must be bf16 or fp16" in _err(_delta(ldt=_lib.MI_F32))
     L = _lib.lib()
     assert L.mi_moe_fc2_lora_delta_workspace_size(8192, 8, 64, 8, 16) > 8192 * 8 * 16 * 4
     assert L.mi_moe_fc2_lora_delta_workspace_size(8, 0, 4, 2, 8) == 0

@@ -7,7 +7,7 @@ import synth
 from moe_expert_grouped_amd import bgmv_moe_gemm2_lora_delta
 from oracle.formats import f64_to_bf16_bits
 from oracle.lora_delta import moe_fc2_lora_delta
-from tests.delta_helpers import contiguous_tables, oracle_bank, scattered_bank
+from tests.delta_helpers import ORACLE_DTYPE, contiguous_tables, oracle_bank, scattered_bank
 from tests.parity import bits16, check_close, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -38,8 +38,8 @@ def run_gpu(case, tb, out_dtype=torch.bfloat16, **over):
     dev = case.act.device
     out = bgmv_moe_gemm2_lora_delta(case.act, kw["perm"], wa.to(dev), sa, wb.to(dev), sb,
                                     kw["topk_ids"], kw["topk_weights"], kw["lora_ids"], case.rank,
-                                    case.H, num_adapters=case.L, scale=kw["scale"],
-                                    out_dtype=out_dtype)
+                                    case.H, num_adapters=case.L, lora_dtype=case.act.dtype,
+                                    scale=kw["scale"], out_dtype=out_dtype)
     torch.cuda.synchronize()
     return out
 
@@ -52,7 +52,8 @@ def run_oracle(case, tb, tokens=None, **over):
     c = lambda t: t.detach().cpu().numpy()
     return moe_fc2_lora_delta(bits16(case.act), c(kw["perm"]), oracle_bank(fa), c(wa), sa,
                               oracle_bank(fb), c(wb), sb, c(kw["topk_ids"]), c(kw["topk_weights"]),
-                              c(kw["lora_ids"]), case.rank, case.H, kw["scale"], tokens=tokens)
+                              c(kw["lora_ids"]), case.rank, case.H, kw["scale"], tokens=tokens,
+                              lora_dtype=ORACLE_DTYPE[case.act.dtype])
 
 
 def test_tiny(gpu):
@@ -122,10 +123,11 @@ def test_medium_random(gpu):
 
 
 @pytest.mark.slow
-def test_at_scale_sampled(gpu):
+@pytest.mark.parametrize("lora_dtype", [torch.bfloat16, torch.float16])
+def test_at_scale_sampled(gpu, lora_dtype):
     """T=8192, top_k=8, E=64, I=2048, H=4096, 8 adapters of rank 16 (the
     bench's launch), checked on sampled tokens (all columns)."""
-    case = synth.delta_at_scale(device=gpu)
+    case = synth.delta_at_scale(device=gpu).cast(lora_dtype)
     tb = tables(case)
     out = run_gpu(case, tb)
     rng = np.random.default_rng(2)
@@ -137,11 +139,12 @@ def test_at_scale_sampled(gpu):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
-def test_workspace_contents_do_not_matter(gpu):
+@pytest.mark.parametrize("lora_dtype", [torch.bfloat16, torch.float16])
+def test_workspace_contents_do_not_matter(gpu, lora_dtype):
     """Every workspace byte the kernels read is written earlier in the same
     call: a workspace full of garbage gives the same bits as a zeroed one."""
     from moe_expert_grouped_amd import delta_workspace_bytes
-    case = to_dev(synth.delta_int_probe(seed=107, r=24, I=128, H=256), gpu)
+    case = to_dev(synth.delta_int_probe(seed=107, r=24, I=128, H=256).cast(lora_dtype), gpu)
     tb = tables(case, scattered=True)
     fa, wa, sa, fb, wb, sb = tb
     nbytes = delta_workspace_bytes(case.T, case.topk_ids.shape[1], case.A.shape[1], case.L,
@@ -152,14 +155,16 @@ def test_workspace_contents_do_not_matter(gpu):
         outs.append(bgmv_moe_gemm2_lora_delta(case.act, case.perm, wa.to(gpu), sa, wb.to(gpu), sb,
                                               case.topk_ids, case.topk_weights, case.lora_ids,
                                               case.rank, case.H, num_adapters=case.L,
-                                              scale=case.scale, workspace=ws))
+                                              lora_dtype=lora_dtype, scale=case.scale,
+                                              workspace=ws))
     torch.cuda.synchronize()
     ref = run_oracle(case, tb)
     for o in outs:
         assert np.array_equal(bits16(o), f64_to_bf16_bits(ref))
 
 
-def test_token_routed_twice_to_one_expert(gpu):
+@pytest.mark.parametrize("lora_dtype", [torch.bfloat16, torch.float16])
+def test_token_routed_twice_to_one_expert(gpu, lora_dtype):
     """Routing that repeats an expert for a token: both slots count (the
     formula sums over j); such tiles accumulate with LDS atomics."""
     case = synth.delta_int_probe(seed=109, T=40, top_k=4, E=6, I=64, H=256, L=2, r=16)
@@ -167,7 +172,8 @@ def test_token_routed_twice_to_one_expert(gpu):
     ids[::3, 1] = ids[::3, 0]      # every third token: slot 1 repeats slot 0's expert
     ids[5, 2] = ids[5, 3] = ids[5, 0]
     case = to_dev(synth.DeltaCase(case.name, case.act, case.perm, case.A, case.B, ids,
-                                  case.topk_weights, case.lora_ids, case.scale, case.extra), gpu)
+                                  case.topk_weights, case.lora_ids, case.scale,
+                                  case.extra).cast(lora_dtype), gpu)
     tb = tables(case, scattered=True)
     out = run_gpu(case, tb)
     ref = run_oracle(case, tb)
@@ -184,3 +190,49 @@ def test_fp16_output_integer_probe_bitwise(gpu):
     tb = tables(case, scattered=True)
     out = run_gpu(case, tb, torch.float16)
     assert np.array_equal(bits16(out), f64_to_f16_bits(run_oracle(case, tb)))
+
+
+# ---------------------------------------------------------------------------
+# lora_dtype fp16
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("r,I,H", [(16, 64, 256), (8, 200, 128), (40, 64, 256), (48, 72, 128),
+                                   (64, 128, 256), (128, 64, 128)])
+def test_fp16_lora_integer_probe_bitwise(gpu, r, I, H):
+    """Activation and banks in fp16: every intermediate of the integer probe
+    is exact, so each output type is the exact value rounded once."""
+    from oracle.formats import f64_to_f16_bits
+    case = to_dev(synth.delta_int_probe(seed=115, r=r, I=I, H=H).cast(torch.float16), gpu)
+    tb = tables(case, scattered=True)
+    ref = run_oracle(case, tb)
+    assert np.array_equal(bits16(run_gpu(case, tb)), f64_to_bf16_bits(ref))
+    assert np.array_equal(bits16(run_gpu(case, tb, torch.float16)), f64_to_f16_bits(ref))
+    assert np.array_equal(to_f64(run_gpu(case, tb, torch.float32)), ref)
+
+
+def test_fp16_lora_medium_random(gpu):
+    case = to_dev(synth.delta_at_scale(seed=9, T=512, top_k=4, E=12, I=256, H=512,
+                                       L=3).cast(torch.float16), gpu)
+    tb = tables(case)
+    check_close(to_f64(run_gpu(case, tb)), run_oracle(case, tb), "medium delta fp16")
+
+
+@pytest.mark.parametrize("act_mul,a_mul", [(2.0 ** 10, 2.0 ** 7), (2.0 ** -7, 2.0 ** -8)])
+def test_fp16_lora_far_from_one(gpu, act_mul, a_mul):
+    """A @ act far from fp16's range: up to ~1.8e5 (past its largest finite
+    value, 65504) or with a median of ~6.5e-6 (below its smallest normal,
+    6.1e-5).  The per-slot power-of-two scaling keeps ~22 significant bits,
+    so the fp32 output is within 1e-5 of the largest |delta|; fp16 hi + lo
+    without it would overflow or lose the low part."""
+    base = synth.delta_at_scale(seed=21, T=256, top_k=4, E=8, I=256, H=256, L=2)
+    case = synth.DeltaCase(base.name, (base.act.float() * act_mul).half(), base.perm,
+                           (base.A.float() * a_mul).half(), base.B.half(), base.topk_ids,
+                           base.topk_weights, base.lora_ids, base.scale)
+    case = to_dev(case, gpu)
+    tb = tables(case)
+    ref = run_oracle(case, tb)
+    out = to_f64(run_gpu(case, tb, torch.float32))
+    assert np.all(np.isfinite(out))
+    err = np.abs(out - ref).max()
+    assert err <= 1e-5 * np.abs(ref).max(), (err, np.abs(ref).max())
+    check_close(to_f64(run_gpu(case, tb)), ref, "fp16 delta far from one")
