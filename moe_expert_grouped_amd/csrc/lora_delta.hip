@@ -627,8 +627,6 @@ __device__ __forceinline__ int acc_chunk(int tl, int c) {
   return tl * (EXP_CW / 4) + (c ^ (tl & 31));
 }
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 template <int NB>
 struct Ring {  // operands of one 16-slot block, loaded D blocks ahead
   u32x4 fu[NB];  // u fragment: hi and lo of 4 ranks
@@ -636,21 +634,6 @@ struct Ring {  // operands of one 16-slot block, loaded D blocks ahead
   uint32_t tw;   // the 4 token-row bytes around this lane's slot
   float f;       // fp16 carrier: 2^-k of this lane's slot
 };
-
-// raw buffer resource (gfx9 layout: dword 3 = 0x00020000) over `bytes` bytes
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ u32x2 buf_ld64(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
-__device__ __forceinline__ uint32_t buf_ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                             uint32_t soff) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
 
 __device__ __forceinline__ const char* uniform_ptr(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);

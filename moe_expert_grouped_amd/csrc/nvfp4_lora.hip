@@ -96,17 +96,6 @@ struct NvArgs {
   int mode;  // 0 off, 1 raw, 2 prepared
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t nv_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 nv_ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ uint32_t nv_ld32(__amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                            uint32_t soff) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-
 // One register stage of a wavefront: for each of its 4 A and 4 B fragment
 // rows, this lane's 64 codes (32 bytes) and their 4 scale bytes.
 struct NvStage {
@@ -146,12 +135,12 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
   const int r32 = lane & 31, h = lane >> 5;
   const uint32_t kb = static_cast<uint32_t>(p.k) / 2;  // code bytes per row
   const int nct = (p.k / 16 + 3) / 4;                   // 128x4 scale tiles along K
-  const __amdgpu_buffer_rsrc_t ra = nv_rsrc(p.a, static_cast<uint32_t>(p.m) * kb);
-  const __amdgpu_buffer_rsrc_t rb = nv_rsrc(p.b, static_cast<uint32_t>(p.n) * kb);
+  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(p.a, static_cast<uint32_t>(p.m) * kb);
+  const __amdgpu_buffer_rsrc_t rb = buf_rsrc(p.b, static_cast<uint32_t>(p.n) * kb);
   const __amdgpu_buffer_rsrc_t rsa =
-      nv_rsrc(p.a_sf, static_cast<uint32_t>((p.m + 127) / 128) * nct * 512);
+      buf_rsrc(p.a_sf, static_cast<uint32_t>((p.m + 127) / 128) * nct * 512);
   const __amdgpu_buffer_rsrc_t rsb =
-      nv_rsrc(p.b_sf, static_cast<uint32_t>((p.n + 127) / 128) * nct * 512);
+      buf_rsrc(p.b_sf, static_cast<uint32_t>((p.n + 127) / 128) * nct * 512);
   uint32_t oa[FM], ob[FN], osa[FM], osb[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -180,15 +169,15 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
     const uint32_t so = static_cast<uint32_t>(kc) * 1024;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      st.a[i][0] = nv_ld128(ra, oa[i], co);
-      st.a[i][1] = nv_ld128(ra, oa[i] + 16, co);
-      st.sa[i] = nv_ld32(rsa, osa[i], so);
+      st.a[i][0] = buf_ld128(ra, oa[i], co);
+      st.a[i][1] = buf_ld128(ra, oa[i] + 16, co);
+      st.sa[i] = buf_ld32(rsa, osa[i], so);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      st.b[j][0] = nv_ld128(rb, ob[j], co);
-      st.b[j][1] = nv_ld128(rb, ob[j] + 16, co);
-      st.sb[j] = nv_ld32(rsb, osb[j], so);
+      st.b[j][0] = buf_ld128(rb, ob[j], co);
+      st.b[j][1] = buf_ld128(rb, ob[j] + 16, co);
+      st.sb[j] = buf_ld32(rsb, osb[j], so);
     }
   };
   auto compute = [&](const NvStage& st) {
