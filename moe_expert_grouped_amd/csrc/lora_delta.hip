@@ -26,6 +26,11 @@
 //             With fp16 activations and weights (lora_dtype fp16) the MFMAs
 //             take fp16 and u, scaled per slot by a power of two, is carried
 //             as fp16 hi + lo (details at the kernel).
+//             When A_le fits in LDS (rank <= 32, 16 * ceil(rank/16) * I <=
+//             32768, I % 128 == 0) the shrink runs per (adapter, expert)
+//             instead: A_le is read once into LDS and the workgroup's
+//             wavefronts take that pair's blocks from all of the adapter's
+//             tiles (same records, same summation order).
 //  4. expand  -- one workgroup per (tile, 128 output columns), in an order
 //             that keeps the tiles of one column chunk on one XCD (they share
 //             B columns through its L2).  An fp32 accumulator [TT tokens x 128
@@ -69,7 +74,7 @@ __device__ __forceinline__ void store_tile(Tile* t, const Tile& v) {
 
 struct Layout {
   size_t u2, tok_list, tiles, counters, blk_a, blk_b, blk_tl, blk_row, blk_w, blk_f, tinfo,
-      total;
+      btile, tex, total;
   long cap;     // padded slot positions per tile
   int maxblk;   // 16-slot blocks per tile, at most
 };
@@ -125,6 +130,10 @@ Layout layout(int64_t T, int64_t top_k, int64_t E, int64_t L, int64_t rank) {
   off = al256(off + mt * ly.maxblk * 16);
   ly.tinfo = off;  // per tile: number of blocks, "a token repeats an expert" flag
   off = al256(off + mt * 8);
+  ly.btile = off;  // first tile of each adapter bucket (L + 2 entries)
+  off = al256(off + static_cast<size_t>(L + 2) * 4);
+  ly.tex = off;    // per tile: first block of each expert (E + 1 entries)
+  off = al256(off + mt * static_cast<size_t>(E + 1) * 4);
   ly.total = off;
   return ly;
 }
@@ -138,6 +147,7 @@ struct PlanArgs {
   int32_t* tok_list;
   Tile* tiles;
   int32_t* counters;  // [0] = number of tiles
+  int32_t* btile;     // [b] = first tile of bucket b, b = 0 .. L+1
 };
 
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs p) {
@@ -183,6 +193,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(PlanArgs p) {
     }
   }
   __syncthreads();
+  for (int b = tid; b <= nb; b += PLAN_THREADS) gst<int>(p.btile + b, s_tile0[b]);
   for (int b = tid; b < nb; b += PLAN_THREADS) {
     const int c = s_cnt[b];
     for (int i = 0; i * p.tt < c; ++i)
@@ -330,6 +341,7 @@ struct ListArgs {
   int32_t* blk_row;   // per block: activation row of each slot (a valid row when empty)
   float* blk_w;       // per block: scale * w of each slot, 0 when empty
   int32_t* tinfo;     // per tile: number of blocks, "a token repeats an expert" flag
+  int32_t* tex;       // per tile: first block of each expert, E + 1 entries
   int L, maxblk;
   float scale;
 };
@@ -355,6 +367,8 @@ __global__ __launch_bounds__(NT_DELTA) void list_kernel(ListArgs p) {
   }
   list_slots(p.src, tile, SL);  // starts and ends with barriers
   const long tb = static_cast<long>(ti) * p.maxblk;
+  for (int e = threadIdx.x; e <= E; e += NT_DELTA)
+    gst<int>(p.tex + static_cast<long>(ti) * (E + 1) + e, SL.poff[e] >> 4);
 
   // per block: its A_le and B_le (one thread per expert, ~1 block each)
   for (int e = threadIdx.x; e < E; e += NT_DELTA) {
@@ -406,6 +420,55 @@ __global__ __launch_bounds__(NT_DELTA) void list_kernel(ListArgs p) {
 // which holds hi then lo of ranks 4q .. 4q+3 of the chunk (part 0 hi, 1 lo).
 __device__ __forceinline__ int u2_elem(int c, int part, int slot, int rr) {
   return c * 512 + ((rr >> 2) * 16 + slot) * 8 + part * 4 + (rr & 3);
+}
+
+// u of one block from the MFMA accumulators: acc[nb][j] = (A_le @ act)[slot
+// 4kq + j][rank 16nb + row].  Scales by scale*w (bw: the block's 16 weights,
+// 0 for empty slots), splits into hi + lo and writes the block's u record
+// (F16: per-slot power-of-two scaling first, factors to bf).
+template <int NB, bool F16>
+__device__ __forceinline__ void shrink_store(const f32x4 (&acc)[NB], uint16_t* rec, const float* bw,
+                                             float* bf, int rank) {
+  const int lane = threadIdx.x & 63, row = lane & 15, kq = lane >> 4;
+  // acc[nb][j] = (A_le @ act)[slot 4*kq + j][rank nb*16 + row]; empty slots have weight 0
+  const f32x4 wv = __builtin_bit_cast(f32x4, gld<u32x4>(bw + 4 * kq));
+  f32x4 fac = f32x4{1.f, 1.f, 1.f, 1.f};  // F16: 2^-k of each of the lane group's 4 slots
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int srow = 4 * kq + j;
+    float v[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) v[nb] = nb * 16 + row < rank ? acc[nb][j] * wv[j] : 0.f;
+    if constexpr (F16) {
+      // slot maximum over the 16 lanes of this lane group (ranks row, row+16, ...)
+      float m = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) m = fmaxf(m, fabsf(v[nb]));
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, __shfl_xor(m, x));
+      // m in [2^(ex-1), 2^ex) -> m * 2^(15-ex) in [2^14, 2^15); the clamp keeps
+      // 2^-k a normal float (a slot that small stays scaled up by 2^112)
+      const int k = min(max(15 - __builtin_amdgcn_frexp_expf(m), -113), 112);
+      fac[j] = __builtin_amdgcn_ldexpf(1.f, -k);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float us = __builtin_amdgcn_ldexpf(v[nb], k);
+        const _Float16 hi = static_cast<_Float16>(us);
+        const _Float16 lo = static_cast<_Float16>(us - static_cast<float>(hi));
+        gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), __builtin_bit_cast(uint16_t, hi));
+        gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), __builtin_bit_cast(uint16_t, lo));
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t hi = f32_to_bf16_rne(v[nb]);
+        const uint32_t lo = f32_to_bf16_rne(v[nb] - bf16_bits_to_f32(hi));
+        gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), static_cast<uint16_t>(hi));
+        gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), static_cast<uint16_t>(lo));
+      }
+    }
+  }
+  if (F16 && row == 0) gst<f32x4>(bf + 4 * kq, fac);
 }
 
 // ---------------------------------------------------------------------------
@@ -555,46 +618,134 @@ __global__ __launch_bounds__(64 * SHR_WAVES) void shrink_kernel(ShrinkArgs p) {
       acc[nb] = mfma16<F16>(fa, fb, acc[nb]);
     }
   }
-  // acc[nb][j] = (A_le @ act)[slot 4*kq + j][rank nb*16 + row]; empty slots have weight 0
-  uint16_t* rec = p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32;
-  const f32x4 wv = __builtin_bit_cast(f32x4, gld<u32x4>(p.blk_w + tb * 16 + 4 * kq));
-  f32x4 fac = f32x4{1.f, 1.f, 1.f, 1.f};  // F16: 2^-k of each of the lane group's 4 slots
+  shrink_store<NB, F16>(acc, p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32,
+                        p.blk_w + tb * 16, p.blk_f + tb * 16, p.rank);
+}
+
+// ---------------------------------------------------------------------------
+// 3b. shrink by (adapter, expert): A_le read once into LDS
+// ---------------------------------------------------------------------------
+// The tiles of adapter l are consecutive and list each expert's blocks
+// consecutively (tex), so the blocks that use one A_le are easy to enumerate.
+// One workgroup per (l, e, part) keeps A_le in LDS (16*NB rows; used when they
+// fit) and its 4 wavefronts take the blocks of (l, e) in the tiles
+// btile[l] + part, + S, ... in turn; each streams its block's 16 activation
+// rows through a wave-private stage as shrink_kernel does.  Per block this
+// reads A_le from LDS instead of from the caches, which the per-tile shrink
+// does once per block.
+constexpr int SLE_KC = 128;          // activation K elements per wave stage
+constexpr int SLE_AMAX = 16 * 2048;  // bf16 of A_le held in LDS: 16 * NB * I <= SLE_AMAX
+
+struct ShrinkLeArgs {
+  const uint16_t* act;
+  const int64_t* w_ptr_a;
+  long stride_a;
+  const int32_t* btile;
+  const int32_t* tex;
+  const int32_t* blk_row;
+  const float* blk_w;
+  uint16_t* u2;
+  float* blk_f;
+  long cap;
+  int I, E, L, rank, maxblk, S;
+};
+
+template <int NB, bool F16>  // NB: 1 or 2
+__global__ __launch_bounds__(256, 2) void shrink_le_kernel(ShrinkLeArgs p) {
+  constexpr int R16 = 16 * NB;       // A_le rows held (ranks past the rank repeat the last one)
+  constexpr int CPR = SLE_KC / 8;    // 16-byte chunks per stage row
+  constexpr int RPI = 64 / CPR;      // stage rows per coalesced load instruction
+  constexpr int NLA = 16 / RPI;      // activation loads per lane per stage
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[SLE_AMAX];
+  __shared__ __attribute__((aligned(16))) uint16_t s_act[4][16 * SLE_KC];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int le = blockIdx.x / p.S, part = blockIdx.x % p.S;
+  const int l = le / p.E, e = le % p.E;
+  if (l >= p.L) return;
+  const int t0 = gld<int>(p.btile + l) + part, t1 = gld<int>(p.btile + l + 1);
+  const int E1 = p.E + 1;
+  int nblk = 0;  // blocks of (l, e) in this part's tiles (the same in every lane)
+  for (int ti = t0; ti < t1; ti += p.S)
+    nblk += gld<int>(p.tex + static_cast<long>(ti) * E1 + e + 1) -
+            gld<int>(p.tex + static_cast<long>(ti) * E1 + e);
+  if (nblk == 0) return;
+
+  // A_le -> LDS: row r, 16-byte chunk c at chunk c ^ (r & 15) (I % 128 == 0)
+  const int cpr = p.I / 8;
+  const uint16_t* Ale =
+      reinterpret_cast<const uint16_t*>(gld<int64_t>(p.w_ptr_a + e) + 2 * p.stride_a * l);
+  for (int c = tid; c < R16 * cpr; c += 256) {
+    const int r = c / cpr, cc = c - r * cpr;
+    const u32x4 v = gld<u32x4>(Ale + static_cast<long>(min(r, p.rank - 1)) * p.I + cc * 8);
+    *reinterpret_cast<u32x4*>(s_a + r * p.I + ((cc ^ (r & 15)) << 3)) = v;
+  }
+  __syncthreads();
+
+  const int row = lane & 15, kq = lane >> 4;      // MFMA fragment roles
+  const int lrow = lane / CPR, lch = lane % CPR;  // coalesced-load roles
+  uint16_t* st = s_act[wave];
+  const int nst = p.I / SLE_KC;  // I % 128 == 0
+  int j = 0;
+  for (int ti = t0; ti < t1; ti += p.S) {
+    const int b0 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e);
+    const int b1 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e + 1);
+    for (int bi = b0; bi < b1; ++bi, ++j) {
+      if ((j & 3) != wave) continue;
+      const long tb = static_cast<long>(ti) * p.maxblk + bi;
+      const uint16_t* asrc[NLA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int srow = 4 * kq + j;
-    float v[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) v[nb] = nb * 16 + row < p.rank ? acc[nb][j] * wv[j] : 0.f;
-    if constexpr (F16) {
-      // slot maximum over the 16 lanes of this lane group (ranks row, row+16, ...)
-      float m = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) m = fmaxf(m, fabsf(v[nb]));
-#pragma unroll
-      for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, __shfl_xor(m, x));
-      // m in [2^(ex-1), 2^ex) -> m * 2^(15-ex) in [2^14, 2^15); the clamp keeps
-      // 2^-k a normal float (a slot that small stays scaled up by 2^112)
-      const int k = min(max(15 - __builtin_amdgcn_frexp_expf(m), -113), 112);
-      fac[j] = __builtin_amdgcn_ldexpf(1.f, -k);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float us = __builtin_amdgcn_ldexpf(v[nb], k);
-        const _Float16 hi = static_cast<_Float16>(us);
-        const _Float16 lo = static_cast<_Float16>(us - static_cast<float>(hi));
-        gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), __builtin_bit_cast(uint16_t, hi));
-        gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), __builtin_bit_cast(uint16_t, lo));
+      for (int jj = 0; jj < NLA; ++jj) {
+        const int r = jj * RPI + lrow;
+        asrc[jj] = p.act + static_cast<long>(gld<int>(p.blk_row + tb * 16 + r)) * p.I + lch * 8;
       }
-    } else {
+      f32x4 acc[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const uint32_t hi = f32_to_bf16_rne(v[nb]);
-        const uint32_t lo = f32_to_bf16_rne(v[nb] - bf16_bits_to_f32(hi));
-        gst<uint16_t>(rec + u2_elem(nb, 0, srow, row), static_cast<uint16_t>(hi));
-        gst<uint16_t>(rec + u2_elem(nb, 1, srow, row), static_cast<uint16_t>(lo));
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // three register stages in flight: stage s + 3 is loaded while s feeds the MFMAs
+      u32x4 ra0[NLA], ra1[NLA], ra2[NLA];
+      auto gload = [&](u32x4 (&ra)[NLA], int s) {
+        if (s < nst) {
+#pragma unroll
+          for (int jj = 0; jj < NLA; ++jj) ra[jj] = gld<u32x4>(asrc[jj] + s * SLE_KC);
+        }
+      };
+      auto consume = [&](u32x4 (&ra)[NLA], int s) {
+#pragma unroll
+        for (int jj = 0; jj < NLA; ++jj) {
+          const int r = jj * RPI + lrow;
+          *reinterpret_cast<u32x4*>(st + r * SLE_KC + ((lch ^ (r % CPR)) << 3)) = ra[jj];
+        }
+        __builtin_amdgcn_wave_barrier();
+        gload(ra, s + 3);
+#pragma unroll
+        for (int s2 = 0; s2 < SLE_KC / 32; ++s2) {
+          const int c = 4 * s2 + kq;
+          const u32x4 fa =
+              *reinterpret_cast<const u32x4*>(st + row * SLE_KC + ((c ^ (row % CPR)) << 3));
+          const int ca = s * CPR + c;  // chunk of A_le's row
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int rr = nb * 16 + row;
+            const u32x4 fb = *reinterpret_cast<const u32x4*>(s_a + rr * p.I + ((ca ^ (rr & 15)) << 3));
+            acc[nb] = mfma16<F16>(fa, fb, acc[nb]);
+          }
+        }
+        __builtin_amdgcn_wave_barrier();  // this stage's reads precede the next stage's writes
+      };
+      gload(ra0, 0);
+      gload(ra1, 1);
+      gload(ra2, 2);
+      for (int s = 0; s < nst; s += 3) {
+        consume(ra0, s);
+        if (s + 1 < nst) consume(ra1, s + 1);
+        if (s + 2 < nst) consume(ra2, s + 2);
       }
+      shrink_store<NB, F16>(acc, p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32,
+                            p.blk_w + tb * 16, p.blk_f + tb * 16, p.rank);
     }
   }
-  if (F16 && row == 0) gst<f32x4>(p.blk_f + tb * 16 + 4 * kq, fac);
 }
 
 // ---------------------------------------------------------------------------
@@ -950,7 +1101,10 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   const int tt = tile_tokens(top_k);
   const int ntiles = static_cast<int>(max_tiles(T, top_k, L));
 
-  PlanArgs pa{lora_ids, static_cast<int>(T), static_cast<int>(L), tt, tok_list, tiles, counters};
+  int32_t* btile = reinterpret_cast<int32_t*>(ws + ly.btile);
+  int32_t* tex = reinterpret_cast<int32_t*>(ws + ly.tex);
+  PlanArgs pa{lora_ids, static_cast<int>(T), static_cast<int>(L), tt, tok_list, tiles, counters,
+              btile};
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, pa);
   mi_status st = launch_status("bgmv_moe_gemm2_lora_delta (plan)");
   if (st != MI_OK) return st;
@@ -961,27 +1115,46 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   if (L > 0) {
     ListArgs la{src, tiles, counters, topk_weights, w_ptr_a, static_cast<long>(lora_stride_a),
                 w_ptr_b, static_cast<long>(lora_stride_b), blk_a, blk_b, blk_tl, blk_row, blk_w,
-                tinfo, static_cast<int>(L), ly.maxblk, scale};
+                tinfo, tex, static_cast<int>(L), ly.maxblk, scale};
     hipLaunchKernelGGL(list_kernel, dim3(ntiles), dim3(NT_DELTA), 0, s, la);
     st = launch_status("bgmv_moe_gemm2_lora_delta (list)");
     if (st != MI_OK) return st;
 
-    const int bpt = (ly.maxblk + SHR_WAVES - 1) / SHR_WAVES;  // shrink workgroups per tile
-    const long swg = static_cast<long>(ntiles) * bpt;
-    MI_REQUIRE(swg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
-    ShrinkArgs sa{static_cast<const uint16_t*>(act), tiles, counters, blk_a, blk_row, blk_w, tinfo,
-                  u2, blk_f, ly.cap, static_cast<int>(inter_size), static_cast<int>(L),
-                  static_cast<int>(rank), ly.maxblk, bpt};
-    const dim3 sgrid(static_cast<unsigned>(swg)), sblock(64 * SHR_WAVES);
-    switch (nb * 2 + (f16 ? 1 : 0)) {
-      case 2: hipLaunchKernelGGL((shrink_kernel<1, false>), sgrid, sblock, 0, s, sa); break;
-      case 3: hipLaunchKernelGGL((shrink_kernel<1, true>), sgrid, sblock, 0, s, sa); break;
-      case 4: hipLaunchKernelGGL((shrink_kernel<2, false>), sgrid, sblock, 0, s, sa); break;
-      case 5: hipLaunchKernelGGL((shrink_kernel<2, true>), sgrid, sblock, 0, s, sa); break;
-      case 8: hipLaunchKernelGGL((shrink_kernel<4, false>), sgrid, sblock, 0, s, sa); break;
-      case 9: hipLaunchKernelGGL((shrink_kernel<4, true>), sgrid, sblock, 0, s, sa); break;
-      case 16: hipLaunchKernelGGL((shrink_kernel<8, false>), sgrid, sblock, 0, s, sa); break;
-      default: hipLaunchKernelGGL((shrink_kernel<8, true>), sgrid, sblock, 0, s, sa); break;
+    // A_le held in LDS when it fits: one workgroup per (adapter, expert, part)
+    const bool by_le = nb <= 2 && 16 * nb * inter_size <= SLE_AMAX && inter_size % 128 == 0;
+    if (by_le) {
+      const long le = L * E;
+      const int S = le >= 2L * num_cus() ? 1 : 2;  // parts: the tiles of an adapter split S ways
+      MI_REQUIRE(le * S < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
+      ShrinkLeArgs sa{static_cast<const uint16_t*>(act), w_ptr_a, static_cast<long>(lora_stride_a),
+                      btile, tex, blk_row, blk_w, u2, blk_f, ly.cap,
+                      static_cast<int>(inter_size), static_cast<int>(E), static_cast<int>(L),
+                      static_cast<int>(rank), ly.maxblk, S};
+      const dim3 g(static_cast<unsigned>(le * S)), b(256);
+      switch (nb * 2 + (f16 ? 1 : 0)) {
+        case 2: hipLaunchKernelGGL((shrink_le_kernel<1, false>), g, b, 0, s, sa); break;
+        case 3: hipLaunchKernelGGL((shrink_le_kernel<1, true>), g, b, 0, s, sa); break;
+        case 4: hipLaunchKernelGGL((shrink_le_kernel<2, false>), g, b, 0, s, sa); break;
+        default: hipLaunchKernelGGL((shrink_le_kernel<2, true>), g, b, 0, s, sa); break;
+      }
+    } else {
+      const int bpt = (ly.maxblk + SHR_WAVES - 1) / SHR_WAVES;  // shrink workgroups per tile
+      const long swg = static_cast<long>(ntiles) * bpt;
+      MI_REQUIRE(swg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
+      ShrinkArgs sa{static_cast<const uint16_t*>(act), tiles, counters, blk_a, blk_row, blk_w, tinfo,
+                    u2, blk_f, ly.cap, static_cast<int>(inter_size), static_cast<int>(L),
+                    static_cast<int>(rank), ly.maxblk, bpt};
+      const dim3 sgrid(static_cast<unsigned>(swg)), sblock(64 * SHR_WAVES);
+      switch (nb * 2 + (f16 ? 1 : 0)) {
+        case 2: hipLaunchKernelGGL((shrink_kernel<1, false>), sgrid, sblock, 0, s, sa); break;
+        case 3: hipLaunchKernelGGL((shrink_kernel<1, true>), sgrid, sblock, 0, s, sa); break;
+        case 4: hipLaunchKernelGGL((shrink_kernel<2, false>), sgrid, sblock, 0, s, sa); break;
+        case 5: hipLaunchKernelGGL((shrink_kernel<2, true>), sgrid, sblock, 0, s, sa); break;
+        case 8: hipLaunchKernelGGL((shrink_kernel<4, false>), sgrid, sblock, 0, s, sa); break;
+        case 9: hipLaunchKernelGGL((shrink_kernel<4, true>), sgrid, sblock, 0, s, sa); break;
+        case 16: hipLaunchKernelGGL((shrink_kernel<8, false>), sgrid, sblock, 0, s, sa); break;
+        default: hipLaunchKernelGGL((shrink_kernel<8, true>), sgrid, sblock, 0, s, sa); break;
+      }
     }
     st = launch_status("bgmv_moe_gemm2_lora_delta (shrink)");
     if (st != MI_OK) return st;

@@ -66,7 +66,10 @@ def test_tiny(gpu):
 
 
 @pytest.mark.parametrize("r,I,H", [(16, 64, 256), (8, 200, 128), (32, 96, 384), (24, 128, 256),
-                                   (40, 64, 256), (48, 72, 128)])
+                                   (40, 64, 256), (48, 72, 128),
+                                   # A_le held in LDS (rank <= 32, I % 128 == 0): the
+                                   # shrink by (adapter, expert), up to its largest A_le
+                                   (16, 256, 256), (8, 384, 128), (32, 1024, 128)])
 def test_integer_probe_bitwise_scattered_bank(gpu, r, I, H):
     case = to_dev(synth.delta_int_probe(r=r, I=I, H=H), gpu)
     tb = tables(case, scattered=True)
@@ -164,10 +167,11 @@ def test_workspace_contents_do_not_matter(gpu, lora_dtype):
 
 
 @pytest.mark.parametrize("lora_dtype", [torch.bfloat16, torch.float16])
-def test_token_routed_twice_to_one_expert(gpu, lora_dtype):
+@pytest.mark.parametrize("I", [64, 128])
+def test_token_routed_twice_to_one_expert(gpu, lora_dtype, I):
     """Routing that repeats an expert for a token: both slots count (the
     formula sums over j); such tiles accumulate with LDS atomics."""
-    case = synth.delta_int_probe(seed=109, T=40, top_k=4, E=6, I=64, H=256, L=2, r=16)
+    case = synth.delta_int_probe(seed=109, T=40, top_k=4, E=6, I=I, H=256, L=2, r=16)
     ids = case.topk_ids.clone()
     ids[::3, 1] = ids[::3, 0]      # every third token: slot 1 repeats slot 0's expert
     ids[5, 2] = ids[5, 3] = ids[5, 0]
