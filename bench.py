@@ -321,43 +321,42 @@ def cpu_baseline(g2, dc, nc, wa, wb, sa, sb):
             cores = min(cores, max(blas))
     except Exception:
         pass
-    flops = 0.0
-    t_total = 0.0
-    # grouped GEMM: the whole uniform workload
+    # inputs as the oracle takes them (host copies, outside the timing)
     a, b, mi_ = bits(g2.a), bits(g2.b), g2.m_indptr.cpu().numpy()
-    t = time.perf_counter()
-    grouped_mm(a, b, mi_)
-    t_total += time.perf_counter() - t
-    flops += 2.0 * g2.a.shape[0] * g2.a.shape[1] * g2.b.shape[1]
-    # LoRA delta: every token
     toks = list(range(dc.T))
     act = bits(dc.act)
     ba, bb = Bank(bits(dc.A.reshape(-1)), dc.A.data_ptr()), Bank(bits(dc.B.reshape(-1)),
                                                                  dc.B.data_ptr())
     perm = dc.perm.cpu().numpy()
     lids = dc.lora_ids.cpu().numpy()
-    t = time.perf_counter()
-    moe_fc2_lora_delta(act, perm, ba, wa.cpu().numpy(), sa, bb, wb.cpu().numpy(), sb,
-                       dc.topk_ids.cpu().numpy(), dc.topk_weights.cpu().numpy(), lids, dc.rank,
-                       dc.H, dc.scale, tokens=toks)
-    t_total += time.perf_counter() - t
+    wa_h, wb_h = wa.cpu().numpy(), wb.cpu().numpy()
+    ids_h, w_h = dc.topk_ids.cpu().numpy(), dc.topk_weights.cpu().numpy()
     pr = perm.reshape(dc.T, dc.top_k)
     n_act = int(((pr[toks] >= 0) & (lids[toks][:, None] >= 0)).sum())
-    flops += n_act * (2.0 * dc.rank * dc.I + 2.0 * dc.H * dc.rank)
-    # NVFP4 raw: the whole workload
     rows = np.arange(nc.M)
     a_c = nc.a.cpu().numpy()[rows]
     b_c, asf, bsf = nc.b.cpu().numpy(), nc.a_sf.cpu().numpy(), nc.b_sf.cpu().numpy()
-    t = time.perf_counter()
-    base = NV.base_product(a_c, b_c, asf, bsf, nc.K, rows, None)
-    NV.mm_nvfp4_raw(base, float(nc.alpha[0]), bits(nc.d)[rows], bits(nc.lora_b),
-                    float(nc.lora_scale[0]), bits(nc.bias))
-    t_total += time.perf_counter() - t
-    flops += 2.0 * len(rows) * nc.N * nc.K + 2.0 * len(rows) * nc.N * nc.rank
+    d_h, lb_h, bias_h = bits(nc.d)[rows], bits(nc.lora_b), bits(nc.bias)
+    pass_flops = (2.0 * g2.a.shape[0] * g2.a.shape[1] * g2.b.shape[1] +
+                  n_act * (2.0 * dc.rank * dc.I + 2.0 * dc.H * dc.rank) +
+                  2.0 * len(rows) * nc.N * nc.K + 2.0 * len(rows) * nc.N * nc.rank)
+    # whole passes over the three workloads until at least 10 s of oracle time
+    # (at most 4 passes)
+    flops, t_total, passes = 0.0, 0.0, 0
+    while passes < 4 and (passes == 0 or t_total < 10.0):
+        t = time.perf_counter()
+        grouped_mm(a, b, mi_)
+        moe_fc2_lora_delta(act, perm, ba, wa_h, sa, bb, wb_h, sb, ids_h, w_h, lids, dc.rank, dc.H,
+                           dc.scale, tokens=toks)
+        base = NV.base_product(a_c, b_c, asf, bsf, nc.K, rows, None)
+        NV.mm_nvfp4_raw(base, float(nc.alpha[0]), d_h, lb_h, float(nc.lora_scale[0]), bias_h)
+        t_total += time.perf_counter() - t
+        flops += pass_flops
+        passes += 1
     return {"value": round(flops / t_total / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(t_total, 2),
-            "sample": "whole grouped GEMM, LoRA delta and NVFP4 raw workloads (one pass each); "
-                      "flops / oracle time"}
+            "sample": f"{passes} pass(es) over the whole grouped GEMM, LoRA delta and NVFP4 raw "
+                      "workloads; flops / oracle time"}
 
 
 if __name__ == "__main__":
