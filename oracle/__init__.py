@@ -16,6 +16,8 @@ passage of the source pages it follows (cited by page title and section):
   parameters -> :mod:`oracle.nvfp4`
 - ``flashinfer.gemm.prepare_nvfp4_lora_adapter`` -- the fold recipe
   -> :mod:`oracle.fold`
+- MoE finalize with the delta added (``bgmv_moe_gemm2_lora_delta``,
+  description and return value) -> :mod:`oracle.finalize`
 
 Inputs are numpy arrays; bf16 tensors are passed as their uint16 bit patterns.
 
@@ -27,4 +29,4 @@ unpinned** by the pages: they follow the public OCP / block-scaling
 convention and are pinned only to that convention (two independent codings
 and hand-worked offsets).
 """
-from . import formats, grouped_mm, lora_delta, nvfp4, fold  # noqa: F401
+from . import formats, grouped_mm, lora_delta, nvfp4, fold, finalize  # noqa: F401
