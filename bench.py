@@ -265,6 +265,37 @@ def main():
                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "traffic": read_traffic()}
 
+    # Outside the step: the MoE finalize with the delta added (FC2 rows of the
+    # delta workload's routing, bf16 [padded_rows, H]), timed on its own.
+    extra = None
+    if not only or "finalize" in only:
+        fc2 = synth.bf16_normal((dc.act.shape[0], dc.H), 1.0, synth.gen(77, dev), dev)
+        fout = torch.empty((dc.T, dc.H), dtype=torch.bfloat16, device=dev)
+        fin = lambda: mi.moe_finalize_lora(fc2, dc.act, dc.perm, wa, sa, wb, sb, dc.topk_ids,
+                                           dc.topk_weights, dc.lora_ids, dc.rank, dc.H,
+                                           num_adapters=dc.L, scale=dc.scale, out=fout,
+                                           workspace=ws)
+        for _ in range(3):
+            fin()
+        fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a_, b_ in fe:
+            a_.record(stream)
+            fin()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        fms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in fe]))
+        n_routed = int((perm >= 0).sum())
+        fbytes = delta_bytes + 2.0 * dc.H * n_routed
+        fflops = delta_flops + 2.0 * dc.H * n_routed
+        extra = {"finalize_fused": {
+            "ms": round(fms, 5), "gbps": round(fbytes / fms / 1e6, 1),
+            "frac_hbm_peak": round(fbytes / fms / 1e6 / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes": fbytes, "algorithmic_flops": fflops,
+            "note": "MoE finalize (weighted combine of the routed FC2 rows) with the LoRA delta "
+                    "added, delta workload; not part of the step"}}
+
     cpu = None
     if not args.no_cpu_baseline and not only:
         cpu = cpu_baseline(g2, dc, nc, wa, wb, sa, sb)
@@ -296,6 +327,7 @@ def main():
             "parallelism": "single GPU",
         },
         "ops": op_report,
+        "extra_ops": extra,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

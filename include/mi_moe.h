@@ -6,6 +6,9 @@
  *                             (flashinfer.grouped_mm.grouped_mm_bf16, formula)
  *   - mi_moe_fc2_lora_delta   FC2 LoRA delta of a routed MoE
  *                             (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta, formula)
+ *   - mi_moe_fc2_finalize_lora  the MoE finalize (routing-weighted combine of the FC2
+ *                             rows) with that delta added, in one pass
+ *                             (bgmv_moe_gemm2_lora_delta, description and return value)
  *   - mi_mm_nvfp4_lora        NVFP4 GEMM with an fp32 LoRA epilogue, raw and prepared
  *                             (flashinfer.gemm.mm_nvfp4_lora, formula and the two bullets)
  *   - mi_prepare_lora_fold    the prepared-path fold
@@ -124,6 +127,36 @@ MI_API mi_status mi_moe_fc2_lora_delta(const void* act, int64_t padded_rows, int
                                 mi_dtype lora_dtype, float scale, mi_dtype out_dtype,
                                 void* out, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/*
+ * MoE finalize with the FC2 LoRA delta added (flashinfer.fused_moe.
+ * bgmv_moe_gemm2_lora_delta, description and return value: the delta is
+ * combined over the experts and added to the MoE output after the combine):
+ *     out[t] = sum_j w[t,j] * fc2[perm[t*top_k+j]] + delta[t]
+ * with delta[t] exactly as mi_moe_fc2_lora_delta defines it.  The sum is
+ * formed in fp32 (delta first, then the slots in order) and rounded once to
+ * out_dtype; the delta is never rounded on its own.
+ *   fc2          fc2_dtype [padded_rows, hidden_size]: the FC2 grouped-GEMM output in
+ *                permuted row order (MI_BF16, MI_F16 or MI_F32), 16-byte aligned
+ *   perm, topk_weights: as for the delta; a slot whose permuted row is < 0 or
+ *                >= padded_rows is not routed here and contributes nothing (to the
+ *                combine and to the delta); every other slot's row is combined with
+ *                its weight, whatever its expert id
+ *   everything else, the workspace (same size) and the validation: as for
+ *   mi_moe_fc2_lora_delta (its messages name that operation).  Tokens without an
+ *   adapter get the combine alone.  num_adapters == 0 gives the plain combine.
+ */
+MI_API mi_status mi_moe_fc2_finalize_lora(const void* fc2, mi_dtype fc2_dtype, const void* act,
+                                   int64_t padded_rows, int64_t inter_size,
+                                   const int32_t* expanded_idx_to_permuted_idx,
+                                   const int64_t* w_ptr_a, int64_t lora_stride_a,
+                                   const int64_t* w_ptr_b, int64_t lora_stride_b,
+                                   const int32_t* topk_ids, const float* topk_weights,
+                                   const int32_t* lora_ids, int64_t num_tokens, int64_t top_k,
+                                   int64_t num_experts, int64_t num_adapters, int64_t rank,
+                                   int64_t hidden_size, mi_dtype lora_dtype, float scale,
+                                   mi_dtype out_dtype, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * NVFP4 GEMM with a BF16 LoRA correction (flashinfer.gemm.mm_nvfp4_lora):

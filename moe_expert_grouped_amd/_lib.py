@@ -20,6 +20,7 @@ EXPORTS = [
     "mi_grouped_mm_bf16",
     "mi_moe_fc2_lora_delta_workspace_size",
     "mi_moe_fc2_lora_delta",
+    "mi_moe_fc2_finalize_lora",
     "mi_mm_nvfp4_lora",
     "mi_prepare_lora_fold",
     "mi_nvfp4_dequant_bf16",
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
             I64, I64, I64, I64, I64, I64,  # T, top_k, E, L, rank, H
             I32, F32, I32,        # lora_dtype, scale, out_dtype
             P, P, SZ, P]          # out, workspace, bytes, stream
+        L.mi_moe_fc2_finalize_lora.restype = I32
+        L.mi_moe_fc2_finalize_lora.argtypes = [
+            P, I32,               # fc2, fc2_dtype
+            *L.mi_moe_fc2_lora_delta.argtypes]
         L.mi_mm_nvfp4_lora.restype = I32
         L.mi_mm_nvfp4_lora.argtypes = [P, P, P, SZ, P, SZ, P, I64, I64, I64, P, I64, P, P, P, P,
                                        P, P, P]

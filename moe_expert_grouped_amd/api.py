@@ -21,6 +21,7 @@ from ._lib import MI_BF16, MI_F16, MI_F32, check
 __all__ = [
     "grouped_mm_bf16",
     "bgmv_moe_gemm2_lora_delta",
+    "moe_finalize_lora",
     "delta_workspace_bytes",
     "fill_w_ptr",
     "mm_nvfp4_lora",
@@ -123,8 +124,38 @@ def bgmv_moe_gemm2_lora_delta(gemm1_activation_output: torch.Tensor,
     ``num_adapters`` is the number of adapters in the banks (ids at or above
     it are treated as no adapter); the other arguments follow the page.
     """
-    act = gemm1_activation_output
-    perm = expanded_idx_to_permuted_idx
+    return _delta_call(None, gemm1_activation_output, expanded_idx_to_permuted_idx, w_ptr_a,
+                       lora_stride_a, w_ptr_b, lora_stride_b, topk_ids, topk_weights, lora_ids,
+                       rank, hidden_size, num_adapters, lora_dtype, scale, out_dtype, out,
+                       workspace)
+
+
+def moe_finalize_lora(fc2_out: torch.Tensor, gemm1_activation_output: torch.Tensor,
+                      expanded_idx_to_permuted_idx: torch.Tensor, w_ptr_a: torch.Tensor,
+                      lora_stride_a: int, w_ptr_b: torch.Tensor, lora_stride_b: int,
+                      topk_ids: torch.Tensor, topk_weights: torch.Tensor, lora_ids: torch.Tensor,
+                      rank: int, hidden_size: int, *, num_adapters: int,
+                      lora_dtype: torch.dtype = torch.bfloat16, scale: float = 1.0,
+                      out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """MoE output ``[T, H]``: the routing-weighted combine of the FC2 rows
+    (``fc2_out``, permuted ``[padded_rows, H]`` in bf16, fp16 or fp32) with
+    the FC2 LoRA delta added, in one pass and one rounding.  The other
+    arguments are those of :func:`bgmv_moe_gemm2_lora_delta`."""
+    _need(isinstance(fc2_out, torch.Tensor) and fc2_out.dim() == 2 and
+          fc2_out.shape[1] == hidden_size and
+          fc2_out.shape[0] == gemm1_activation_output.shape[0],
+          "moe_finalize_lora: fc2_out must be [padded_rows, hidden_size]")
+    _need(fc2_out.dtype in _DT, "moe_finalize_lora: fc2_out must be bf16, fp16 or fp32")
+    return _delta_call(fc2_out, gemm1_activation_output, expanded_idx_to_permuted_idx, w_ptr_a,
+                       lora_stride_a, w_ptr_b, lora_stride_b, topk_ids, topk_weights, lora_ids,
+                       rank, hidden_size, num_adapters, lora_dtype, scale, out_dtype, out,
+                       workspace)
+
+
+def _delta_call(fc2, act, perm, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, topk_ids,
+                topk_weights, lora_ids, rank, hidden_size, num_adapters, lora_dtype, scale,
+                out_dtype, out, workspace):
     _need(act.dim() == 2, "bgmv_moe_gemm2_lora_delta: activation must be [padded_rows, I]")
     _need(topk_ids.dim() == 2 and topk_weights.shape == topk_ids.shape,
           "bgmv_moe_gemm2_lora_delta: topk_ids / topk_weights must be [T, top_k]")
@@ -141,7 +172,7 @@ def bgmv_moe_gemm2_lora_delta(gemm1_activation_output: torch.Tensor,
     _need(act.dtype == lora_dtype, "bgmv_moe_gemm2_lora_delta: activation dtype must be lora_dtype")
     _need(lora_dtype in _DT and out_dtype in _DT, "bgmv_moe_gemm2_lora_delta: unsupported dtype")
     _need_cuda("bgmv_moe_gemm2_lora_delta", act, perm, w_ptr_a, w_ptr_b, topk_ids, topk_weights,
-               lora_ids, out, workspace)
+               lora_ids, out, workspace, fc2)
     E = w_ptr_a.numel()
     act = act.contiguous()
     perm, topk_ids, topk_weights, lora_ids = (x.contiguous() for x in
@@ -154,12 +185,16 @@ def bgmv_moe_gemm2_lora_delta(gemm1_activation_output: torch.Tensor,
     need = delta_workspace_bytes(T, top_k, E, num_adapters, rank)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=act.device)
-    check(_lib.lib().mi_moe_fc2_lora_delta(
-        _ptr(act), act.shape[0], act.shape[1], _ptr(perm), _ptr(w_ptr_a), int(lora_stride_a),
-        _ptr(w_ptr_b), int(lora_stride_b), _ptr(topk_ids), _ptr(topk_weights), _ptr(lora_ids),
-        T, top_k, E, int(num_adapters), int(rank), int(hidden_size), _DT[lora_dtype],
-        float(scale), _DT[out_dtype], _ptr(out), _ptr(workspace), workspace.numel(),
-        _stream(act.device)))
+    args = (_ptr(act), act.shape[0], act.shape[1], _ptr(perm), _ptr(w_ptr_a), int(lora_stride_a),
+            _ptr(w_ptr_b), int(lora_stride_b), _ptr(topk_ids), _ptr(topk_weights), _ptr(lora_ids),
+            T, top_k, E, int(num_adapters), int(rank), int(hidden_size), _DT[lora_dtype],
+            float(scale), _DT[out_dtype], _ptr(out), _ptr(workspace), workspace.numel(),
+            _stream(act.device))
+    if fc2 is None:
+        check(_lib.lib().mi_moe_fc2_lora_delta(*args))
+    else:
+        fc2 = fc2.contiguous()
+        check(_lib.lib().mi_moe_fc2_finalize_lora(_ptr(fc2), _DT[fc2.dtype], *args))
     return out
 
 

@@ -771,7 +771,152 @@ struct ExpandArgs {
   long cap;
   int L, H, rank, maxblk, max_tiles, nch;
   int out_kind;  // 0 bf16, 1 fp32, 2 fp16
+  // finalize (fc2 != NULL): add the routing-weighted FC2 rows of each token
+  const void* fc2;
+  const int32_t* perm;
+  const float* topk_weights;
+  int fc2_kind;  // 0 bf16, 1 fp32, 2 fp16
+  int top_k, padded_rows;
 };
+
+// 8 consecutive values of an FC2 row as fp32 (exact conversions)
+__device__ __forceinline__ void fc2_load8(const void* base, int kind, long off, f32x4& x0,
+                                          f32x4& x1) {
+  if (kind == 1) {
+    x0 = gld<f32x4>(static_cast<const float*>(base) + off);
+    x1 = gld<f32x4>(static_cast<const float*>(base) + off + 4);
+  } else if (kind == 2) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const h8 h = __builtin_bit_cast(h8, gld<u32x4>(static_cast<const uint16_t*>(base) + off));
+    x0 = f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
+               static_cast<float>(h[3])};
+    x1 = f32x4{static_cast<float>(h[4]), static_cast<float>(h[5]), static_cast<float>(h[6]),
+               static_cast<float>(h[7])};
+  } else {
+    const u32x4 v = gld<u32x4>(static_cast<const uint16_t*>(base) + off);
+    x0 = f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+    x1 = f32x4{__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+               __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u)};
+  }
+}
+
+// 8 output columns of token t rounded once to the output type
+__device__ __forceinline__ void store_out8(const ExpandArgs& p, int t, int col, f32x4 v0,
+                                           f32x4 v1) {
+  const long o = static_cast<long>(t) * p.H + col;
+  if (p.out_kind == 1) {
+    gst<f32x4>(static_cast<float*>(p.out) + o, v0);
+    gst<f32x4>(static_cast<float*>(p.out) + o + 4, v1);
+  } else if (p.out_kind == 2) {  // IEEE fp16, round to nearest even
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const h8 h = {static_cast<_Float16>(v0.x), static_cast<_Float16>(v0.y),
+                  static_cast<_Float16>(v0.z), static_cast<_Float16>(v0.w),
+                  static_cast<_Float16>(v1.x), static_cast<_Float16>(v1.y),
+                  static_cast<_Float16>(v1.z), static_cast<_Float16>(v1.w)};
+    gst<u32x4>(static_cast<uint16_t*>(p.out) + o, __builtin_bit_cast(u32x4, h));
+  } else {
+    u32x4 w;
+    w.x = pack_bf16x2(v0.x, v0.y);
+    w.y = pack_bf16x2(v0.z, v0.w);
+    w.z = pack_bf16x2(v1.x, v1.y);
+    w.w = pack_bf16x2(v1.z, v1.w);
+    gst<u32x4>(static_cast<uint16_t*>(p.out) + o, w);
+  }
+}
+
+// Finalize: the routed FC2 rows of a token, FIN_KB slots at a time.  A slot
+// not routed here (row < 0 or >= padded_rows, or past top_k) gets row 0 and
+// weight 0 and is skipped when summing.
+constexpr int FIN_KB = 8;
+struct Route {
+  int r[FIN_KB];
+  float w[FIN_KB];
+};
+__device__ __forceinline__ Route load_route(const ExpandArgs& p, int t, int j0) {
+  Route rt;
+#pragma unroll
+  for (int jj = 0; jj < FIN_KB; ++jj) {
+    const int j = j0 + jj;
+    const long s = static_cast<long>(t) * p.top_k + j;
+    const int rr = j < p.top_k ? gld<int>(p.perm + s) : -1;
+    const bool ok = rr >= 0 && rr < p.padded_rows;
+    rt.r[jj] = ok ? rr : 0;
+    rt.w[jj] = ok ? gld<float>(p.topk_weights + s) : 0.f;
+  }
+  return rt;
+}
+struct Rows8 {
+  f32x4 x0[FIN_KB], x1[FIN_KB];
+};
+__device__ __forceinline__ Rows8 load_rows(const ExpandArgs& p, const Route& rt, int col) {
+  Rows8 x;
+#pragma unroll
+  for (int jj = 0; jj < FIN_KB; ++jj)
+    fc2_load8(p.fc2, p.fc2_kind, static_cast<long>(rt.r[jj]) * p.H + col, x.x0[jj], x.x1[jj]);
+  return x;
+}
+// v += sum over the batch of w * row, in slot order (one FMA each)
+__device__ __forceinline__ void add_rows(const Route& rt, const Rows8& x, f32x4& v0, f32x4& v1) {
+#pragma unroll
+  for (int jj = 0; jj < FIN_KB; ++jj) {
+    if (rt.w[jj] == 0.f) continue;  // not routed here (or a zero weight: adds nothing)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v0[q] = __builtin_fmaf(rt.w[jj], x.x0[jj][q], v0[q]);
+      v1[q] = __builtin_fmaf(rt.w[jj], x.x1[jj][q], v1[q]);
+    }
+  }
+}
+
+// Write-out of a tile's TT x EXP_CW outputs, 8 columns per item, items tid,
+// tid + NT_EXP, ...: the delta of item i comes from `delta(i)` (fp32), plus,
+// when finalizing, the routed FC2 rows.  For top_k <= FIN_KB the loads are
+// pipelined over items: the rows of item i and the routing of item i+NT_EXP
+// are in flight together.
+template <typename DeltaFn>
+__device__ __forceinline__ void write_tile(const ExpandArgs& p, const Tile& tile, int h0,
+                                           DeltaFn delta) {
+  const int tid = threadIdx.x;
+  const int nit = tile.count * (EXP_CW / 8);
+  auto tok = [&](int i) { return gld<int>(p.tok_list + tile.start + i / (EXP_CW / 8)); };
+  auto colof = [&](int i) { return h0 + (i % (EXP_CW / 8)) * 8; };
+  if (p.fc2 == nullptr) {
+    for (int i = tid; i < nit; i += NT_EXP) {
+      f32x4 v0, v1;
+      delta(i, v0, v1);
+      store_out8(p, tok(i), colof(i), v0, v1);
+    }
+    return;
+  }
+  if (p.top_k <= FIN_KB) {
+    int t = tid < nit ? tok(tid) : 0;
+    Route rt = load_route(p, tid < nit ? t : 0, tid < nit ? 0 : p.top_k);
+    for (int i = tid; i < nit; i += NT_EXP) {
+      const Rows8 x = load_rows(p, rt, colof(i));
+      const int in = i + NT_EXP;
+      const int tn = in < nit ? tok(in) : 0;
+      const Route rn = load_route(p, tn, in < nit ? 0 : p.top_k);
+      f32x4 v0, v1;
+      delta(i, v0, v1);
+      add_rows(rt, x, v0, v1);
+      store_out8(p, t, colof(i), v0, v1);
+      rt = rn;
+      t = tn;
+    }
+    return;
+  }
+  for (int i = tid; i < nit; i += NT_EXP) {
+    const int t = tok(i);
+    f32x4 v0, v1;
+    delta(i, v0, v1);
+    for (int j0 = 0; j0 < p.top_k; j0 += FIN_KB) {
+      const Route rt = load_route(p, t, j0);
+      add_rows(rt, load_rows(p, rt, colof(i)), v0, v1);
+    }
+    store_out8(p, t, colof(i), v0, v1);
+  }
+}
 
 // accumulator rows of EXP_CW floats; 16-byte chunk c of row tl sits at c ^ (tl & 31)
 __device__ __forceinline__ int acc_chunk(int tl, int c) {
@@ -953,15 +1098,11 @@ __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
   const int tid = threadIdx.x;
   const int h0 = ch * EXP_CW;
 
-  if (tile.bucket >= p.L) {  // no adapter: +0 rows
-    for (int i = tid; i < tile.count * (EXP_CW / 4); i += NT_EXP) {
-      const int tl = i / (EXP_CW / 4), c = (i % (EXP_CW / 4)) * 4;
-      const long o = static_cast<long>(gld<int>(p.tok_list + tile.start + tl)) * p.H + h0 + c;
-      if (p.out_kind == 1)
-        gst<f32x4>(static_cast<float*>(p.out) + o, f32x4{0.f, 0.f, 0.f, 0.f});
-      else
-        gst<uint64_t>(static_cast<uint16_t*>(p.out) + o, 0ull);
-    }
+  if (tile.bucket >= p.L) {  // no adapter: a +0 delta (plus the combine when finalizing)
+    write_tile(p, tile, h0, [](int, f32x4& v0, f32x4& v1) {
+      v0 = f32x4{0.f, 0.f, 0.f, 0.f};
+      v1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    });
     return;
   }
   const int nblk = gld<int>(p.tinfo + 2 * ti);
@@ -983,32 +1124,12 @@ __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
       expand_blocks<NB, PART, false, F16>(s_acc, s_bp, u2t, tlt, ft, nblk, p.rank, p.H, h0);
   }
   __syncthreads();
-  // write out: 8 columns per thread-iteration
-  for (int i = tid; i < tile.count * (EXP_CW / 8); i += NT_EXP) {
+  const f32x4* a = reinterpret_cast<const f32x4*>(s_acc);
+  write_tile(p, tile, h0, [&](int i, f32x4& v0, f32x4& v1) {
     const int tl = i / (EXP_CW / 8), c = (i % (EXP_CW / 8)) * 8;
-    const f32x4* a = reinterpret_cast<const f32x4*>(s_acc);
-    const long o = static_cast<long>(gld<int>(p.tok_list + tile.start + tl)) * p.H + h0 + c;
-    const f32x4 v0 = a[acc_chunk(tl, c / 4)];
-    const f32x4 v1 = a[acc_chunk(tl, c / 4 + 1)];
-    if (p.out_kind == 1) {
-      gst<f32x4>(static_cast<float*>(p.out) + o, v0);
-      gst<f32x4>(static_cast<float*>(p.out) + o + 4, v1);
-    } else if (p.out_kind == 2) {  // IEEE fp16, round to nearest even
-      typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-      const h8 h = {static_cast<_Float16>(v0.x), static_cast<_Float16>(v0.y),
-                    static_cast<_Float16>(v0.z), static_cast<_Float16>(v0.w),
-                    static_cast<_Float16>(v1.x), static_cast<_Float16>(v1.y),
-                    static_cast<_Float16>(v1.z), static_cast<_Float16>(v1.w)};
-      gst<u32x4>(static_cast<uint16_t*>(p.out) + o, __builtin_bit_cast(u32x4, h));
-    } else {
-      u32x4 w;
-      w.x = pack_bf16x2(v0.x, v0.y);
-      w.y = pack_bf16x2(v0.z, v0.w);
-      w.z = pack_bf16x2(v1.x, v1.y);
-      w.w = pack_bf16x2(v1.z, v1.w);
-      gst<u32x4>(static_cast<uint16_t*>(p.out) + o, w);
-    }
-  }
+    v0 = a[acc_chunk(tl, c / 4)];
+    v1 = a[acc_chunk(tl, c / 4 + 1)];
+  });
 }
 
 int num_cus() {
@@ -1031,14 +1152,18 @@ extern "C" size_t mi_moe_fc2_lora_delta_workspace_size(int64_t num_tokens, int64
   return mi::layout(num_tokens, top_k, num_experts, num_adapters, rank).total;
 }
 
-extern "C" mi_status mi_moe_fc2_lora_delta(
-    const void* act, int64_t padded_rows, int64_t inter_size, const int32_t* perm,
-    const int64_t* w_ptr_a, int64_t lora_stride_a, const int64_t* w_ptr_b, int64_t lora_stride_b,
-    const int32_t* topk_ids, const float* topk_weights, const int32_t* lora_ids, int64_t T,
-    int64_t top_k, int64_t E, int64_t L, int64_t rank, int64_t H, mi_dtype lora_dtype, float scale,
-    mi_dtype out_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  using namespace mi;
-  clear_error();
+namespace mi {
+namespace {
+
+// The delta and, when fc2 is given, the finalize: both entry points below.
+mi_status run_delta(const char* what, const void* act, int64_t padded_rows, int64_t inter_size,
+                    const int32_t* perm, const int64_t* w_ptr_a, int64_t lora_stride_a,
+                    const int64_t* w_ptr_b, int64_t lora_stride_b, const int32_t* topk_ids,
+                    const float* topk_weights, const int32_t* lora_ids, int64_t T, int64_t top_k,
+                    int64_t E, int64_t L, int64_t rank, int64_t H, mi_dtype lora_dtype,
+                    float scale, const void* fc2, mi_dtype fc2_dtype, mi_dtype out_dtype,
+                    void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)what;
   MI_REQUIRE(top_k >= 1 && top_k <= MAX_TOPK, "bgmv_moe_gemm2_lora_delta: top_k must be in [1, %d]",
              MAX_TOPK);
   MI_REQUIRE(T >= 0 && T * top_k < (1LL << 24),
@@ -1163,7 +1288,10 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
   const int nch = static_cast<int>(H / EXP_CW);
   ExpandArgs ea{tok_list, tiles, counters, u2, blk_b, blk_tl, blk_f, tinfo, out, ly.cap,
                 static_cast<int>(L), static_cast<int>(H), static_cast<int>(rank), ly.maxblk,
-                ntiles, nch, out_dtype == MI_F32 ? 1 : (out_dtype == MI_F16 ? 2 : 0)};
+                ntiles, nch, out_dtype == MI_F32 ? 1 : (out_dtype == MI_F16 ? 2 : 0),
+                fc2, perm, topk_weights,
+                fc2_dtype == MI_F32 ? 1 : (fc2_dtype == MI_F16 ? 2 : 0),
+                static_cast<int>(top_k), static_cast<int>(padded_rows)};
   // whole runs of 8 tiles x nch chunks, rounded to a multiple of the 8 XCDs
   const long ewg = ((static_cast<long>(ntiles) + 7) / 8 * 8 * nch + 7) & ~7L;
   MI_REQUIRE(ewg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
@@ -1186,4 +1314,40 @@ extern "C" mi_status mi_moe_fc2_lora_delta(
                         (long long)rank);
   }
   return launch_status("bgmv_moe_gemm2_lora_delta (expand)");
+}
+
+}  // namespace
+}  // namespace mi
+
+extern "C" mi_status mi_moe_fc2_lora_delta(
+    const void* act, int64_t padded_rows, int64_t inter_size, const int32_t* perm,
+    const int64_t* w_ptr_a, int64_t lora_stride_a, const int64_t* w_ptr_b, int64_t lora_stride_b,
+    const int32_t* topk_ids, const float* topk_weights, const int32_t* lora_ids, int64_t T,
+    int64_t top_k, int64_t E, int64_t L, int64_t rank, int64_t H, mi_dtype lora_dtype, float scale,
+    mi_dtype out_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  mi::clear_error();
+  return mi::run_delta("bgmv_moe_gemm2_lora_delta", act, padded_rows, inter_size, perm, w_ptr_a,
+                       lora_stride_a, w_ptr_b, lora_stride_b, topk_ids, topk_weights, lora_ids, T,
+                       top_k, E, L, rank, H, lora_dtype, scale, nullptr, MI_BF16, out_dtype, out,
+                       workspace, workspace_bytes, stream);
+}
+
+extern "C" mi_status mi_moe_fc2_finalize_lora(
+    const void* fc2, mi_dtype fc2_dtype, const void* act, int64_t padded_rows,
+    int64_t inter_size, const int32_t* perm, const int64_t* w_ptr_a, int64_t lora_stride_a,
+    const int64_t* w_ptr_b, int64_t lora_stride_b, const int32_t* topk_ids,
+    const float* topk_weights, const int32_t* lora_ids, int64_t T, int64_t top_k, int64_t E,
+    int64_t L, int64_t rank, int64_t H, mi_dtype lora_dtype, float scale, mi_dtype out_dtype,
+    void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  mi::clear_error();
+  MI_REQUIRE(fc2_dtype == MI_BF16 || fc2_dtype == MI_F16 || fc2_dtype == MI_F32,
+             "moe_fc2_finalize_lora: fc2_out dtype must be bf16, fp16 or fp32");
+  if (T > 0) {
+    MI_REQUIRE(fc2 != nullptr, "moe_fc2_finalize_lora: fc2_out is null");
+    MI_REQUIRE(mi::aligned16(fc2), "moe_fc2_finalize_lora: fc2_out must be 16-byte aligned");
+  }
+  return mi::run_delta("moe_fc2_finalize_lora", act, padded_rows, inter_size, perm, w_ptr_a,
+                       lora_stride_a, w_ptr_b, lora_stride_b, topk_ids, topk_weights, lora_ids, T,
+                       top_k, E, L, rank, H, lora_dtype, scale, fc2, fc2_dtype, out_dtype, out,
+                       workspace, workspace_bytes, stream);
 }

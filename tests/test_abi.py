@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert syms == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(L, s), s
-    assert L.mi_abi_version() == 2
+    assert L.mi_abi_version() == 3
 
 
 def _err(status):
@@ -101,5 +101,13 @@ def test_delta_validation():
         _lib.check(_delta(H=200))
     assert "lora_dtype must be bf16 or fp16" in _err(_delta(ldt=_lib.MI_F32))
     L = _lib.lib()
+    fin = lambda fc2, fdt, **kw: L.mi_moe_fc2_finalize_lora(fc2, fdt, *dict(
+        dict(act=FAKE, padded_rows=64, inter=128, perm=FAKE, wa=FAKE, sa=1024, wb=FAKE, sb=1024,
+             ids=FAKE, w=FAKE, lids=FAKE, T=16, k=2, E=4, L=2, r=16, H=256, ldt=_lib.MI_BF16,
+             scale=2.0, odt=_lib.MI_BF16, out=FAKE, ws=FAKE, wsb=1 << 30, stream=NULL),
+        **kw).values())
+    assert "fc2_out dtype" in _err(fin(FAKE, 7))
+    assert "fc2_out is null" in _err(fin(NULL, _lib.MI_BF16))
+    assert "rank" in _err(fin(FAKE, _lib.MI_F32, r=12))
     assert L.mi_moe_fc2_lora_delta_workspace_size(8192, 8, 64, 8, 16) > 8192 * 8 * 16 * 4
     assert L.mi_moe_fc2_lora_delta_workspace_size(8, 0, 4, 2, 8) == 0
