@@ -18,6 +18,9 @@ passage of the source pages it follows (cited by page title and section):
   -> :mod:`oracle.fold`
 - MoE finalize with the delta added (``bgmv_moe_gemm2_lora_delta``,
   description and return value) -> :mod:`oracle.finalize`
+- routing output -> expert-sorted permutation and permuted rows
+  (``expanded_idx_to_permuted_idx`` and ``m_indptr`` parameters) ->
+  :mod:`oracle.permute`
 
 Inputs are numpy arrays; bf16 tensors are passed as their uint16 bit patterns.
 
@@ -29,4 +32,4 @@ unpinned** by the pages: they follow the public OCP / block-scaling
 convention and are pinned only to that convention (two independent codings
 and hand-worked offsets).
 """
-from . import formats, grouped_mm, lora_delta, nvfp4, fold, finalize  # noqa: F401
+from . import formats, grouped_mm, lora_delta, nvfp4, fold, finalize, permute  # noqa: F401
