@@ -45,7 +45,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling aid); "
                    "'copy_probe' (not part of the step) is a 512 MiB fp32 negation (read + write) used to "
-                   "calibrate the HBM byte counters")
+                   "calibrate the HBM byte counters; 'finalize' and 'permute' time the ops "
+                   "outside the step")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                    "'--only nvfp4_raw,copy_probe' into the committed traffic summary")
@@ -265,36 +266,61 @@ def main():
                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / PEAK_MFMA_TFLOPS, 4), "traffic": read_traffic()}
 
-    # Outside the step: the MoE finalize with the delta added (FC2 rows of the
-    # delta workload's routing, bf16 [padded_rows, H]), timed on its own.
-    extra = None
-    if not only or "finalize" in only:
-        fc2 = synth.bf16_normal((dc.act.shape[0], dc.H), 1.0, synth.gen(77, dev), dev)
-        fout = torch.empty((dc.T, dc.H), dtype=torch.bfloat16, device=dev)
-        fin = lambda: mi.moe_finalize_lora(fc2, dc.act, dc.perm, wa, sa, wb, sb, dc.topk_ids,
-                                           dc.topk_weights, dc.lora_ids, dc.rank, dc.H,
-                                           num_adapters=dc.L, scale=dc.scale, out=fout,
-                                           workspace=ws)
+    def time_alone(fn):
         for _ in range(3):
-            fin()
+            fn()
         fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
         torch.cuda.synchronize()
         for a_, b_ in fe:
             a_.record(stream)
-            fin()
+            fn()
             b_.record(stream)
         torch.cuda.synchronize()
-        fms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in fe]))
+        return float(np.mean([a_.elapsed_time(b_) for a_, b_ in fe]))
+
+    def hbm_entry(ms, nbytes, note, flops=None):
+        e = {"ms": round(ms, 5), "gbps": round(nbytes / ms / 1e6, 1),
+             "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBPS, 4),
+             "algorithmic_bytes": nbytes, "note": note}
+        if flops is not None:
+            e["algorithmic_flops"] = flops
+        return e
+
+    # Outside the step, each timed on its own: the MoE finalize with the delta
+    # added (FC2 rows of the delta workload's routing, bf16 [padded_rows, H]),
+    # and the routing -> permutation -> permuted FC1 input rows of the same
+    # routing (T=8192, top_k=8, E=64; bf16 token rows of H=4096).
+    extra = {}
+    if not only or "finalize" in only:
+        fc2 = synth.bf16_normal((dc.act.shape[0], dc.H), 1.0, synth.gen(77, dev), dev)
+        fout = torch.empty((dc.T, dc.H), dtype=torch.bfloat16, device=dev)
+        fms = time_alone(lambda: mi.moe_finalize_lora(
+            fc2, dc.act, dc.perm, wa, sa, wb, sb, dc.topk_ids, dc.topk_weights, dc.lora_ids,
+            dc.rank, dc.H, num_adapters=dc.L, scale=dc.scale, out=fout, workspace=ws))
         n_routed = int((perm >= 0).sum())
-        fbytes = delta_bytes + 2.0 * dc.H * n_routed
-        fflops = delta_flops + 2.0 * dc.H * n_routed
-        extra = {"finalize_fused": {
-            "ms": round(fms, 5), "gbps": round(fbytes / fms / 1e6, 1),
-            "frac_hbm_peak": round(fbytes / fms / 1e6 / PEAK_HBM_GBPS, 4),
-            "algorithmic_bytes": fbytes, "algorithmic_flops": fflops,
-            "note": "MoE finalize (weighted combine of the routed FC2 rows) with the LoRA delta "
-                    "added, delta workload; not part of the step"}}
+        extra["finalize_fused"] = hbm_entry(
+            fms, delta_bytes + 2.0 * dc.H * n_routed,
+            "MoE finalize (weighted combine of the routed FC2 rows) with the LoRA delta added, "
+            "delta workload; not part of the step", delta_flops + 2.0 * dc.H * n_routed)
+    if not only or "permute" in only:
+        nslot = dc.T * dc.top_k
+        rws = torch.empty(mi.route_workspace_bytes(nslot, dc.E), dtype=torch.uint8, device=dev)
+        rms = time_alone(lambda: mi.moe_route_permutation(dc.topk_ids, dc.E, with_inverse=True,
+                                                          workspace=rws))
+        extra["route_permutation"] = hbm_entry(
+            rms, 12.0 * nslot + 4.0 * (dc.E + 1),
+            "topk_ids [8192, 8] -> m_indptr, expanded_idx_to_permuted_idx and its inverse "
+            "(E=64); three launches, latency-bound at this size")
+        _, rperm = mi.moe_route_permutation(dc.topk_ids, dc.E)
+        xtok = synth.bf16_normal((dc.T, dc.H), 1.0, synth.gen(78, dev), dev)
+        xperm = torch.empty((nslot, dc.H), dtype=torch.bfloat16, device=dev)
+        pms = time_alone(lambda: mi.moe_permute_rows(xtok, rperm, dc.top_k, out=xperm))
+        extra["permute_rows"] = hbm_entry(
+            pms, 2.0 * dc.H * (dc.T + nslot) + 4.0 * nslot,
+            "token rows bf16 [8192, 4096] -> permuted rows [65536, 4096] (each token row read "
+            "once, written top_k times)")
+    extra = extra or None
 
     cpu = None
     if not args.no_cpu_baseline and not only:
@@ -302,7 +328,7 @@ def main():
 
     line = {
         "metric": METRIC,
-        "value": round(step_flops / (ms_step * 1e-3) / 1e12, 2),
+        "value": round(step_flops / (max(ms_step, 1e-9) * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,

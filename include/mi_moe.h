@@ -9,6 +9,9 @@
  *   - mi_moe_fc2_finalize_lora  the MoE finalize (routing-weighted combine of the FC2
  *                             rows) with that delta added, in one pass
  *                             (bgmv_moe_gemm2_lora_delta, description and return value)
+ *   - mi_moe_route_permutation  routing output -> expert-sorted permutation
+ *                             (bgmv_moe_gemm2_lora_delta and grouped_mm_bf16, parameters)
+ *   - mi_moe_permute_rows     token rows -> permuted rows (the FC1 input)
  *   - mi_mm_nvfp4_lora        NVFP4 GEMM with an fp32 LoRA epilogue, raw and prepared
  *                             (flashinfer.gemm.mm_nvfp4_lora, formula and the two bullets)
  *   - mi_prepare_lora_fold    the prepared-path fold
@@ -157,6 +160,51 @@ MI_API mi_status mi_moe_fc2_finalize_lora(const void* fc2, mi_dtype fc2_dtype, c
                                    int64_t hidden_size, mi_dtype lora_dtype, float scale,
                                    mi_dtype out_dtype, void* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/*
+ * Routing output -> the expert-sorted permutation that the grouped GEMM, the
+ * delta and the finalize consume (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta,
+ * parameter expanded_idx_to_permuted_idx: expanded index t*top_k+j -> permuted
+ * row, negative when inactive; flashinfer.grouped_mm.grouped_mm_bf16, parameter
+ * m_indptr: cumulative rows per group).  The permuted order is a stable sort of
+ * the slots by expert id: expert e owns rows m_indptr[e] .. m_indptr[e+1]-1 and,
+ * inside it, the slots keep their expanded order.  A slot whose id is outside
+ * [0, num_experts) is not routed here: its entry is -1 and it takes no row.
+ * The result is deterministic (bit-identical on every run).
+ *   topk_ids      int32 [num_tokens, top_k], device
+ *   m_indptr      int32 [num_experts + 1], device, written (m_indptr[0] = 0)
+ *   expanded_idx_to_permuted_idx  int32 [num_tokens * top_k], device, written
+ *   permuted_idx_to_expanded_idx  int32 [num_tokens * top_k] or NULL: entry p is
+ *                 the expanded index at permuted row p for p < m_indptr[E], -1 after
+ *   workspace     device scratch of mi_moe_route_workspace_size(num_tokens*top_k,
+ *                 num_experts) bytes; its contents are not kept between calls
+ * Requirements: top_k >= 1, num_tokens >= 0, num_tokens*top_k < 2^31,
+ * 1 <= num_experts <= 1024; the output arrays may not alias topk_ids or each
+ * other.  num_tokens == 0 writes m_indptr = 0 only.
+ */
+MI_API size_t mi_moe_route_workspace_size(int64_t num_slots, int64_t num_experts);
+MI_API mi_status mi_moe_route_permutation(const int32_t* topk_ids, int64_t num_tokens,
+                                   int64_t top_k, int64_t num_experts, int32_t* m_indptr,
+                                   int32_t* expanded_idx_to_permuted_idx,
+                                   int32_t* permuted_idx_to_expanded_idx, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * The FC1 input in permuted row order: out[perm[t*top_k+j]] = x[t] for every
+ * slot whose entry lies in [0, out_rows); other rows of out are untouched
+ * (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta, parameter
+ * expanded_idx_to_permuted_idx, read in the gathering direction).  A byte copy:
+ * any element type, rows of row_bytes bytes.
+ *   x     [num_tokens, row_bytes] bytes, 16-byte aligned, device
+ *   perm  int32 [num_tokens * top_k], device (e.g. from mi_moe_route_permutation)
+ *   out   [out_rows, row_bytes] bytes, 16-byte aligned, device; may not alias x
+ * Requirements: row_bytes > 0 and a multiple of 16, top_k >= 1,
+ * 0 <= num_tokens*top_k < 2^31, out_rows >= 0.  Two slots with the same row
+ * (an invalid permutation) leave one of the token rows there.
+ */
+MI_API mi_status mi_moe_permute_rows(const void* x, int64_t num_tokens, int64_t row_bytes,
+                              const int32_t* perm, int64_t top_k, void* out, int64_t out_rows,
+                              void* stream);
 
 /*
  * NVFP4 GEMM with a BF16 LoRA correction (flashinfer.gemm.mm_nvfp4_lora):

@@ -21,6 +21,9 @@ EXPORTS = [
     "mi_moe_fc2_lora_delta_workspace_size",
     "mi_moe_fc2_lora_delta",
     "mi_moe_fc2_finalize_lora",
+    "mi_moe_route_workspace_size",
+    "mi_moe_route_permutation",
+    "mi_moe_permute_rows",
     "mi_mm_nvfp4_lora",
     "mi_prepare_lora_fold",
     "mi_nvfp4_dequant_bf16",
@@ -64,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.mi_moe_fc2_finalize_lora.argtypes = [
             P, I32,               # fc2, fc2_dtype
             *L.mi_moe_fc2_lora_delta.argtypes]
+        L.mi_moe_route_workspace_size.restype = SZ
+        L.mi_moe_route_workspace_size.argtypes = [I64, I64]
+        L.mi_moe_route_permutation.restype = I32
+        L.mi_moe_route_permutation.argtypes = [P, I64, I64, I64, P, P, P, P, SZ, P]
+        L.mi_moe_permute_rows.restype = I32
+        L.mi_moe_permute_rows.argtypes = [P, I64, I64, P, I64, P, I64, P]
         L.mi_mm_nvfp4_lora.restype = I32
         L.mi_mm_nvfp4_lora.argtypes = [P, P, P, SZ, P, SZ, P, I64, I64, I64, P, I64, P, P, P, P,
                                        P, P, P]

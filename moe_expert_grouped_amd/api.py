@@ -22,6 +22,9 @@ __all__ = [
     "grouped_mm_bf16",
     "bgmv_moe_gemm2_lora_delta",
     "moe_finalize_lora",
+    "moe_route_permutation",
+    "moe_permute_rows",
+    "route_workspace_bytes",
     "delta_workspace_bytes",
     "fill_w_ptr",
     "mm_nvfp4_lora",
@@ -195,6 +198,60 @@ def _delta_call(fc2, act, perm, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, 
     else:
         fc2 = fc2.contiguous()
         check(_lib.lib().mi_moe_fc2_finalize_lora(_ptr(fc2), _DT[fc2.dtype], *args))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# routing output -> permutation, permuted rows
+# ---------------------------------------------------------------------------
+
+def route_workspace_bytes(num_slots: int, num_experts: int) -> int:
+    return int(_lib.lib().mi_moe_route_workspace_size(num_slots, num_experts))
+
+
+def moe_route_permutation(topk_ids: torch.Tensor, num_experts: int, *,
+                          with_inverse: bool = False, workspace: torch.Tensor | None = None):
+    """``(m_indptr, expanded_idx_to_permuted_idx[, permuted_idx_to_expanded_idx])``
+    from ``topk_ids`` int32 ``[T, top_k]``: the slots sorted stably by expert
+    id, ids outside ``[0, num_experts)`` left out (entry -1).  All int32 on
+    the device; ``m_indptr`` is ``[num_experts + 1]``."""
+    _need(topk_ids.dim() == 2 and topk_ids.dtype == torch.int32,
+          "moe_route_permutation: topk_ids must be int32 [num_tokens, top_k]")
+    _need_cuda("moe_route_permutation", topk_ids, workspace)
+    T, top_k = topk_ids.shape
+    dev = topk_ids.device
+    topk_ids = topk_ids.contiguous()
+    m_indptr = torch.empty(int(num_experts) + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * top_k, dtype=torch.int32, device=dev)
+    inverse = torch.empty(T * top_k, dtype=torch.int32, device=dev) if with_inverse else None
+    need = route_workspace_bytes(T * top_k, num_experts)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    check(_lib.lib().mi_moe_route_permutation(
+        _ptr(topk_ids), T, top_k, int(num_experts), _ptr(m_indptr), _ptr(perm), _ptr(inverse),
+        _ptr(workspace), workspace.numel(), _stream(dev)))
+    return (m_indptr, perm, inverse) if with_inverse else (m_indptr, perm)
+
+
+def moe_permute_rows(x: torch.Tensor, expanded_idx_to_permuted_idx: torch.Tensor, top_k: int,
+                     out_rows: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """``out[perm[t*top_k + j]] = x[t]`` for every slot whose row lies in
+    ``[0, out_rows)`` (other rows of ``out`` untouched; a fresh ``out`` is
+    zero-filled).  ``x`` ``[T, ...]`` of any dtype, rows of a multiple of 16 bytes."""
+    _need(x.dim() >= 1, "moe_permute_rows: x must be [num_tokens, ...]")
+    perm = expanded_idx_to_permuted_idx
+    _need(perm.dtype == torch.int32 and perm.numel() == x.shape[0] * int(top_k),
+          "moe_permute_rows: expanded_idx_to_permuted_idx must be int32 [num_tokens*top_k]")
+    _need_cuda("moe_permute_rows", x, perm, out)
+    x, perm = x.contiguous(), perm.contiguous()
+    if out is None:
+        rows = perm.numel() if out_rows is None else int(out_rows)
+        out = torch.zeros((rows,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    _need(out.dtype == x.dtype and out.shape[1:] == x.shape[1:] and out.is_contiguous(),
+          "moe_permute_rows: out must be contiguous [out_rows, ...] of x's dtype")
+    row_bytes = x[0].numel() * x.element_size() if x.shape[0] else 16
+    check(_lib.lib().mi_moe_permute_rows(_ptr(x), x.shape[0], row_bytes, _ptr(perm), int(top_k),
+                                         _ptr(out), out.shape[0], _stream(x.device)))
     return out
 
 

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmi_moe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["errors.cpp", "grouped_mm.hip", "lora_delta.hip", "nvfp4_lora.hip"]
+SOURCES = ["errors.cpp", "grouped_mm.hip", "lora_delta.hip", "nvfp4_lora.hip", "permute.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

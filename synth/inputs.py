@@ -23,6 +23,7 @@ __all__ = [
     "bf16_normal",
     "bf16_ints",
     "route",
+    "routing_ids",
     "zipf_counts",
     "sf_buffer_bytes",
     "GroupedCase",
@@ -94,6 +95,34 @@ def route(topk_ids: torch.Tensor, num_experts: int, g: torch.Generator,
 
 def distinct_topk(T: int, E: int, k: int, g: torch.Generator) -> torch.Tensor:
     return torch.rand(T, E, generator=g).argsort(dim=1)[:, :k].to(torch.int32)
+
+
+def routing_ids(seed: int, T: int, top_k: int, E: int, invalid_frac: float = 0.0,
+                zipf_s: float = 0.0) -> torch.Tensor:
+    """Router output ``topk_ids`` int32 ``[T, top_k]`` (CPU).
+
+    ``zipf_s == 0``: each token's ``top_k`` experts are distinct and uniform.
+    ``zipf_s > 0``: every slot draws an expert independently with probability
+    ``~ rank**-zipf_s`` over a seeded rank order (hot experts; repeats allowed).
+    Then ``round(invalid_frac * T*top_k)`` random slots get an id outside
+    ``[0, E)`` (-1, E, or a large value), i.e. an expert not held here.
+    """
+    g = gen(seed)
+    if zipf_s == 0.0:
+        ids = distinct_topk(T, E, top_k, g) if top_k <= E else \
+            torch.randint(0, E, (T, top_k), generator=g, dtype=torch.int32)
+    else:
+        order = torch.randperm(E, generator=g)
+        p = torch.arange(1, E + 1, dtype=torch.float64) ** (-zipf_s)
+        draw = torch.multinomial(p, T * top_k, replacement=True, generator=g)
+        ids = order[draw].reshape(T, top_k).to(torch.int32)
+    n_bad = int(round(invalid_frac * T * top_k))
+    if n_bad:
+        flat = ids.reshape(-1)
+        where = torch.randperm(flat.numel(), generator=g)[:n_bad]
+        bad = torch.tensor([-1, E, E + 4096, -(1 << 30)], dtype=torch.int32)
+        flat[where] = bad[torch.randint(0, 4, (n_bad,), generator=g)]
+    return ids
 
 
 def softmax_weights(T: int, k: int, g: torch.Generator) -> torch.Tensor:

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert syms == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(L, s), s
-    assert L.mi_abi_version() == 3
+    assert L.mi_abi_version() == 4
 
 
 def _err(status):
@@ -111,3 +111,33 @@ def test_delta_validation():
     assert "rank" in _err(fin(FAKE, _lib.MI_F32, r=12))
     assert L.mi_moe_fc2_lora_delta_workspace_size(8192, 8, 64, 8, 16) > 8192 * 8 * 16 * 4
     assert L.mi_moe_fc2_lora_delta_workspace_size(8, 0, 4, 2, 8) == 0
+
+
+def test_route_permutation_and_permute_rows_validation():
+    L = _lib.lib()
+    ws = L.mi_moe_route_workspace_size(65536, 64)
+    assert ws == 64 * 64 * 4 + 256  # chunks of 1024 slots x experts x int32, plus slack
+    assert L.mi_moe_route_workspace_size(0, 64) == 256
+    assert L.mi_moe_route_workspace_size(-1, 64) == 0
+    rp = lambda **kw: L.mi_moe_route_permutation(*{**dict(
+        ids=FAKE, T=8192, k=8, E=64, indptr=FAKE, perm=FAKE, inv=NULL, ws=FAKE, wsb=ws,
+        stream=NULL), **kw}.values())
+    assert "num_experts must be in [1, 1024]" in _err(rp(E=1025))
+    assert "num_experts must be in [1, 1024]" in _err(rp(E=0))
+    assert "[0, 2^31)" in _err(rp(k=0))
+    assert "[0, 2^31)" in _err(rp(T=1 << 28))
+    assert "workspace needs" in _err(rp(wsb=ws - 1))
+    assert "workspace needs" in _err(rp(ws=NULL))
+    assert "m_indptr is null" in _err(rp(indptr=NULL))
+    assert "is null" in _err(rp(perm=NULL))
+    pr = lambda **kw: L.mi_moe_permute_rows(*{**dict(
+        x=FAKE, T=16, rb=8192, perm=FAKE, k=8, out=FAKE, rows=128, stream=NULL), **kw}.values())
+    assert "multiple of 16" in _err(pr(rb=8200))
+    assert "multiple of 16" in _err(pr(rb=0))
+    assert "16-byte aligned" in _err(pr(x=FAKE + 8))
+    assert "null pointer" in _err(pr(perm=NULL))
+    assert "out_rows" in _err(pr(rows=-1))
+    assert "[0, 2^31)" in _err(pr(k=0))
+    # nothing to copy: returns before touching the device
+    assert pr(T=0, x=NULL, perm=NULL, out=NULL) == 0
+    assert pr(rows=0, out=NULL) == 0
