@@ -62,3 +62,22 @@ def test_permute_rows():
     for p in range(m[-1]):
         assert np.array_equal(out[p], x[inv[p] // k])
     assert (out[m[-1]:] == 7.0).all()  # rows no slot maps to keep their values
+
+
+def test_hand_worked_example():
+    """Three tokens, top_k=2, E=3; slot 3's id 5 is not an expert held here.
+    Slots by expert, in slot order: e0 <- {1, 4}; e1 <- {0, 5}; e2 <- {2}."""
+    ids = np.array([[1, 0], [2, 5], [0, 1]])
+    m, perm, inv = route_permutation(ids, 3)
+    assert m.tolist() == [0, 2, 4, 5]
+    assert perm.tolist() == [2, 0, 4, -1, 1, 3]
+    assert inv.tolist() == [1, 4, 0, 5, 2, -1]
+    out = permute_rows(np.array([[10.0], [20.0], [30.0]]), perm, 2, np.zeros((6, 1)))
+    assert out[:, 0].tolist() == [10.0, 30.0, 10.0, 30.0, 20.0, 0.0]
+
+
+def test_one_expert_is_the_identity():
+    ids = np.zeros((17, 1), dtype=np.int64)
+    m, perm, inv = route_permutation(ids, 1)
+    assert m.tolist() == [0, 17]
+    assert perm.tolist() == list(range(17)) and inv.tolist() == list(range(17))
