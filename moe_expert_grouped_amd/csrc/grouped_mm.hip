@@ -281,6 +281,351 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large groups: 256-column tiles of 256 or 128 rows, four wavefronts of 128
+// rows each (one per SIMD), one tile per workgroup.
+//
+// Tiles.  Every expert's rows are cut into 256-row tiles; a last piece of at
+// most 128 rows becomes a 128-row tile instead, which takes about half the
+// time (at most 127 padded rows per expert instead of 255).  The 256-row tiles
+// come first in the walk and the 128-row ones after; each list, in grouped
+// order (GM_GROUP_M m-tiles sweep each n-panel together), is cut into 8
+// contiguous runs, one per XCD, so the XCDs get equal work and each keeps its
+// a and b panels in its own L2.
+//
+// K loop.  Per 64-wide K step every wavefront runs 4 sub-steps of
+// v_mfma_f32_32x32x16 blocks (4 x FN of them).  The fragments of sub-step s+1
+// are read from LDS while the MFMAs of sub-step s run (two fragment register
+// sets), so with one wavefront per SIMD the LDS latency stays hidden.  The K
+// step's one barrier sits before the last sub-step's MFMAs, and the next
+// stage's first fragments are read right after it, under those MFMAs.  Global
+// loads run GB_P K steps ahead in registers; the next stage is copied to the
+// other LDS buffer during sub-step 1.  LDS rows are padded to 72 elements
+// (144 bytes): the 32 rows of a fragment read and the 8 chunks of a row write
+// both spread over all banks.
+// ---------------------------------------------------------------------------
+constexpr int GB_BN = 256, GB_BK = 64, GB_P = 2;
+constexpr int GB_RS = GB_BK + 8;                 // padded LDS row (16-bit elements)
+constexpr int GB_STAGE = (256 + GB_BN) * GB_RS;  // elements per LDS stage (largest tile)
+
+// Device-side walk of m_indptr by wavefront 0: the clamped first row of every
+// expert (s_row0[E] = the end of the last one), the first 256-row tile
+// (s_full0) and the first 128-row tile (s_half0) of each expert.
+__device__ __forceinline__ void gb_walk(const int32_t* __restrict__ m_indptr, int m_rows, int E,
+                                        int* s_full0, int* s_half0, int* s_row0) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;
+  const int e0 = lane * per;
+  int nf = 0, nh = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int s = min(max(m_indptr[e], 0), m_rows);
+      const int t = min(max(m_indptr[e + 1], s), m_rows);
+      s_row0[e] = s;
+      const int q = (t - s) >> 8, r = (t - s) & 255;
+      nf += q + (r > 128);
+      nh += (r > 0 && r <= 128);
+    }
+  }
+  int incl_f = nf, incl_h = nh;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int vf = __shfl_up(incl_f, off, 64), vh = __shfl_up(incl_h, off, 64);
+    if (lane >= off) {
+      incl_f += vf;
+      incl_h += vh;
+    }
+  }
+  int run_f = incl_f - nf, run_h = incl_h - nh;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      s_full0[e] = run_f;
+      s_half0[e] = run_h;
+      const int s = s_row0[e];
+      const int t = min(max(m_indptr[e + 1], s), m_rows);
+      const int q = (t - s) >> 8, r = (t - s) & 255;
+      run_f += q + (r > 128);
+      run_h += (r > 0 && r <= 128);
+    }
+  }
+  if (lane == 63) {
+    s_full0[E] = incl_f;
+    s_half0[E] = incl_h;
+    s_row0[E] = min(max(m_indptr[E], 0), m_rows);
+  }
+}
+
+// m-tile and n-panel of linear index L in the grouped order of a list of
+// `count` m-tiles
+__device__ __forceinline__ void gb_order(long L, int count, int nt, int& mt, int& ni) {
+  const long span = static_cast<long>(GM_GROUP_M) * nt;
+  const int grp = static_cast<int>(L / span);
+  const int first = grp * GM_GROUP_M;
+  const int gsize = min(count - first, GM_GROUP_M);
+  const int in_grp = static_cast<int>(L - static_cast<long>(grp) * span);
+  mt = first + in_grp % gsize;
+  ni = in_grp / gsize;
+}
+
+// expert owning list entry mt: last e with pre[e] <= mt (pre non-decreasing,
+// pre[0] = 0 <= mt < pre[E])
+__device__ __forceinline__ int gb_owner(const int* pre, int E, int mt) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= mt) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// four consecutive output columns of one row: one buffer store at byte offset
+// `off`; a store past the descriptor's range is dropped
+template <typename OutT>
+__device__ __forceinline__ void bstore_out4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v);
+template <>
+__device__ __forceinline__ void bstore_out4<Bf16Out>(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                     f32x4 v) {
+  typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+  // hardware conversion: round to nearest even
+  const b4 h = __builtin_convertvector(v, b4);
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ void bstore_out4<_Float16>(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                      f32x4 v) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const h4 h = __builtin_convertvector(v, h4);
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ void bstore_out4<float>(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                   f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+
+// Instruction interleave of a sub-step: the NR LDS reads of the next
+// fragments go out between the first NR of its NM MFMAs, so they complete
+// under this sub-step.
+template <int NR, int NM>
+__device__ __forceinline__ void gb_interleave_reads() {
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+}
+// sub-step 1 also copies the next stage to LDS (NC writes) and refills its
+// register slot (NC global loads), spread over the remaining MFMAs
+template <int NR, int NM, int NC>
+__device__ __forceinline__ void gb_interleave_copy() {
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  }
+  constexpr int REST = NM - NR, PER = (NC + REST - 1) / REST;
+#pragma unroll
+  for (int i = 0; i < REST; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x200, PER, 0);  // LDS write
+    __builtin_amdgcn_sched_group_barrier(0x020, PER, 0);  // global load
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+  }
+}
+
+// One output tile: 256 rows (FN = 4: waves 2 x 2, 128 x 128 each) or 128 rows
+// (FN = 2: waves 1 x 4, 128 x 64 each), 256 columns.  `rows` (1..BM) of the
+// tile belong to the expert; the a descriptor covers only those, so rows past
+// them read as zero and their stores are dropped.
+template <int FN, bool F16, typename OutT>
+__device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
+                                        const uint16_t* __restrict__ b, OutT* __restrict__ out,
+                                        uint16_t* smem, int e, int m0, int rows, int n0, int k,
+                                        int n) {
+  constexpr int WN = FN == 4 ? 2 : 4;        // wavefronts along n
+  constexpr int BM = 128 * (4 / WN);         // tile rows
+  constexpr int CPT_A = BM / 32, CPT_B = 8;  // 16-byte chunks per thread per stage
+  constexpr int NR = 4 + FN, NM = 4 * FN;    // fragment reads and MFMAs per sub-step
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int r = lane & 31, h = lane >> 5;
+  const int KT = k / GB_BK;
+  const uint32_t kbytes = static_cast<uint32_t>(k) * 2;
+
+  const __amdgpu_buffer_rsrc_t ar = buf_rsrc(a + static_cast<long>(m0) * k, rows * kbytes);
+  const __amdgpu_buffer_rsrc_t br =
+      buf_rsrc(b + (static_cast<long>(e) * n + n0) * k, GB_BN * kbytes);
+
+  // staging: chunk c = tid + 256 i is row c/8 = tid/8 + 32 i, 16-byte chunk
+  // tid%8 of the stage
+  const uint32_t g_off = static_cast<uint32_t>(tid >> 3) * kbytes + (tid & 7) * 16;
+  const uint32_t g_step = 32 * kbytes;  // 32 rows
+  const int st_lds = (tid >> 3) * GB_RS + (tid & 7) * 8;
+  // fragments: lane (r, h) reads row r of each 32-row block, 16-byte chunk 2s+h
+  const int fa_base = (wm * 128 + r) * GB_RS + 8 * h;
+  const int fb_base = 256 * GB_RS + (wn * 32 * FN + r) * GB_RS + 8 * h;
+
+  f32x16 acc[4][FN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  struct Frag {
+    u32x4 a[4], b[FN];
+  };
+  u32x4 ra[GB_P][CPT_A], rb[GB_P][CPT_B];
+  auto gload = [&](int p, int kt) {
+    // stages past the end reload the last one: every step issues the same loads
+    const uint32_t so = static_cast<uint32_t>(min(kt, KT - 1)) * (GB_BK * 2);
+#pragma unroll
+    for (int i = 0; i < CPT_A; ++i) ra[p][i] = buf_ld128(ar, g_off + i * g_step, so);
+#pragma unroll
+    for (int i = 0; i < CPT_B; ++i) rb[p][i] = buf_ld128(br, g_off + i * g_step, so);
+  };
+  auto lstore = [&](int p, uint16_t* st) {
+#pragma unroll
+    for (int i = 0; i < CPT_A; ++i)
+      *reinterpret_cast<u32x4*>(st + st_lds + i * 32 * GB_RS) = ra[p][i];
+#pragma unroll
+    for (int i = 0; i < CPT_B; ++i)
+      *reinterpret_cast<u32x4*>(st + 256 * GB_RS + st_lds + i * 32 * GB_RS) = rb[p][i];
+  };
+  auto fload = [&](Frag& f, const uint16_t* st, int s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = *reinterpret_cast<const u32x4*>(st + fa_base + i * 32 * GB_RS + 16 * s);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      f.b[j] = *reinterpret_cast<const u32x4*>(st + fb_base + j * 32 * GB_RS + 16 * s);
+  };
+  // C[m][n] with m = output column (b row), n = output row (a row)
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<F16>(f.b[j], f.a[i], acc[i][j]);
+  };
+
+  Frag f0, f1;
+#pragma unroll
+  for (int p = 0; p < GB_P; ++p) {
+    gload(p, p);
+    __builtin_amdgcn_sched_barrier(0);  // slots in order: the loop's waits stay exact
+  }
+  lstore(0, smem);
+  gload(0, GB_P);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  fload(f0, smem, 0);
+
+  // one K step; `q` = register slot holding stage kt+1
+  auto kstep = [&](int kt, int q) {
+    uint16_t* st = smem + (kt & 1) * GB_STAGE;
+    uint16_t* nx = smem + ((kt & 1) ^ 1) * GB_STAGE;
+    fload(f1, st, 1);
+    mma(f0);
+    gb_interleave_reads<NR, NM>();
+    __builtin_amdgcn_sched_barrier(0);
+    fload(f0, st, 2);
+    lstore(q, nx);
+    gload(q, kt + 1 + GB_P);
+    mma(f1);
+    gb_interleave_copy<NR, NM, CPT_A + CPT_B>();
+    __builtin_amdgcn_sched_barrier(0);
+    fload(f1, st, 3);
+    mma(f0);
+    gb_interleave_reads<NR, NM>();
+    __builtin_amdgcn_sched_barrier(0);
+    // every wavefront's LDS work of this step is done: the next stage is
+    // complete and this one may be overwritten one step later
+    __syncthreads();
+    fload(f0, nx, 0);
+    mma(f1);
+    gb_interleave_reads<NR, NM>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The loop body is straight-line code (all MFMAs unconditional: rows past
+  // the group's end are zeros), so the compiler's wait counts stay exact.
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    kstep(kt, 1);
+    kstep(kt + 1, 0);
+  }
+  if (kt < KT) kstep(kt, 1);
+
+  if (wm * 128 >= rows) return;  // all of this wavefront's rows lie past the group's end
+  // acc[i][j][q]: tile row wm*128 + i*32 + r, column wn*32*FN + j*32 + 8*(q/4) + 4h + q%4.
+  const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(out + static_cast<long>(m0) * n,
+                                                static_cast<uint32_t>(rows) * n * sizeof(OutT));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t orow =
+        (static_cast<uint32_t>(wm * 128 + i * 32 + r) * n + n0 + wn * 32 * FN + 4 * h) *
+        sizeof(OutT);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                         acc[i][j][4 * g + 3]};
+        bstore_out4<OutT>(orsrc, orow + (j * 32 + 8 * g) * sizeof(OutT), v);
+      }
+    }
+  }
+}
+
+template <bool F16, typename OutT>
+__global__ __launch_bounds__(256, 1) void grouped_mm_big_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+    const int32_t* __restrict__ m_indptr, OutT* __restrict__ out, int m_rows, int k, int n,
+    int E) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * GB_STAGE];
+  __shared__ int s_full0[GM_MAX_EXPERTS + 1];
+  __shared__ int s_half0[GM_MAX_EXPERTS + 1];
+  __shared__ int s_row0[GM_MAX_EXPERTS + 1];
+
+  if ((threadIdx.x >> 6) == 0) gb_walk(m_indptr, m_rows, E, s_full0, s_half0, s_row0);
+  __syncthreads();
+
+  const int nt = n / GB_BN;
+  const int count_f = s_full0[E], count_h = s_half0[E];
+  const long total_f = static_cast<long>(count_f) * nt, total_h = static_cast<long>(count_h) * nt;
+  // The grid is an upper bound on the tiles; the dispatcher deals workgroup
+  // ids to the 8 XCDs in turn.  An XCD's first run_f workgroups take its run
+  // of the 256-row tiles, the next run_h its run of the 128-row tiles.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const long run_f = (total_f + 7) / 8, run_h = (total_h + 7) / 8;
+  if (slot < run_f) {
+    const long L = xcd * run_f + slot;
+    if (L >= total_f) return;
+    int mt, ni;
+    gb_order(L, count_f, nt, mt, ni);
+    const int e = __builtin_amdgcn_readfirstlane(gb_owner(s_full0, E, mt));
+    const int m0 = __builtin_amdgcn_readfirstlane(s_row0[e] + (mt - s_full0[e]) * 256);
+    const int end = max(s_row0[e + 1], s_row0[e]);
+    const int rows = __builtin_amdgcn_readfirstlane(min(end - m0, 256));
+    gb_tile<4, F16, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n);
+  } else {
+    const long L = xcd * run_h + (slot - run_f);
+    if (slot - run_f >= run_h || L >= total_h) return;
+    int mt, ni;
+    gb_order(L, count_h, nt, mt, ni);
+    const int e = __builtin_amdgcn_readfirstlane(gb_owner(s_half0, E, mt));
+    // the expert's last piece: after its 256-row tiles
+    const int m0 = __builtin_amdgcn_readfirstlane(s_row0[e] + (s_full0[e + 1] - s_full0[e]) * 256);
+    const int end = max(s_row0[e + 1], s_row0[e]);
+    const int rows = __builtin_amdgcn_readfirstlane(end - m0);
+    gb_tile<2, F16, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n);
+  }
+}
+
 int num_cus() {
   static int cached[64] = {0};
   int dev = 0;
@@ -313,6 +658,24 @@ mi_status launch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b
 }
 
 template <bool F16, typename OutT>
+mi_status launch_grouped_big(const void* a, int64_t m_rows, int64_t k, const void* b, int64_t batch,
+                             int64_t n, const int32_t* m_indptr, void* out, hipStream_t stream) {
+  // one workgroup per tile of the upper bound (the real count is known on the
+  // device only); each XCD's run of the real tiles fits in its G/8 ids
+  const long ub_tiles = ((m_rows + 255) / 256 + batch) * (n / GB_BN);
+  const long G = ((ub_tiles + 7) / 8 + 2) * 8;
+  MI_REQUIRE(G < (1L << 31), "grouped_mm_bf16: problem too large");
+  MI_REQUIRE(static_cast<uint64_t>(k) * 2 * GB_BN < (1ULL << 32) &&
+                 static_cast<uint64_t>(n) * 256 * sizeof(OutT) < (1ULL << 32),
+             "grouped_mm_bf16: n or k too large for 256-row tiles");
+  hipLaunchKernelGGL((grouped_mm_big_kernel<F16, OutT>), dim3(G), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), m_indptr,
+                     static_cast<OutT*>(out), static_cast<int>(m_rows), static_cast<int>(k),
+                     static_cast<int>(n), static_cast<int>(batch));
+  return launch_status("grouped_mm_bf16");
+}
+
+template <bool F16, typename OutT>
 mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b,
                            int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
                            hipStream_t stream) {
@@ -320,9 +683,7 @@ mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void*
   // large average groups take 256x256 tiles; smaller groups stream b from HBM
   // and take 64x64 tiles, two workgroups per CU, with 4 K steps in flight.
   const int64_t avg = m_rows / batch;
-  if (avg >= 192)
-    return launch_grouped<256, 256, 64, 4, 2, 1, F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
-                                                   1);
+  if (avg >= 192) return launch_grouped_big<F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream);
   return launch_grouped<64, 64, 64, 2, 2, 4, F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
 }
 

@@ -34,6 +34,9 @@ def test_tiny_moe_fc2(gpu):
     ((0, 1, 17, 128, 0, 255), 256, 128),          # small groups: 64x64 tiles
     ((100, 0, 150, 177, 0, 229), 512, 192),       # medium: 64x64 tiles, several per group
     ((300, 0, 513, 1, 256, 0, 390), 256, 256),    # large: 256x256 tiles, ragged tails
+    # large, odd K-step count: last pieces of 128 / 129 / 255 / 1 / 0 / 128 / 88 / 232 rows
+    # (128-row tiles for pieces up to 128 rows, 256-row tiles above)
+    ((128, 129, 255, 257, 0, 384, 600, 1000), 512, 192),
 ])
 def test_integer_probe_bitwise(gpu, counts, n, k):
     case = synth.grouped_int_probe(counts=counts, n=n, k=k)
