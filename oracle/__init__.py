@@ -21,6 +21,8 @@ passage of the source pages it follows (cited by page title and section):
 - routing output -> expert-sorted permutation and permuted rows
   (``expanded_idx_to_permuted_idx`` and ``m_indptr`` parameters) ->
   :mod:`oracle.permute`
+- NVFP4 grouped GEMM (``grouped_mm_bf16`` formula with the
+  ``mm_nvfp4_lora`` operand format) -> :mod:`oracle.nvfp4_grouped`
 
 Inputs are numpy arrays; bf16 tensors are passed as their uint16 bit patterns.
 
@@ -33,3 +35,4 @@ convention and are pinned only to that convention (two independent codings
 and hand-worked offsets).
 """
 from . import formats, grouped_mm, lora_delta, nvfp4, fold, finalize, permute  # noqa: F401
+from . import nvfp4_grouped  # noqa: F401

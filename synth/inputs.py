@@ -38,6 +38,8 @@ __all__ = [
     "delta_int_probe",
     "nvfp4_lora_case",
     "nvfp4_probe",
+    "Nvfp4GroupedCase",
+    "nvfp4_grouped_case",
 ]
 
 
@@ -435,3 +437,47 @@ def nvfp4_probe(kind: str, seed: int = 103, M=128, N=256, K=256, r=16) -> Nvfp4C
         raise ValueError(kind)
     return Nvfp4Case(f"nvfp4-probe-{kind} M={M} N={N} K={K}", a, b, a_sf, b_sf, alpha, d,
                      lora_b, lora_scale, bias, K)
+
+
+@dataclass
+class Nvfp4GroupedCase:
+    name: str
+    a: torch.Tensor          # uint8 [cum_m, K/2]
+    a_sf: torch.Tensor       # uint8, 128x4 layout over cum_m rows
+    b: torch.Tensor          # uint8 [E, N, K/2]
+    b_sf: torch.Tensor       # uint8, E consecutive 128x4 buffers of [N, K/16]
+    alpha: torch.Tensor      # fp32 [E]
+    m_indptr: torch.Tensor   # int32 [E+1]
+    k: int
+
+
+def nvfp4_grouped_case(seed: int = 6, device="cpu", counts=None, E=128, T=4096, top_k=8,
+                       n=7168, k=2048, exact=False) -> Nvfp4GroupedCase:
+    """NVFP4 grouped GEMM operands.  Default: the skewed MoE FC2 routing of
+    ``grouped_zipf`` (E=128, cum_m=32768, Zipf 1.1 counts with 8 empty
+    experts) with FP4 weights of n=7168, k=2048.  Code bytes uniform over
+    0..255; scale bytes uniform over 0x28..0x48 (0.25..4); alpha per expert
+    uniform over 0.005..0.02.  ``exact``: all scales 1.0 and alpha a power of
+    two per expert, so every fp32 sum is exact."""
+    if counts is None:
+        counts = zipf_counts(T * top_k, E, 8, 1.1, T, 3)
+    counts = np.asarray(counts, dtype=np.int64)
+    E = len(counts)
+    m_indptr = torch.zeros(E + 1, dtype=torch.int32)
+    m_indptr[1:] = torch.from_numpy(np.cumsum(counts)).to(torch.int32)
+    cum = int(m_indptr[-1])
+    g = gen(seed, device)
+    a = torch.randint(0, 256, (cum, k // 2), generator=g, device=device).to(torch.uint8)
+    b = torch.randint(0, 256, (E, n, k // 2), generator=g, device=device).to(torch.uint8)
+    a_bytes, b_bytes = sf_buffer_bytes(cum, k), E * sf_buffer_bytes(n, k)
+    if exact:
+        a_sf = torch.full((a_bytes,), 0x38, dtype=torch.uint8, device=device)
+        b_sf = torch.full((b_bytes,), 0x38, dtype=torch.uint8, device=device)
+        ex = torch.randint(-3, 2, (E,), generator=g, device=device)
+        alpha = torch.pow(2.0, ex.to(torch.float32))
+    else:
+        a_sf = _scale_codes(a_bytes, 0x28, 0x48, g, device)
+        b_sf = _scale_codes(b_bytes, 0x28, 0x48, g, device)
+        alpha = 0.005 + 0.015 * torch.rand(E, generator=g, device=device, dtype=torch.float32)
+    return Nvfp4GroupedCase(f"nvfp4-grouped E={E} cum_m={cum} n={n} k={k}", a, a_sf, b, b_sf,
+                            alpha.to(torch.float32), m_indptr.to(device), k)
