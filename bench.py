@@ -45,8 +45,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling aid); "
                    "'copy_probe' (not part of the step) is a 512 MiB fp32 negation (read + write) used to "
-                   "calibrate the HBM byte counters; 'finalize' and 'permute' time the ops "
-                   "outside the step")
+                   "calibrate the HBM byte counters; 'finalize', 'permute' and 'nvfp4_grouped' time "
+                   "the ops outside the step")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                    "'--only nvfp4_raw,copy_probe' into the committed traffic summary")
@@ -320,6 +320,28 @@ def main():
             pms, 2.0 * dc.H * (dc.T + nslot) + 4.0 * nslot,
             "token rows bf16 [8192, 4096] -> permuted rows [65536, 4096] (each token row read "
             "once, written top_k times)")
+    if not only or "nvfp4_grouped" in only:
+        # NVFP4 grouped GEMM on the skewed MoE FC2 routing (E=128, cum_m=32768,
+        # Zipf 1.1 counts, 8 empty experts) with FP4 weights n=7168, k=2048
+        ng = synth.nvfp4_grouped_case(device=dev)
+        ngo = torch.empty((ng.a.shape[0], ng.b.shape[1]), dtype=torch.bfloat16, device=dev)
+        gms = time_alone(lambda: mi.grouped_mm_nvfp4(ng.a, ng.a_sf, ng.b, ng.b_sf, ng.m_indptr,
+                                                     ng.alpha, out=ngo))
+        cnts = np.diff(ng.m_indptr.cpu().numpy())
+        nn, kk = ng.b.shape[1], ng.k
+        gflops = 2.0 * ng.a.shape[0] * nn * kk
+        per_e = ng.b_sf.numel() // ng.b.shape[0]
+        gbytes = ng.a.numel() + ng.a_sf.numel() + (nn * kk / 2 + per_e) * int((cnts > 0).sum()) + \
+            2.0 * ng.a.shape[0] * nn + 4.0 * (len(cnts) + 1) + 4.0 * len(cnts)
+        sec = gms * 1e-3
+        extra["nvfp4_grouped"] = {
+            "ms": round(gms, 5), "tflops": round(gflops / sec / 1e12, 2),
+            "frac_mfma_peak": round(gflops / sec / 1e12 / PEAK_MFMA_TFLOPS, 4),
+            "gbps": round(gbytes / sec / 1e9, 1), "algorithmic_flops": gflops,
+            "algorithmic_bytes": gbytes,
+            "note": "NVFP4 grouped GEMM, E=128 Zipf(1.1) routing of 4096 tokens x top-8 "
+                    "(cum_m=32768), n=7168, k=2048, per-expert alpha, bf16 out; the fp16 MFMA "
+                    "peak (2516.6 TFLOP/s) is the denominator"}
     extra = extra or None
 
     cpu = None

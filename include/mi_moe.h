@@ -12,6 +12,8 @@
  *   - mi_moe_route_permutation  routing output -> expert-sorted permutation
  *                             (bgmv_moe_gemm2_lora_delta and grouped_mm_bf16, parameters)
  *   - mi_moe_permute_rows     token rows -> permuted rows (the FC1 input)
+ *   - mi_grouped_mm_nvfp4     ragged grouped GEMM with NVFP4 operands
+ *                             (grouped_mm_bf16 formula, mm_nvfp4_lora operand format)
  *   - mi_mm_nvfp4_lora        NVFP4 GEMM with an fp32 LoRA epilogue, raw and prepared
  *                             (flashinfer.gemm.mm_nvfp4_lora, formula and the two bullets)
  *   - mi_prepare_lora_fold    the prepared-path fold
@@ -241,6 +243,33 @@ MI_API mi_status mi_mm_nvfp4_lora(const uint8_t* a, const uint8_t* b,
                            const void* lora_b, const float* lora_scale,
                            const void* b_folded, const uint32_t* fold_flags,
                            const void* bias, void* out, void* stream);
+
+/*
+ * NVFP4 grouped GEMM: the ragged per-expert walk of flashinfer.grouped_mm.
+ * grouped_mm_bf16 (formula) with FP4 expert weights in the operand format of
+ * flashinfer.gemm.mm_nvfp4_lora (parameters a, b, a_sf, b_sf, alpha) -- the
+ * weight format the FP4 fused-MoE page names for its experts:
+ *   out[m_indptr[e]:m_indptr[e+1]] = alpha[e] * dequant(a[...]) @ dequant(b[e])^T
+ * acc in fp32, one rounding to out_dtype; rows outside [m_indptr[0],
+ * m_indptr[batch]) are not written.
+ *   a         uint8 [m_rows, k/2] codes (element 2i in the low nibble), device
+ *   a_sf      UE4M3 scales of a in the 128x4 layout over all m_rows rows (rows
+ *             padded to 128), a_sf_bytes its size (larger is fine)
+ *   b         uint8 [batch, n, k/2] codes
+ *   b_sf      batch consecutive 128x4 scale buffers, each for [n, k/16] scales
+ *             (ceil(n/128) * ceil(k/64) * 512 bytes apiece); b_sf_bytes the total
+ *   m_indptr  int32 [batch + 1], device, non-decreasing (clamped into [0, m_rows])
+ *   alpha     fp32 [batch], device: each expert's base scale
+ *   out       out_dtype (MI_BF16 or MI_F32) [m_rows, n]
+ * Requirements: 1 <= batch <= 1024, n % 256 == 0, k % 256 == 0 (k >= 256),
+ * a and b 16-byte aligned, scale buffers 4-byte aligned, a's codes, a's scales
+ * and one expert's codes below 4 GiB each.  m_rows == 0 is a no-op.
+ */
+MI_API mi_status mi_grouped_mm_nvfp4(const uint8_t* a, const uint8_t* a_sf, size_t a_sf_bytes,
+                              int64_t m_rows, int64_t k, const uint8_t* b, const uint8_t* b_sf,
+                              size_t b_sf_bytes, int64_t batch, int64_t n,
+                              const int32_t* m_indptr, const float* alpha, void* out,
+                              mi_dtype out_dtype, void* stream);
 
 /*
  * The prepared-path fold (flashinfer.gemm.prepare_nvfp4_lora_adapter):

@@ -25,6 +25,7 @@ EXPORTS = [
     "mi_moe_route_permutation",
     "mi_moe_permute_rows",
     "mi_mm_nvfp4_lora",
+    "mi_grouped_mm_nvfp4",
     "mi_prepare_lora_fold",
     "mi_nvfp4_dequant_bf16",
 ]
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.mi_mm_nvfp4_lora.restype = I32
         L.mi_mm_nvfp4_lora.argtypes = [P, P, P, SZ, P, SZ, P, I64, I64, I64, P, I64, P, P, P, P,
                                        P, P, P]
+        L.mi_grouped_mm_nvfp4.restype = I32
+        L.mi_grouped_mm_nvfp4.argtypes = [P, P, SZ, I64, I64, P, P, SZ, I64, I64, P, P, P, I32, P]
         L.mi_prepare_lora_fold.restype = I32
         L.mi_prepare_lora_fold.argtypes = [P, I64, I64, P, P, P, P, P]
         L.mi_nvfp4_dequant_bf16.restype = I32

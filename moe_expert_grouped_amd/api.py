@@ -28,6 +28,7 @@ __all__ = [
     "delta_workspace_bytes",
     "fill_w_ptr",
     "mm_nvfp4_lora",
+    "grouped_mm_nvfp4",
     "prepare_nvfp4_lora_adapter",
     "PreparedNvFp4LoraAdapter",
     "StaleAdapterError",
@@ -397,6 +398,45 @@ def mm_nvfp4_lora(a: torch.Tensor, b: torch.Tensor, a_sf: torch.Tensor, b_sf: to
                                       b_sf.numel(), _ptr(alpha), M, N, K, d_ptr, rank, lb_ptr,
                                       ls_ptr, bf_ptr, ff_ptr, _ptr(bias), _ptr(out),
                                       _stream(a.device)))
+    return out
+
+
+def grouped_mm_nvfp4(a: torch.Tensor, a_sf: torch.Tensor, b: torch.Tensor, b_sf: torch.Tensor,
+                     m_indptr: torch.Tensor, alpha: torch.Tensor,
+                     out: torch.Tensor | None = None,
+                     out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """``out[m_indptr[e]:m_indptr[e+1]] = alpha[e] * dequant(a[...]) @ dequant(b[e])^T``.
+
+    ``a`` uint8 ``(cum_m, k/2)`` with its 128x4 scales ``a_sf`` over all
+    rows; ``b`` uint8 ``(batch, n, k/2)`` with ``b_sf`` holding one 128x4
+    scale buffer per expert; ``alpha`` fp32 ``(batch,)``; ``m_indptr`` int32
+    ``(batch+1,)`` read on the device.  Rows outside the groups of a
+    caller-provided ``out`` are untouched (a fresh ``out`` is zero-filled there).
+    """
+    _need(a.dtype == torch.uint8 and b.dtype == torch.uint8 and a.dim() == 2 and b.dim() == 3
+          and b.shape[2] == a.shape[1],
+          "grouped_mm_nvfp4: a must be uint8 (cum_m, k/2) and b uint8 (batch_size, n, k/2)")
+    _need(a_sf.dtype == torch.uint8 and b_sf.dtype == torch.uint8,
+          "grouped_mm_nvfp4: scale buffers must be uint8")
+    _need(m_indptr.dtype == torch.int32 and m_indptr.shape == (b.shape[0] + 1,),
+          "grouped_mm_nvfp4: m_indptr must be int32 of shape (batch_size + 1,)")
+    _need(alpha.dtype == torch.float32 and alpha.numel() == b.shape[0],
+          "grouped_mm_nvfp4: alpha must be float32 with one value per expert")
+    _need(out_dtype in (torch.bfloat16, torch.float32),
+          "grouped_mm_nvfp4: out_dtype must be bfloat16 or float32")
+    _need_cuda("grouped_mm_nvfp4", a, a_sf, b, b_sf, m_indptr, alpha, out)
+    cum_m, k = a.shape[0], a.shape[1] * 2
+    n = b.shape[1]
+    a, b, a_sf, b_sf = a.contiguous(), b.contiguous(), a_sf.contiguous(), b_sf.contiguous()
+    m_indptr, alpha = m_indptr.contiguous(), alpha.contiguous()
+    if out is None:
+        out = torch.zeros((cum_m, n), dtype=out_dtype, device=a.device)
+    _need(out.shape == (cum_m, n) and out.dtype == out_dtype and out.is_contiguous(),
+          "grouped_mm_nvfp4: out must be a contiguous (cum_m, n) tensor of out_dtype")
+    check(_lib.lib().mi_grouped_mm_nvfp4(
+        _ptr(a), _ptr(a_sf), a_sf.numel(), cum_m, k, _ptr(b), _ptr(b_sf), b_sf.numel(),
+        b.shape[0], n, _ptr(m_indptr), _ptr(alpha), _ptr(out), _DT[out_dtype],
+        _stream(a.device)))
     return out
 
 

@@ -103,81 +103,39 @@ struct NvStage {
   uint32_t sa[4], sb[4];
 };
 
-// One wavefront computes a 128 x 128 block as 4 x 4 v_mfma_f32_32x32x16_f16
-// tiles; the accumulators (256 floats a lane) live in AGPRs.  There is no LDS:
-// the sum over K is order-free, so inside every 128-wide K stage lane half h
-// (lane / 32) takes the 64 consecutive elements [64h, 64h + 64) and MFMA step
-// s (0..7) consumes elements 64h + 8s .. +7 from both halves -- A and B use
-// the same assignment.  Each lane therefore reads its row's codes as 32
-// contiguous bytes and decodes them straight into MFMA operands.  Every A and
-// B row is decoded by the two wavefronts that share it.
-__global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
-  constexpr int WTM = NV_BM / NV_WM, WTN = NV_BN / NV_WN;  // 128 x 128
-  constexpr int FM = WTM / 32, FN = WTN / 32;               // 4 x 4
+// Operands of one wavefront's 128 x 128 block: buffer descriptors of codes
+// and scales, and the lane's byte offsets of its 4 A and 4 B fragment rows
+// (codes: the row's first byte plus 32 * lane half; scales: its 128x4 word).
+struct NvOps {
+  __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+  uint32_t oa[4], ob[4], osa[4], osb[4];
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / NV_WN, wn = wave % NV_WN;
-
-  // ---- tile order: XCD-contiguous runs, GROUP_M m-tiles per n sweep ----
-  const int mt = (p.m + NV_BM - 1) / NV_BM, ntile = (p.n + NV_BN - 1) / NV_BN;
-  const int total = mt * ntile;
-  const int G = gridDim.x;  // == total rounded up to a multiple of 8
-  const int L = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  if (L >= total) return;
-  const int span = NV_GROUP_M * ntile;
-  const int grp = L / span, first = grp * NV_GROUP_M;
-  const int gsize = min(mt - first, NV_GROUP_M);
-  const int in_grp = L - grp * span;
-  const int m0 = (first + in_grp % gsize) * NV_BM;
-  const int n0 = (in_grp / gsize) * NV_BN;
-
-  // ---- per-lane byte offsets (codes and scales), rows clamped into range ----
-  const int r32 = lane & 31, h = lane >> 5;
-  const uint32_t kb = static_cast<uint32_t>(p.k) / 2;  // code bytes per row
-  const int nct = (p.k / 16 + 3) / 4;                   // 128x4 scale tiles along K
-  const __amdgpu_buffer_rsrc_t ra = buf_rsrc(p.a, static_cast<uint32_t>(p.m) * kb);
-  const __amdgpu_buffer_rsrc_t rb = buf_rsrc(p.b, static_cast<uint32_t>(p.n) * kb);
-  const __amdgpu_buffer_rsrc_t rsa =
-      buf_rsrc(p.a_sf, static_cast<uint32_t>((p.m + 127) / 128) * nct * 512);
-  const __amdgpu_buffer_rsrc_t rsb =
-      buf_rsrc(p.b_sf, static_cast<uint32_t>((p.n + 127) / 128) * nct * 512);
-  uint32_t oa[FM], ob[FN], osa[FM], osb[FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int row = min(m0 + wm * WTM + i * 32 + r32, p.m - 1);
-    oa[i] = static_cast<uint32_t>(row) * kb + h * 32;
-    osa[i] = static_cast<uint32_t>(sf_tile_word(row, h, nct));
-  }
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int row = min(n0 + wn * WTN + j * 32 + r32, p.n - 1);
-    ob[j] = static_cast<uint32_t>(row) * kb + h * 32;
-    osb[j] = static_cast<uint32_t>(sf_tile_word(row, h, nct));
-  }
-
-  f32x16 acc[FM][FN];
+// The K loop of one wavefront (NKC stages of 128, NKC even): acc = dequant(A
+// rows) x dequant(B rows)^T in fp32.
+__device__ __forceinline__ void nv_kloop(f32x16 (&acc)[4][4], const NvOps& op, int NKC) {
+  constexpr int FM = 4, FN = 4;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
   // stage kc: codes at byte kc*64 of the row, scales in scale tile 2*kc + h
   auto load = [&](NvStage& st, int kc) {
     const uint32_t co = static_cast<uint32_t>(kc) * (NV_KC / 2);
     const uint32_t so = static_cast<uint32_t>(kc) * 1024;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      st.a[i][0] = buf_ld128(ra, oa[i], co);
-      st.a[i][1] = buf_ld128(ra, oa[i] + 16, co);
-      st.sa[i] = buf_ld32(rsa, osa[i], so);
+      st.a[i][0] = buf_ld128(op.ra, op.oa[i], co);
+      st.a[i][1] = buf_ld128(op.ra, op.oa[i] + 16, co);
+      st.sa[i] = buf_ld32(op.rsa, op.osa[i], so);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      st.b[j][0] = buf_ld128(rb, ob[j], co);
-      st.b[j][1] = buf_ld128(rb, ob[j] + 16, co);
-      st.sb[j] = buf_ld32(rsb, osb[j], so);
+      st.b[j][0] = buf_ld128(op.rb, op.ob[j], co);
+      st.b[j][1] = buf_ld128(op.rb, op.ob[j] + 16, co);
+      st.sb[j] = buf_ld32(op.rsb, op.osb[j], so);
     }
   };
   auto compute = [&](const NvStage& st) {
@@ -228,7 +186,6 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
 
   // K / 128 is even (K % 256 == 0): two stages per trip, the refill index is
   // clamped so every trip issues the same loads
-  const int NKC = p.k / NV_KC;
   NvStage s0, s1;
   load(s0, 0);
   for (int kc = 0; kc < NKC; kc += 2) {
@@ -242,6 +199,61 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
     compute(s1);
     __builtin_amdgcn_sched_barrier(0);
   }
+
+}
+
+// One wavefront computes a 128 x 128 block as 4 x 4 v_mfma_f32_32x32x16_f16
+// tiles; the accumulators (256 floats a lane) live in AGPRs.  There is no LDS:
+// the sum over K is order-free, so inside every 128-wide K stage lane half h
+// (lane / 32) takes the 64 consecutive elements [64h, 64h + 64) and MFMA step
+// s (0..7) consumes elements 64h + 8s .. +7 from both halves -- A and B use
+// the same assignment.  Each lane therefore reads its row's codes as 32
+// contiguous bytes and decodes them straight into MFMA operands.  Every A and
+// B row is decoded by the two wavefronts that share it.
+__global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
+  constexpr int WTM = NV_BM / NV_WM, WTN = NV_BN / NV_WN;  // 128 x 128
+  constexpr int FM = WTM / 32, FN = WTN / 32;               // 4 x 4
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NV_WN, wn = wave % NV_WN;
+
+  // ---- tile order: XCD-contiguous runs, GROUP_M m-tiles per n sweep ----
+  const int mt = (p.m + NV_BM - 1) / NV_BM, ntile = (p.n + NV_BN - 1) / NV_BN;
+  const int total = mt * ntile;
+  const int G = gridDim.x;  // == total rounded up to a multiple of 8
+  const int L = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  if (L >= total) return;
+  const int span = NV_GROUP_M * ntile;
+  const int grp = L / span, first = grp * NV_GROUP_M;
+  const int gsize = min(mt - first, NV_GROUP_M);
+  const int in_grp = L - grp * span;
+  const int m0 = (first + in_grp % gsize) * NV_BM;
+  const int n0 = (in_grp / gsize) * NV_BN;
+
+  // ---- per-lane byte offsets (codes and scales), rows clamped into range ----
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t kb = static_cast<uint32_t>(p.k) / 2;  // code bytes per row
+  const int nct = (p.k / 16 + 3) / 4;                   // 128x4 scale tiles along K
+  NvOps op;
+  op.ra = buf_rsrc(p.a, static_cast<uint32_t>(p.m) * kb);
+  op.rb = buf_rsrc(p.b, static_cast<uint32_t>(p.n) * kb);
+  op.rsa = buf_rsrc(p.a_sf, static_cast<uint32_t>((p.m + 127) / 128) * nct * 512);
+  op.rsb = buf_rsrc(p.b_sf, static_cast<uint32_t>((p.n + 127) / 128) * nct * 512);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int row = min(m0 + wm * WTM + i * 32 + r32, p.m - 1);
+    op.oa[i] = static_cast<uint32_t>(row) * kb + h * 32;
+    op.osa[i] = static_cast<uint32_t>(sf_tile_word(row, h, nct));
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int row = min(n0 + wn * WTN + j * 32 + r32, p.n - 1);
+    op.ob[j] = static_cast<uint32_t>(row) * kb + h * 32;
+    op.osb[j] = static_cast<uint32_t>(sf_tile_word(row, h, nct));
+  }
+
+  f32x16 acc[FM][FN];
+  nv_kloop(acc, op, p.k / NV_KC);
 
   // ---- epilogue ----
   const float alpha = p.alpha[0];
@@ -310,6 +322,182 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
             p.out[static_cast<long>(row) * p.n + col] = static_cast<uint16_t>(f32_to_bf16_rne(v));
           }
         }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 grouped GEMM: the ragged per-expert walk with FP4 expert weights
+//   out[m_indptr[e]:m_indptr[e+1]] = alpha[e] * dequant(a[...]) @ dequant(b[e])^T
+// (flashinfer.grouped_mm.grouped_mm_bf16, formula, with the operand format of
+// flashinfer.gemm.mm_nvfp4_lora).  Same wavefront blocks and K loop as above;
+// the tiles are cut per expert from a device-side scan of m_indptr (none
+// padded in memory): 256-row tiles, and a 128 x 512 tile for a last piece of
+// at most 128 rows, so an expert pads at most 127 rows.
+// ---------------------------------------------------------------------------
+constexpr int NVG_MAX_EXPERTS = 1024;
+
+template <typename OutT>
+struct NvgArgs {
+  const uint8_t* a;
+  const uint8_t* a_sf;
+  const uint8_t* b;
+  const uint8_t* b_sf;
+  const int32_t* m_indptr;
+  const float* alpha;  // [E]
+  OutT* out;
+  int m_rows, n, k, E;
+  uint32_t b_sf_per;  // bytes of one expert's scale buffer
+};
+
+__device__ __forceinline__ void nvg_store(uint16_t* p, float v) {
+  *p = static_cast<uint16_t>(f32_to_bf16_rne(v));
+}
+__device__ __forceinline__ void nvg_store(float* p, float v) { *p = v; }
+
+template <typename OutT>
+__global__ __launch_bounds__(NV_NT, 1) void nvfp4_grouped_kernel(NvgArgs<OutT> p) {
+  constexpr int FM = 4, FN = 4;                  // 32x32 blocks per wavefront (128 x 128)
+  __shared__ int s_full0[NVG_MAX_EXPERTS + 1];  // first 256-row tile of each expert
+  __shared__ int s_half0[NVG_MAX_EXPERTS + 1];  // first 128-row tile of each expert
+  __shared__ int s_row0[NVG_MAX_EXPERTS + 1];   // clamped first row (s_row0[E]: the end)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = p.E;
+  // 128-row tiles (for an expert's last piece of at most 128 rows) span 512
+  // columns, so every wavefront keeps its 128 x 128 block; they need n % 512 == 0
+  const bool halves = (p.n & 511) == 0;
+
+  // ---- device-side walk of m_indptr (wavefront 0): per expert, the number of
+  // 256-row tiles and whether its last piece is a 128-row tile ----
+  auto pieces = [&](int len, int& nf, int& nh) {
+    const int q = len >> 8, r = len & 255;
+    const bool h = halves && r > 0 && r <= 128;
+    nf = q + (r > 0 && !h);
+    nh = h;
+  };
+  if (wave == 0) {
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    int lf = 0, lh = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < E) {
+        const int s = min(max(p.m_indptr[e], 0), p.m_rows);
+        const int t = min(max(p.m_indptr[e + 1], s), p.m_rows);
+        s_row0[e] = s;
+        int nf, nh;
+        pieces(t - s, nf, nh);
+        lf += nf;
+        lh += nh;
+      }
+    }
+    int inf = lf, inh = lh;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int vf = __shfl_up(inf, off, 64), vh = __shfl_up(inh, off, 64);
+      if (lane >= off) {
+        inf += vf;
+        inh += vh;
+      }
+    }
+    int rf = inf - lf, rh = inh - lh;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < E) {
+        s_full0[e] = rf;
+        s_half0[e] = rh;
+        const int s = s_row0[e];
+        const int t = min(max(p.m_indptr[e + 1], s), p.m_rows);
+        int nf, nh;
+        pieces(t - s, nf, nh);
+        rf += nf;
+        rh += nh;
+      }
+    }
+    if (lane == 63) {
+      s_full0[E] = inf;
+      s_half0[E] = inh;
+      s_row0[E] = min(max(p.m_indptr[E], 0), p.m_rows);
+    }
+  }
+  __syncthreads();
+
+  // ---- tile of this workgroup.  The 256-row tiles (256-column panels) come
+  // first, then the 128-row ones (512-column panels); each list in grouped
+  // order is cut into 8 contiguous runs, one per XCD: an XCD's first run_f
+  // workgroups take its run of the first list, the next run_h its run of the
+  // second ----
+  const int cnt_f = s_full0[E], cnt_h = s_half0[E];
+  const int nt_f = p.n / NV_BN, nt_h = p.n / (2 * NV_BN);
+  const long total_f = static_cast<long>(cnt_f) * nt_f, total_h = static_cast<long>(cnt_h) * nt_h;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const long run_f = (total_f + 7) / 8, run_h = (total_h + 7) / 8;
+  const bool half = slot >= run_f;
+  const long L = half ? xcd * run_h + (slot - run_f) : xcd * run_f + slot;
+  if (half ? (slot - run_f >= run_h || L >= total_h) : L >= total_f) return;
+  const int cnt = half ? cnt_h : cnt_f, nt = half ? nt_h : nt_f;
+  const long span = static_cast<long>(NV_GROUP_M) * nt;
+  const int grp = static_cast<int>(L / span), first = grp * NV_GROUP_M;
+  const int gsize = min(cnt - first, NV_GROUP_M);
+  const int in_grp = static_cast<int>(L - grp * span);
+  const int mt = first + in_grp % gsize, ni = in_grp / gsize;
+  const int* pre = half ? s_half0 : s_full0;
+  int lo = 0, hi = E;  // expert of list entry mt: pre[lo] <= mt < pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= mt) lo = mid; else hi = mid;
+  }
+  const int e = __builtin_amdgcn_readfirstlane(lo);
+  // a 128-row tile is the expert's last piece, after its 256-row tiles
+  const int m0 = __builtin_amdgcn_readfirstlane(
+      s_row0[e] + (half ? s_full0[e + 1] - s_full0[e] : mt - s_full0[e]) * NV_BM);
+  const int m_end = __builtin_amdgcn_readfirstlane(max(s_row0[e + 1], s_row0[e]));
+  // wavefront block: rows m0 + wm*128, columns n0 + wn*128
+  const int wm = half ? 0 : wave / NV_WN, wn = half ? wave : wave % NV_WN;
+  const int n0 = ni * (half ? 2 * NV_BN : NV_BN);
+
+  // ---- operands: a rows clamped into the expert's rows; b, b_sf of expert e ----
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t kb = static_cast<uint32_t>(p.k) / 2;
+  const int nct = (p.k / 16 + 3) / 4;
+  NvOps op;
+  op.ra = buf_rsrc(p.a, static_cast<uint32_t>(p.m_rows) * kb);
+  op.rb = buf_rsrc(p.b + static_cast<long>(e) * p.n * kb, static_cast<uint32_t>(p.n) * kb);
+  op.rsa = buf_rsrc(p.a_sf, static_cast<uint32_t>((p.m_rows + 127) / 128) * nct * 512);
+  op.rsb = buf_rsrc(p.b_sf + static_cast<long>(e) * p.b_sf_per, p.b_sf_per);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int row = min(m0 + wm * 128 + i * 32 + r32, m_end - 1);
+    op.oa[i] = static_cast<uint32_t>(row) * kb + h * 32;
+    op.osa[i] = static_cast<uint32_t>(sf_tile_word(row, h, nct));
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int row = n0 + wn * 128 + j * 32 + r32;
+    op.ob[j] = static_cast<uint32_t>(row) * kb + h * 32;
+    op.osb[j] = static_cast<uint32_t>(sf_tile_word(row, h, nct));
+  }
+
+  f32x16 acc[FM][FN];
+  nv_kloop(acc, op, p.k / NV_KC);
+
+  // ---- epilogue: alpha[e] * acc, one rounding; rows past the expert's end dropped ----
+  if (m0 + wm * 128 >= m_end) return;
+  const float alpha = p.alpha[e];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int rbase = m0 + wm * 128 + i * 32;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + r32;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = rbase + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (row < m_end)
+          nvg_store(p.out + static_cast<long>(row) * p.n + col, __fmul_rn(alpha, acc[i][j][q]));
       }
     }
   }
@@ -487,4 +675,72 @@ extern "C" mi_status mi_nvfp4_dequant_bf16(const uint8_t* codes, const uint8_t* 
                      static_cast<hipStream_t>(stream), codes, sf, static_cast<int>(rows),
                      static_cast<int>(k), static_cast<uint16_t*>(out));
   return launch_status("nvfp4_dequant");
+}
+
+extern "C" mi_status mi_grouped_mm_nvfp4(const uint8_t* a, const uint8_t* a_sf, size_t a_sf_bytes,
+                                         int64_t m_rows, int64_t k, const uint8_t* b,
+                                         const uint8_t* b_sf, size_t b_sf_bytes, int64_t batch,
+                                         int64_t n, const int32_t* m_indptr, const float* alpha,
+                                         void* out, mi_dtype out_dtype, void* stream) {
+  using namespace mi;
+  clear_error();
+  MI_REQUIRE(batch >= 1 && batch <= NVG_MAX_EXPERTS,
+             "grouped_mm_nvfp4: batch_size must be in [1, %d] (got %lld)", NVG_MAX_EXPERTS,
+             (long long)batch);
+  MI_REQUIRE(m_rows >= 0 && m_rows < (1LL << 31), "grouped_mm_nvfp4: cum_m out of range");
+  MI_REQUIRE(n > 0 && n % 256 == 0 && n < (1LL << 31),
+             "grouped_mm_nvfp4: n %% 256 == 0 required (got n=%lld)", (long long)n);
+  MI_REQUIRE(k >= 256 && k % 256 == 0 && k < (1LL << 31),
+             "grouped_mm_nvfp4: K must be a multiple of 256 (got %lld)", (long long)k);
+  MI_REQUIRE(out_dtype == MI_BF16 || out_dtype == MI_F32,
+             "grouped_mm_nvfp4: out_dtype must be bf16 or fp32");
+  MI_REQUIRE(m_indptr != nullptr && alpha != nullptr && b != nullptr && b_sf != nullptr,
+             "grouped_mm_nvfp4: m_indptr, alpha, b and b_sf must be non-null");
+  MI_REQUIRE_SUPPORTED(m_rows * (k / 2) < (1LL << 32) && n * (k / 2) < (1LL << 32) &&
+                           sf_needed(m_rows, k) < (1ULL << 32),
+                       "grouped_mm_nvfp4: a's codes and scales and one expert's codes must stay "
+                       "below 4 GiB");
+  const size_t per = sf_needed(n, k);
+  MI_REQUIRE(b_sf_bytes >= per * static_cast<size_t>(batch),
+             "grouped_mm_nvfp4: b_sf holds %zu bytes, %lld experts' 128x4 layouts need %zu",
+             b_sf_bytes, (long long)batch, per * static_cast<size_t>(batch));
+  if (m_rows == 0) return MI_OK;
+  MI_REQUIRE(a != nullptr && a_sf != nullptr && out != nullptr,
+             "grouped_mm_nvfp4: a, a_sf and out must be non-null");
+  MI_REQUIRE(a_sf_bytes >= sf_needed(m_rows, k),
+             "grouped_mm_nvfp4: a_sf holds %zu bytes, the 128x4 layout needs %zu", a_sf_bytes,
+             sf_needed(m_rows, k));
+  MI_REQUIRE(aligned16(a) && aligned16(b), "grouped_mm_nvfp4: a and b must be 16-byte aligned");
+  MI_REQUIRE((reinterpret_cast<uintptr_t>(a_sf) & 3) == 0 &&
+                 (reinterpret_cast<uintptr_t>(b_sf) & 3) == 0,
+             "grouped_mm_nvfp4: scale buffers must be 4-byte aligned");
+  // slots per XCD: both lists' runs (each at most ceil(tiles / 8))
+  const long ub = ((m_rows + NV_BM - 1) / NV_BM + batch) * (n / NV_BN);
+  const long grid = ((ub + 7) / 8 + 2) * 8;
+  MI_REQUIRE(grid < (1L << 31), "grouped_mm_nvfp4: problem too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto fill = [&](auto& args, auto* o) {
+    args.a = a;
+    args.a_sf = a_sf;
+    args.b = b;
+    args.b_sf = b_sf;
+    args.m_indptr = m_indptr;
+    args.alpha = alpha;
+    args.out = o;
+    args.m_rows = static_cast<int>(m_rows);
+    args.n = static_cast<int>(n);
+    args.k = static_cast<int>(k);
+    args.E = static_cast<int>(batch);
+    args.b_sf_per = static_cast<uint32_t>(per);
+  };
+  if (out_dtype == MI_BF16) {
+    NvgArgs<uint16_t> args;
+    fill(args, static_cast<uint16_t*>(out));
+    hipLaunchKernelGGL(nvfp4_grouped_kernel<uint16_t>, dim3(grid), dim3(NV_NT), 0, s, args);
+  } else {
+    NvgArgs<float> args;
+    fill(args, static_cast<float*>(out));
+    hipLaunchKernelGGL(nvfp4_grouped_kernel<float>, dim3(grid), dim3(NV_NT), 0, s, args);
+  }
+  return launch_status("grouped_mm_nvfp4");
 }

@@ -60,14 +60,19 @@ def grouped_mm_nvfp4(a, a_sf, b, b_sf, alpha, m_indptr, k: int):
     return out, written
 
 
-def grouped_mm_nvfp4_rows(a, a_sf, b, b_sf, alpha, m_indptr, k: int, rows, cols):
+def grouped_mm_nvfp4_rows(a_rows, a_sf, b_codes_of, b_sf, alpha, m_indptr, k: int, n: int,
+                          rows, cols):
     """float64 ``[len(rows), len(cols)]``: the same values at sampled rows
-    (each inside some group) and columns, one row at a time."""
-    a = np.asarray(a, dtype=np.uint8)
-    b = np.asarray(b, dtype=np.uint8)
-    E, n, _ = b.shape
+    (each inside some group) and columns, one row at a time.
+
+    ``a_rows`` holds the codes of the sampled rows ``[len(rows), K/2]``;
+    ``b_codes_of(e)`` returns expert ``e``'s codes at ``cols`` ``[len(cols), K/2]``
+    (so a large ``b`` need not be copied whole).
+    """
+    a_rows = np.asarray(a_rows, dtype=np.uint8)
     m_indptr = np.asarray(m_indptr, dtype=np.int64)
     alpha = np.asarray(alpha, dtype=np.float32).astype(np.float64).reshape(-1)
+    E = m_indptr.size - 1
     per = expert_sf_bytes(n, k)
     b_sf = np.asarray(b_sf, dtype=np.uint8).reshape(-1)
     cols = np.asarray(cols, dtype=np.int64)
@@ -75,7 +80,7 @@ def grouped_mm_nvfp4_rows(a, a_sf, b, b_sf, alpha, m_indptr, k: int, rows, cols)
     for i, r in enumerate(rows):
         e = int(np.searchsorted(m_indptr, r, side="right")) - 1
         assert 0 <= e < E and m_indptr[e] <= r < m_indptr[e + 1]
-        prod = base_product(a[r:r + 1], b[e][cols], a_sf, b_sf[e * per:(e + 1) * per], k,
-                            a_rows=[r], b_rows=cols)
+        prod = base_product(a_rows[i:i + 1], np.asarray(b_codes_of(e), dtype=np.uint8), a_sf,
+                            b_sf[e * per:(e + 1) * per], k, a_rows=[r], b_rows=cols)
         out[i] = alpha[e] * prod[0]
     return out

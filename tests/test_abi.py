@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert syms == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(L, s), s
-    assert L.mi_abi_version() == 4
+    assert L.mi_abi_version() == 5
 
 
 def _err(status):
@@ -141,3 +141,23 @@ def test_route_permutation_and_permute_rows_validation():
     # nothing to copy: returns before touching the device
     assert pr(T=0, x=NULL, perm=NULL, out=NULL) == 0
     assert pr(rows=0, out=NULL) == 0
+
+
+def test_grouped_nvfp4_validation():
+    L = _lib.lib()
+    per = 56 * 32 * 512  # n=7168 -> 56 row tiles, k=2048 -> 32 column tiles
+    g = lambda **kw: L.mi_grouped_mm_nvfp4(*{**dict(
+        a=FAKE, a_sf=FAKE, a_sf_bytes=1 << 30, m=32768, k=2048, b=FAKE, b_sf=FAKE,
+        b_sf_bytes=128 * per, batch=128, n=7168, mi=FAKE, alpha=FAKE, out=FAKE,
+        odt=_lib.MI_BF16, stream=NULL), **kw}.values())
+    assert "n % 256" in _err(g(n=7000))
+    assert "multiple of 256" in _err(g(k=2000))
+    assert "batch_size" in _err(g(batch=0))
+    assert "batch_size" in _err(g(batch=1025))
+    assert "bf16 or fp32" in _err(g(odt=_lib.MI_F16))
+    assert "experts' 128x4 layouts need" in _err(g(b_sf_bytes=128 * per - 1))
+    assert "a_sf holds" in _err(g(a_sf_bytes=1000))
+    assert "non-null" in _err(g(alpha=NULL))
+    assert "16-byte aligned" in _err(g(a=FAKE + 8))
+    assert "4-byte aligned" in _err(g(b_sf=FAKE + 2))
+    assert g(m=0, a=NULL, a_sf=NULL, out=NULL) == 0  # no rows: nothing to do

@@ -89,5 +89,6 @@ def test_per_expert_alpha_unwritten_rows_and_sampled_rows():
     keep[g2] = False
     assert np.array_equal(out2[keep], out[keep])
     rows, cols = [2, 6, 7, 13, 14, 16], [0, 3, 7]
-    samp = grouped_mm_nvfp4_rows(a2, a2_sf, b, b_sf, alpha, mi_off, k, rows, cols)
+    samp = grouped_mm_nvfp4_rows(a2[rows], a2_sf, lambda e: b[e][cols], b_sf, alpha, mi_off, k,
+                                 8, rows, cols)
     assert np.array_equal(samp, out[np.ix_(rows, cols)])
