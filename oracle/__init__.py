@@ -23,6 +23,8 @@ passage of the source pages it follows (cited by page title and section):
   :mod:`oracle.permute`
 - NVFP4 grouped GEMM (``grouped_mm_bf16`` formula with the
   ``mm_nvfp4_lora`` operand format) -> :mod:`oracle.nvfp4_grouped`
+- FC1 gate/up grouped GEMM with its SwiGLU activation
+  (``prims_ts_fp4_block_scale_moe`` parameters) -> :mod:`oracle.fc1`
 
 Inputs are numpy arrays; bf16 tensors are passed as their uint16 bit patterns.
 
@@ -35,4 +37,4 @@ convention and are pinned only to that convention (two independent codings
 and hand-worked offsets).
 """
 from . import formats, grouped_mm, lora_delta, nvfp4, fold, finalize, permute  # noqa: F401
-from . import nvfp4_grouped  # noqa: F401
+from . import nvfp4_grouped, fc1  # noqa: F401
