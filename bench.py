@@ -45,8 +45,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="", help="comma list of ops to run (profiling aid); "
                    "'copy_probe' (not part of the step) is a 512 MiB fp32 negation (read + write) used to "
-                   "calibrate the HBM byte counters; 'finalize', 'permute' and 'nvfp4_grouped' time "
-                   "the ops outside the step")
+                   "calibrate the HBM byte counters; 'finalize', 'permute', 'nvfp4_grouped' and "
+                   "'fc1_swiglu' time the ops outside the step")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                    "'--only nvfp4_raw,copy_probe' into the committed traffic summary")
@@ -342,6 +342,27 @@ def main():
             "note": "NVFP4 grouped GEMM, E=128 Zipf(1.1) routing of 4096 tokens x top-8 "
                     "(cum_m=32768), n=7168, k=2048, per-expert alpha, bf16 out; the fp16 MFMA "
                     "peak (2516.6 TFLOP/s) is the denominator"}
+    if not only or "fc1_swiglu" in only:
+        # FC1: gate/up grouped GEMM + SwiGLU on the same skewed routing
+        # (E=128, cum_m=32768), hidden=7168, inter=2048 (b is [128, 4096, 7168])
+        fc = synth.fc1_case(device=dev)
+        fco = torch.empty((fc.a.shape[0], fc.b.shape[1] // 2), dtype=torch.bfloat16, device=dev)
+        fms = time_alone(lambda: mi.grouped_mm_swiglu(fc.a, fc.b, fc.m_indptr, out=fco))
+        cnts = np.diff(fc.m_indptr.cpu().numpy())
+        cm, hid, two_i = fc.a.shape[0], fc.a.shape[1], fc.b.shape[1]
+        fflops = 2.0 * cm * two_i * hid
+        fbytes = 2.0 * cm * hid + 2.0 * two_i * hid * int((cnts > 0).sum()) + \
+            2.0 * cm * two_i / 2 + 4.0 * (len(cnts) + 1)
+        sec = fms * 1e-3
+        extra["fc1_swiglu"] = {
+            "ms": round(fms, 5), "tflops": round(fflops / sec / 1e12, 2),
+            "frac_mfma_peak": round(fflops / sec / 1e12 / PEAK_MFMA_TFLOPS, 4),
+            "gbps": round(fbytes / sec / 1e9, 1), "algorithmic_flops": fflops,
+            "algorithmic_bytes": fbytes,
+            "note": "FC1 gate/up grouped GEMM with the SwiGLU epilogue, E=128 Zipf(1.1) routing "
+                    "(cum_m=32768), hidden=7168, inter=2048, bf16; weights read once per expert "
+                    "(7.3 GB)"}
+        del fc, fco
     extra = extra or None
 
     cpu = None

@@ -4,6 +4,8 @@
  * Operations (sources are cited by page title and section):
  *   - mi_grouped_mm_bf16      ragged per-expert grouped GEMM
  *                             (flashinfer.grouped_mm.grouped_mm_bf16, formula)
+ *   - mi_grouped_mm_swiglu    FC1: gate/up grouped GEMM + SwiGLU epilogue
+ *                             (prims_ts_fp4_block_scale_moe, gemm1 parameters)
  *   - mi_moe_fc2_lora_delta   FC2 LoRA delta of a routed MoE
  *                             (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta, formula)
  *   - mi_moe_fc2_finalize_lora  the MoE finalize (routing-weighted combine of the FC2
@@ -87,6 +89,32 @@ MI_API mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k,
                              mi_dtype ab_dtype, const void* b, int64_t batch,
                              int64_t n, const int32_t* m_indptr,
                              void* out, mi_dtype out_dtype, void* stream);
+
+/*
+ * FC1 of a routed MoE: the gate/up grouped GEMM with its SwiGLU activation in
+ * the epilogue (flashinfer.fused_moe.prims_ts_fp4_block_scale_moe, parameters
+ * gemm1_weights, gemm1_alpha, gemm1_beta, gemm1_clamp_limit, activation_type;
+ * the ragged product of flashinfer.grouped_mm.grouped_mm_bf16, formula).  For
+ * every expert e and row t in [m_indptr[e], m_indptr[e+1]):
+ *   h = a[t] @ b[e]^T (+ fc1_delta[t])            fp32, [2I]
+ *   g = min(h[0:I], limit[e]);  u = clamp(h[I:2I], -limit[e], limit[e])
+ *   out[t] = g * sigmoid(alpha[e] * g) * (u + beta[e])      rounded once
+ * which is silu(gate) * up with the defaults (alpha 1, beta 0, no limit).
+ *   a          ab_dtype [m_rows, k] (the permuted FC1 input)
+ *   b          ab_dtype [batch, 2*inter_size, k]: rows 0..I-1 gate, I..2I-1 up
+ *   m_indptr   int32 [batch + 1], device, non-decreasing (clamped into [0, m_rows])
+ *   fc1_delta  bf16 [m_rows, 2*inter_size] added before the activation (the FC1
+ *              LoRA delta), or NULL; 8-byte aligned
+ *   alpha, beta, limit  fp32 [batch] each, or NULL for the default
+ *   out        out_dtype [m_rows, inter_size] (MI_BF16, MI_F16 or MI_F32), 16-byte
+ *              aligned; rows outside the groups are untouched
+ * Requirements: 1 <= batch <= 1024, inter_size % 128 == 0, k % 64 == 0.
+ */
+MI_API mi_status mi_grouped_mm_swiglu(const void* a, int64_t m_rows, int64_t k, mi_dtype ab_dtype,
+                               const void* b, int64_t batch, int64_t inter_size,
+                               const int32_t* m_indptr, const void* fc1_delta, const float* alpha,
+                               const float* beta, const float* limit, void* out,
+                               mi_dtype out_dtype, void* stream);
 
 /*
  * FC2 LoRA delta of a routed MoE (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta,

@@ -18,6 +18,7 @@ EXPORTS = [
     "mi_last_error",
     "mi_abi_version",
     "mi_grouped_mm_bf16",
+    "mi_grouped_mm_swiglu",
     "mi_moe_fc2_lora_delta_workspace_size",
     "mi_moe_fc2_lora_delta",
     "mi_moe_fc2_finalize_lora",
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.mi_abi_version.argtypes = []
         L.mi_grouped_mm_bf16.restype = I32
         L.mi_grouped_mm_bf16.argtypes = [P, I64, I64, I32, P, I64, I64, P, P, I32, P]
+        L.mi_grouped_mm_swiglu.restype = I32
+        L.mi_grouped_mm_swiglu.argtypes = [P, I64, I64, I32, P, I64, I64, P, P, P, P, P, P, I32, P]
         L.mi_moe_fc2_lora_delta_workspace_size.restype = SZ
         L.mi_moe_fc2_lora_delta_workspace_size.argtypes = [I64, I64, I64, I64, I64]
         L.mi_moe_fc2_lora_delta.restype = I32

@@ -20,6 +20,7 @@ from ._lib import MI_BF16, MI_F16, MI_F32, check
 
 __all__ = [
     "grouped_mm_bf16",
+    "grouped_mm_swiglu",
     "bgmv_moe_gemm2_lora_delta",
     "moe_finalize_lora",
     "moe_route_permutation",
@@ -97,6 +98,54 @@ def grouped_mm_bf16(a: torch.Tensor, b: torch.Tensor, m_indptr: torch.Tensor,
 # ---------------------------------------------------------------------------
 # FC2 LoRA delta
 # ---------------------------------------------------------------------------
+
+def grouped_mm_swiglu(a: torch.Tensor, b: torch.Tensor, m_indptr: torch.Tensor, *,
+                      fc1_delta: torch.Tensor | None = None,
+                      gemm1_alpha: torch.Tensor | None = None,
+                      gemm1_beta: torch.Tensor | None = None,
+                      gemm1_clamp_limit: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None,
+                      out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """FC1 of a routed MoE: ``h = a @ b[e]^T (+ fc1_delta)`` per expert's rows,
+    then ``out = g * sigmoid(alpha*g) * (u + beta)`` with ``g`` the clamped gate
+    half and ``u`` the clamped up half of ``h`` (plain SwiGLU by default).
+
+    ``a`` bf16/fp16 ``(cum_m, k)``, ``b`` ``(batch, 2I, k)`` (gate rows, then
+    up rows), ``fc1_delta`` bf16 ``(cum_m, 2I)``, ``gemm1_*`` fp32 ``(batch,)``.
+    Returns ``(cum_m, I)``; rows outside the groups of a caller-provided ``out``
+    are untouched (a fresh ``out`` is zero-filled there).
+    """
+    _need(a.dtype in (torch.bfloat16, torch.float16) and b.dtype == a.dtype,
+          "grouped_mm_swiglu: a and b must both be bfloat16 or both float16")
+    _need(a.dim() == 2 and b.dim() == 3 and b.shape[2] == a.shape[1] and b.shape[1] % 2 == 0,
+          "grouped_mm_swiglu: a must be (cum_m, k) and b (batch_size, 2*I, k)")
+    _need(m_indptr.dtype == torch.int32 and m_indptr.shape == (b.shape[0] + 1,),
+          "grouped_mm_swiglu: m_indptr must be int32 of shape (batch_size + 1,)")
+    _need(out_dtype in (torch.bfloat16, torch.float32, torch.float16),
+          "grouped_mm_swiglu: out_dtype must be bfloat16, float16 or float32")
+    E, two_i = b.shape[0], b.shape[1]
+    for name, t in (("gemm1_alpha", gemm1_alpha), ("gemm1_beta", gemm1_beta),
+                    ("gemm1_clamp_limit", gemm1_clamp_limit)):
+        _need(t is None or (t.dtype == torch.float32 and t.numel() == E),
+              f"grouped_mm_swiglu: {name} must be float32 with one value per expert")
+    _need(fc1_delta is None or (fc1_delta.dtype == torch.bfloat16 and
+                                fc1_delta.shape == (a.shape[0], two_i)),
+          "grouped_mm_swiglu: fc1_delta must be bfloat16 (cum_m, 2*I)")
+    _need_cuda("grouped_mm_swiglu", a, b, m_indptr, fc1_delta, gemm1_alpha, gemm1_beta,
+               gemm1_clamp_limit, out)
+    a, b, m_indptr = a.contiguous(), b.contiguous(), m_indptr.contiguous()
+    opt = [None if t is None else t.contiguous()
+           for t in (fc1_delta, gemm1_alpha, gemm1_beta, gemm1_clamp_limit)]
+    if out is None:
+        out = torch.zeros((a.shape[0], two_i // 2), dtype=out_dtype, device=a.device)
+    _need(out.shape == (a.shape[0], two_i // 2) and out.dtype == out_dtype and
+          out.is_contiguous(),
+          "grouped_mm_swiglu: out must be a contiguous (cum_m, I) tensor of out_dtype")
+    check(_lib.lib().mi_grouped_mm_swiglu(
+        _ptr(a), a.shape[0], a.shape[1], _DT[a.dtype], _ptr(b), E, two_i // 2, _ptr(m_indptr),
+        *(_ptr(t) for t in opt), _ptr(out), _DT[out_dtype], _stream(a.device)))
+    return out
+
 
 def fill_w_ptr(bank: torch.Tensor) -> torch.Tensor:
     """Base-pointer table ``[1, E]`` (int64 byte addresses) of a contiguous

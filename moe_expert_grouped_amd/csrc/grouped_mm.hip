@@ -435,15 +435,28 @@ __device__ __forceinline__ void gb_interleave_copy() {
   }
 }
 
+// FC1 epilogue parameters: the gate/up halves of b and the SwiGLU activation
+struct GbGlu {
+  const uint16_t* delta;  // bf16 [m_rows, 2I] added before the activation, or null
+  const float* alpha;     // [E] or null (1)
+  const float* beta;      // [E] or null (0)
+  const float* limit;     // [E] or null (no clamp)
+};
+
 // One output tile: 256 rows (FN = 4: waves 2 x 2, 128 x 128 each) or 128 rows
 // (FN = 2: waves 1 x 4, 128 x 64 each), 256 columns.  `rows` (1..BM) of the
 // tile belong to the expert; the a descriptor covers only those, so rows past
 // them read as zero and their stores are dropped.
-template <int FN, bool F16, typename OutT>
+//
+// GLU (FC1): b[e] is [n = 2I, k], gate rows 0..I-1 and up rows I..2I-1.  A
+// tile then covers 128 output columns c0 = n0/2 ..: each wavefront's b
+// fragments j < FN/2 are gate rows and j >= FN/2 the matching up rows, so one
+// lane holds both operands of every output it writes; out is [m_rows, I].
+template <int FN, bool F16, bool GLU, typename OutT>
 __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
                                         const uint16_t* __restrict__ b, OutT* __restrict__ out,
                                         uint16_t* smem, int e, int m0, int rows, int n0, int k,
-                                        int n) {
+                                        int n, const GbGlu& gl) {
   constexpr int WN = FN == 4 ? 2 : 4;        // wavefronts along n
   constexpr int BM = 128 * (4 / WN);         // tile rows
   constexpr int CPT_A = BM / 32, CPT_B = 8;  // 16-byte chunks per thread per stage
@@ -457,8 +470,21 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
   const uint32_t kbytes = static_cast<uint32_t>(k) * 2;
 
   const __amdgpu_buffer_rsrc_t ar = buf_rsrc(a + static_cast<long>(m0) * k, rows * kbytes);
-  const __amdgpu_buffer_rsrc_t br =
-      buf_rsrc(b + (static_cast<long>(e) * n + n0) * k, GB_BN * kbytes);
+  const int inter = n / 2, c0 = n0 / 2;  // GLU: output width and first output column
+  const long b_row0 = static_cast<long>(e) * n + (GLU ? c0 : n0);
+  const __amdgpu_buffer_rsrc_t br = buf_rsrc(
+      b + b_row0 * k, static_cast<uint32_t>(GLU ? inter + 128 : GB_BN) * kbytes);
+  // b row (relative to b_row0) of staging block i (LDS rows 32i .. 32i+31)
+  uint32_t b_so[CPT_B];
+#pragma unroll
+  for (int i = 0; i < CPT_B; ++i) {
+    int row = 32 * i;
+    if constexpr (GLU) {
+      const int jj = i % FN;  // fragment of wavefront i / FN
+      row = (jj < FN / 2 ? 0 : inter) + (i / FN) * 16 * FN + (jj % (FN / 2)) * 32;
+    }
+    b_so[i] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(row) * kbytes);
+  }
 
   // staging: chunk c = tid + 256 i is row c/8 = tid/8 + 32 i, 16-byte chunk
   // tid%8 of the stage
@@ -487,7 +513,7 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
 #pragma unroll
     for (int i = 0; i < CPT_A; ++i) ra[p][i] = buf_ld128(ar, g_off + i * g_step, so);
 #pragma unroll
-    for (int i = 0; i < CPT_B; ++i) rb[p][i] = buf_ld128(br, g_off + i * g_step, so);
+    for (int i = 0; i < CPT_B; ++i) rb[p][i] = buf_ld128(br, g_off, so + b_so[i]);
   };
   auto lstore = [&](int p, uint16_t* st) {
 #pragma unroll
@@ -561,31 +587,82 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
   if (kt < KT) kstep(kt, 1);
 
   if (wm * 128 >= rows) return;  // all of this wavefront's rows lie past the group's end
-  // acc[i][j][q]: tile row wm*128 + i*32 + r, column wn*32*FN + j*32 + 8*(q/4) + 4h + q%4.
-  const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(out + static_cast<long>(m0) * n,
-                                                static_cast<uint32_t>(rows) * n * sizeof(OutT));
+  if constexpr (!GLU) {
+    // acc[i][j][q]: tile row wm*128 + i*32 + r, column wn*32*FN + j*32 + 8*(q/4) + 4h + q%4.
+    const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(out + static_cast<long>(m0) * n,
+                                                  static_cast<uint32_t>(rows) * n * sizeof(OutT));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t orow =
-        (static_cast<uint32_t>(wm * 128 + i * 32 + r) * n + n0 + wn * 32 * FN + 4 * h) *
-        sizeof(OutT);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t orow =
+          (static_cast<uint32_t>(wm * 128 + i * 32 + r) * n + n0 + wn * 32 * FN + 4 * h) *
+          sizeof(OutT);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+      for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                         acc[i][j][4 * g + 3]};
-        bstore_out4<OutT>(orsrc, orow + (j * 32 + 8 * g) * sizeof(OutT), v);
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                           acc[i][j][4 * g + 3]};
+          bstore_out4<OutT>(orsrc, orow + (j * 32 + 8 * g) * sizeof(OutT), v);
+        }
+      }
+    }
+  } else {
+    // gate acc[i][j], up acc[i][j + FN/2] (j < FN/2): tile row wm*128 + i*32 + r,
+    // output column c0 + wn*16*FN + j*32 + 8*(q/4) + 4h + q%4
+    const float alpha = gl.alpha ? gl.alpha[e] : 1.f;
+    const float beta = gl.beta ? gl.beta[e] : 0.f;
+    const float limit = gl.limit ? gl.limit[e] : __builtin_inff();
+    const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(
+        out + static_cast<long>(m0) * inter, static_cast<uint32_t>(rows) * inter * sizeof(OutT));
+    const bool has_delta = gl.delta != nullptr;
+    const __amdgpu_buffer_rsrc_t drsrc =
+        buf_rsrc(has_delta ? gl.delta + static_cast<long>(m0) * n : gl.delta,
+                 has_delta ? static_cast<uint32_t>(rows) * n * 2 : 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t trow = wm * 128 + i * 32 + r;
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t col = c0 + wn * 16 * FN + j * 32 + 8 * g + 4 * h;
+          float hg[4], hu[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            hg[q] = acc[i][j][4 * g + q];
+            hu[q] = acc[i][j + FN / 2][4 * g + q];
+          }
+          if (has_delta) {
+            const u32x2 dg = buf_ld64(drsrc, (trow * n + col) * 2, 0);
+            const u32x2 du = buf_ld64(drsrc, (trow * n + inter + col) * 2, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t wg = dg[q >> 1], wu = du[q >> 1];
+              hg[q] += __uint_as_float((q & 1) ? (wg & 0xffff0000u) : (wg << 16));
+              hu[q] += __uint_as_float((q & 1) ? (wu & 0xffff0000u) : (wu << 16));
+            }
+          }
+          f32x4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float gg = fminf(hg[q], limit);
+            const float uu = fminf(fmaxf(hu[q], -limit), limit);
+            // logistic function from the hardware exp2 and reciprocal (a few ulp)
+            const float sig = __builtin_amdgcn_rcpf(1.f + __expf(-alpha * gg));
+            v[q] = gg * sig * (uu + beta);
+          }
+          bstore_out4<OutT>(orsrc, (trow * inter + col) * sizeof(OutT), v);
+        }
       }
     }
   }
 }
 
-template <bool F16, typename OutT>
+template <bool F16, bool GLU, typename OutT>
 __global__ __launch_bounds__(256, 1) void grouped_mm_big_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
     const int32_t* __restrict__ m_indptr, OutT* __restrict__ out, int m_rows, int k, int n,
-    int E) {
+    int E, GbGlu gl) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * GB_STAGE];
   __shared__ int s_full0[GM_MAX_EXPERTS + 1];
   __shared__ int s_half0[GM_MAX_EXPERTS + 1];
@@ -611,7 +688,7 @@ __global__ __launch_bounds__(256, 1) void grouped_mm_big_kernel(
     const int m0 = __builtin_amdgcn_readfirstlane(s_row0[e] + (mt - s_full0[e]) * 256);
     const int end = max(s_row0[e + 1], s_row0[e]);
     const int rows = __builtin_amdgcn_readfirstlane(min(end - m0, 256));
-    gb_tile<4, F16, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n);
+    gb_tile<4, F16, GLU, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n, gl);
   } else {
     const long L = xcd * run_h + (slot - run_f);
     if (slot - run_f >= run_h || L >= total_h) return;
@@ -622,7 +699,7 @@ __global__ __launch_bounds__(256, 1) void grouped_mm_big_kernel(
     const int m0 = __builtin_amdgcn_readfirstlane(s_row0[e] + (s_full0[e + 1] - s_full0[e]) * 256);
     const int end = max(s_row0[e + 1], s_row0[e]);
     const int rows = __builtin_amdgcn_readfirstlane(end - m0);
-    gb_tile<2, F16, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n);
+    gb_tile<2, F16, GLU, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n, gl);
   }
 }
 
@@ -657,22 +734,23 @@ mi_status launch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b
   return launch_status("grouped_mm_bf16");
 }
 
-template <bool F16, typename OutT>
+template <bool F16, bool GLU, typename OutT>
 mi_status launch_grouped_big(const void* a, int64_t m_rows, int64_t k, const void* b, int64_t batch,
-                             int64_t n, const int32_t* m_indptr, void* out, hipStream_t stream) {
+                             int64_t n, const int32_t* m_indptr, void* out, hipStream_t stream,
+                             const GbGlu& gl) {
   // one workgroup per tile of the upper bound (the real count is known on the
   // device only); each XCD's run of the real tiles fits in its G/8 ids
   const long ub_tiles = ((m_rows + 255) / 256 + batch) * (n / GB_BN);
   const long G = ((ub_tiles + 7) / 8 + 2) * 8;
   MI_REQUIRE(G < (1L << 31), "grouped_mm_bf16: problem too large");
-  MI_REQUIRE(static_cast<uint64_t>(k) * 2 * GB_BN < (1ULL << 32) &&
+  MI_REQUIRE(static_cast<uint64_t>(k) * 2 * (GLU ? n / 2 + 128 : GB_BN) < (1ULL << 32) &&
                  static_cast<uint64_t>(n) * 256 * sizeof(OutT) < (1ULL << 32),
              "grouped_mm_bf16: n or k too large for 256-row tiles");
-  hipLaunchKernelGGL((grouped_mm_big_kernel<F16, OutT>), dim3(G), dim3(256), 0, stream,
+  hipLaunchKernelGGL((grouped_mm_big_kernel<F16, GLU, OutT>), dim3(G), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), m_indptr,
                      static_cast<OutT*>(out), static_cast<int>(m_rows), static_cast<int>(k),
-                     static_cast<int>(n), static_cast<int>(batch));
-  return launch_status("grouped_mm_bf16");
+                     static_cast<int>(n), static_cast<int>(batch), gl);
+  return launch_status(GLU ? "grouped_mm_swiglu" : "grouped_mm_bf16");
 }
 
 template <bool F16, typename OutT>
@@ -683,7 +761,9 @@ mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void*
   // large average groups take 256x256 tiles; smaller groups stream b from HBM
   // and take 64x64 tiles, two workgroups per CU, with 4 K steps in flight.
   const int64_t avg = m_rows / batch;
-  if (avg >= 192) return launch_grouped_big<F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream);
+  if (avg >= 192)
+    return launch_grouped_big<F16, false, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
+                                               GbGlu{});
   return launch_grouped<64, 64, 64, 2, 2, 4, F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
 }
 
@@ -725,4 +805,47 @@ extern "C" mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k
                : dispatch_grouped<false, _Float16>(a, m_rows, k, b, batch, n, m_indptr, out, s);
   return f16 ? dispatch_grouped<true, float>(a, m_rows, k, b, batch, n, m_indptr, out, s)
              : dispatch_grouped<false, float>(a, m_rows, k, b, batch, n, m_indptr, out, s);
+}
+
+extern "C" mi_status mi_grouped_mm_swiglu(const void* a, int64_t m_rows, int64_t k,
+                                          mi_dtype ab_dtype, const void* b, int64_t batch,
+                                          int64_t inter_size, const int32_t* m_indptr,
+                                          const void* fc1_delta, const float* alpha,
+                                          const float* beta, const float* limit, void* out,
+                                          mi_dtype out_dtype, void* stream) {
+  using namespace mi;
+  clear_error();
+  MI_REQUIRE(batch >= 1 && batch <= GM_MAX_EXPERTS,
+             "grouped_mm_swiglu: batch_size must be in [1, %d] (got %lld)", GM_MAX_EXPERTS,
+             (long long)batch);
+  MI_REQUIRE(m_rows >= 0 && m_rows < (1LL << 31), "grouped_mm_swiglu: cum_m out of range");
+  MI_REQUIRE(inter_size > 0 && inter_size % 128 == 0 && inter_size < (1LL << 30),
+             "grouped_mm_swiglu: intermediate size %% 128 == 0 required (got %lld)",
+             (long long)inter_size);
+  MI_REQUIRE(k > 0 && k % 64 == 0 && k < (1LL << 31),
+             "grouped_mm_swiglu: k %% 64 == 0 required (got k=%lld)", (long long)k);
+  MI_REQUIRE(ab_dtype == MI_BF16 || ab_dtype == MI_F16,
+             "grouped_mm_swiglu: a and b must be bf16 or fp16");
+  MI_REQUIRE(out_dtype == MI_BF16 || out_dtype == MI_F32 || out_dtype == MI_F16,
+             "grouped_mm_swiglu: out_dtype must be bf16, fp16 or fp32");
+  MI_REQUIRE(m_indptr != nullptr && b != nullptr, "grouped_mm_swiglu: m_indptr or b is null");
+  if (m_rows == 0) return MI_OK;
+  MI_REQUIRE(a != nullptr && out != nullptr, "grouped_mm_swiglu: a/out is null");
+  MI_REQUIRE(aligned16(a) && aligned16(b), "grouped_mm_swiglu: a and b must be 16-byte aligned");
+  MI_REQUIRE(fc1_delta == nullptr || (reinterpret_cast<uintptr_t>(fc1_delta) & 7) == 0,
+             "grouped_mm_swiglu: fc1_delta must be 8-byte aligned");
+  MI_REQUIRE((reinterpret_cast<uintptr_t>(out) & 15) == 0,
+             "grouped_mm_swiglu: out must be 16-byte aligned");
+  const int64_t n = 2 * inter_size;
+  const GbGlu gl{static_cast<const uint16_t*>(fc1_delta), alpha, beta, limit};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f16 = ab_dtype == MI_F16;
+  if (out_dtype == MI_BF16)
+    return f16 ? launch_grouped_big<true, true, Bf16Out>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl)
+               : launch_grouped_big<false, true, Bf16Out>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl);
+  if (out_dtype == MI_F16)
+    return f16 ? launch_grouped_big<true, true, _Float16>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl)
+               : launch_grouped_big<false, true, _Float16>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl);
+  return f16 ? launch_grouped_big<true, true, float>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl)
+             : launch_grouped_big<false, true, float>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl);
 }

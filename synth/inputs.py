@@ -40,6 +40,8 @@ __all__ = [
     "nvfp4_probe",
     "Nvfp4GroupedCase",
     "nvfp4_grouped_case",
+    "Fc1Case",
+    "fc1_case",
 ]
 
 
@@ -481,3 +483,49 @@ def nvfp4_grouped_case(seed: int = 6, device="cpu", counts=None, E=128, T=4096, 
         alpha = 0.005 + 0.015 * torch.rand(E, generator=g, device=device, dtype=torch.float32)
     return Nvfp4GroupedCase(f"nvfp4-grouped E={E} cum_m={cum} n={n} k={k}", a, a_sf, b, b_sf,
                             alpha.to(torch.float32), m_indptr.to(device), k)
+
+
+@dataclass
+class Fc1Case:
+    name: str
+    a: torch.Tensor          # [cum_m, hidden] bf16 (permuted FC1 input)
+    b: torch.Tensor          # [E, 2*inter, hidden] bf16 (gate rows, then up rows)
+    m_indptr: torch.Tensor   # [E+1] int32
+    delta: torch.Tensor | None   # [cum_m, 2*inter] bf16
+    alpha: torch.Tensor | None   # [E] fp32
+    beta: torch.Tensor | None
+    limit: torch.Tensor | None
+
+
+def fc1_case(seed: int = 7, device="cpu", counts=None, E=128, T=4096, top_k=8, hidden=7168,
+             inter=2048, with_delta=False, act_params=False, ints=False) -> Fc1Case:
+    """FC1 operands.  Default: the skewed routing of ``grouped_zipf`` (E=128,
+    cum_m=32768) with hidden=7168 and inter=2048; a ~ N(0,1), b ~ N(0, 1/hidden)
+    (so h ~ N(0,1)).  ``with_delta``: an additive FC1 delta ~ N(0, 0.1);
+    ``act_params``: per-expert alpha uniform 1..2, beta uniform -1..1, clamp
+    limit uniform 0.5..4 (so the clamp acts on part of h).  ``ints``: small
+    integers (h exact in fp32)."""
+    if counts is None:
+        counts = zipf_counts(T * top_k, E, 8, 1.1, T, 3)
+    counts = np.asarray(counts, dtype=np.int64)
+    E = len(counts)
+    m_indptr = torch.zeros(E + 1, dtype=torch.int32)
+    m_indptr[1:] = torch.from_numpy(np.cumsum(counts)).to(torch.int32)
+    cum = int(m_indptr[-1])
+    g = gen(seed, device)
+    if ints:
+        a = bf16_ints((cum, hidden), -2, 2, g, device)
+        b = bf16_ints((E, 2 * inter, hidden), -1, 1, g, device)
+    else:
+        a = bf16_normal((cum, hidden), 1.0, g, device)
+        b = torch.empty((E, 2 * inter, hidden), dtype=torch.bfloat16, device=device)
+        for e in range(E):  # per expert to bound the float32 staging buffer
+            b[e] = bf16_normal((2 * inter, hidden), hidden ** -0.5, g, device)
+    delta = bf16_normal((cum, 2 * inter), 0.1, g, device) if with_delta else None
+    alpha = beta = limit = None
+    if act_params:
+        alpha = 1.0 + torch.rand(E, generator=g, device=device, dtype=torch.float32)
+        beta = 2.0 * torch.rand(E, generator=g, device=device, dtype=torch.float32) - 1.0
+        limit = 0.5 + 3.5 * torch.rand(E, generator=g, device=device, dtype=torch.float32)
+    return Fc1Case(f"fc1 E={E} cum_m={cum} hidden={hidden} inter={inter}", a, b,
+                   m_indptr.to(device), delta, alpha, beta, limit)

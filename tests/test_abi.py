@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert syms == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(L, s), s
-    assert L.mi_abi_version() == 5
+    assert L.mi_abi_version() == 6
 
 
 def _err(status):
@@ -161,3 +161,19 @@ def test_grouped_nvfp4_validation():
     assert "16-byte aligned" in _err(g(a=FAKE + 8))
     assert "4-byte aligned" in _err(g(b_sf=FAKE + 2))
     assert g(m=0, a=NULL, a_sf=NULL, out=NULL) == 0  # no rows: nothing to do
+
+
+def test_swiglu_validation():
+    L = _lib.lib()
+    g = lambda **kw: L.mi_grouped_mm_swiglu(*{**dict(
+        a=FAKE, m=4096, k=2048, adt=_lib.MI_BF16, b=FAKE, batch=8, inter=1024, mi=FAKE,
+        delta=NULL, alpha=NULL, beta=NULL, limit=NULL, out=FAKE, odt=_lib.MI_BF16,
+        stream=NULL), **kw}.values())
+    assert "% 128" in _err(g(inter=1000))
+    assert "k % 64" in _err(g(k=100))
+    assert "batch_size" in _err(g(batch=0))
+    assert "bf16 or fp16" in _err(g(adt=_lib.MI_F32))
+    assert "8-byte aligned" in _err(g(delta=FAKE + 4))
+    assert "16-byte aligned" in _err(g(out=FAKE + 8))
+    assert "null" in _err(g(mi=NULL))
+    assert g(m=0, a=NULL, out=NULL) == 0
