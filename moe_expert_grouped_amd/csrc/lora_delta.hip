@@ -676,10 +676,21 @@ __global__ __launch_bounds__(256, 2) void shrink_le_kernel(ShrinkLeArgs p) {
   const int cpr = p.I / 8;
   const uint16_t* Ale =
       reinterpret_cast<const uint16_t*>(gld<int64_t>(p.w_ptr_a + e) + 2 * p.stride_a * l);
-  for (int c = tid; c < R16 * cpr; c += 256) {
-    const int r = c / cpr, cc = c - r * cpr;
-    const u32x4 v = gld<u32x4>(Ale + static_cast<long>(min(r, p.rank - 1)) * p.I + cc * 8);
-    *reinterpret_cast<u32x4*>(s_a + r * p.I + ((cc ^ (r & 15)) << 3)) = v;
+  // eight 16-byte loads per thread in flight before their LDS writes
+  for (int c0 = 0; c0 < R16 * cpr; c0 += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // past the end: reload the last chunk (not stored)
+      const int c = min(c0 + u * 256 + tid, R16 * cpr - 1);
+      const int r = c / cpr, cc = c - r * cpr;
+      v[u] = gld<u32x4>(Ale + static_cast<long>(min(r, p.rank - 1)) * p.I + cc * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * 256 + tid;
+      const int r = c / cpr, cc = c - r * cpr;
+      if (c < R16 * cpr) *reinterpret_cast<u32x4*>(s_a + r * p.I + ((cc ^ (r & 15)) << 3)) = v[u];
+    }
   }
   __syncthreads();
 
