@@ -124,3 +124,12 @@ def test_route_then_grouped_gemm(gpu):
         for j in range(k):
             e = int(ids[t, j])
             assert torch.equal(y[p[t, j]].cpu(), ws[e] @ xs[t]), (t, j)
+
+
+def test_route_top1_many_experts_and_long_lists(gpu):
+    """top_k = 1 over the largest expert count, and one hot expert taking
+    most of 2^20 slots (long runs inside every chunk)."""
+    ids = synth.routing_ids(seed=51, T=20000, top_k=1, E=1024, invalid_frac=0.02)
+    check_route(ids, 1024, gpu)
+    hot = synth.routing_ids(seed=52, T=131072, top_k=8, E=16, zipf_s=3.0)
+    check_route(hot, 16, gpu)

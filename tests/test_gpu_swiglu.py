@@ -108,3 +108,16 @@ def test_full_size_sampled(gpu):
     assert written.all()
     got = to_f64(out[torch.from_numpy(rows).to(gpu)][:, torch.from_numpy(cols).to(gpu)])
     check_close(got, ref, "swiglu full size (sampled)")
+
+
+def test_fp16_operands(gpu):
+    """fp16 a and b (the GEMM's other input type), every output type."""
+    c = synth.fc1_case(seed=13, counts=(150, 0, 300, 7), hidden=192, inter=128, act_params=True)
+    c16 = synth.Fc1Case("fp16 operands", c.a.to(torch.float16), c.b.to(torch.float16),
+                        c.m_indptr, None, c.alpha, c.beta, c.limit)
+    np_ = lambda t: t.cpu().numpy()
+    ref, written = oracle_fc1(bits16(c16.a), bits16(c16.b), c16.m_indptr.numpy(), dtype="f16",
+                              alpha=np_(c.alpha), beta=np_(c.beta), limit=np_(c.limit))
+    for dt in (torch.bfloat16, torch.float16, torch.float32):
+        out = run(c16, gpu, dt)
+        check_close(to_f64(out)[written], ref[written], f"swiglu fp16 operands {dt}")
