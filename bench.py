@@ -295,14 +295,17 @@ def main():
     if not only or "finalize" in only:
         fc2 = synth.bf16_normal((dc.act.shape[0], dc.H), 1.0, synth.gen(77, dev), dev)
         fout = torch.empty((dc.T, dc.H), dtype=torch.bfloat16, device=dev)
+        fws = torch.empty(mi.finalize_workspace_bytes(dc.T, dc.top_k, dc.E, dc.L, dc.rank, dc.H),
+                          dtype=torch.uint8, device=dev)
         fms = time_alone(lambda: mi.moe_finalize_lora(
             fc2, dc.act, dc.perm, wa, sa, wb, sb, dc.topk_ids, dc.topk_weights, dc.lora_ids,
-            dc.rank, dc.H, num_adapters=dc.L, scale=dc.scale, out=fout, workspace=ws))
+            dc.rank, dc.H, num_adapters=dc.L, scale=dc.scale, out=fout, workspace=fws))
         n_routed = int((perm >= 0).sum())
         extra["finalize_fused"] = hbm_entry(
             fms, delta_bytes + 2.0 * dc.H * n_routed,
             "MoE finalize (weighted combine of the routed FC2 rows) with the LoRA delta added, "
-            "delta workload; not part of the step", delta_flops + 2.0 * dc.H * n_routed)
+            "delta workload, two passes (fp32 delta in the workspace, then the combine); not "
+            "part of the step", delta_flops + 2.0 * dc.H * n_routed)
     if not only or "permute" in only:
         nslot = dc.T * dc.top_k
         rws = torch.empty(mi.route_workspace_bytes(nslot, dc.E), dtype=torch.uint8, device=dev)

@@ -175,10 +175,18 @@ MI_API mi_status mi_moe_fc2_lora_delta(const void* act, int64_t padded_rows, int
  *                >= padded_rows is not routed here and contributes nothing (to the
  *                combine and to the delta); every other slot's row is combined with
  *                its weight, whatever its expert id
- *   everything else, the workspace (same size) and the validation: as for
- *   mi_moe_fc2_lora_delta (its messages name that operation).  Tokens without an
- *   adapter get the combine alone.  num_adapters == 0 gives the plain combine.
+ *   everything else and the validation: as for mi_moe_fc2_lora_delta (its
+ *   messages name that operation).  Tokens without an adapter get the combine
+ *   alone.  num_adapters == 0 gives the plain combine.
+ *   workspace    at least mi_moe_fc2_lora_delta_workspace_size(...) bytes.  With
+ *                mi_moe_fc2_finalize_workspace_size(...) bytes (room for an fp32
+ *                [num_tokens, hidden_size] delta) the call runs in two passes --
+ *                the delta to the workspace, then a combine that reads whole FC2
+ *                rows -- which is faster; both give bitwise the same output.
  */
+MI_API size_t mi_moe_fc2_finalize_workspace_size(int64_t num_tokens, int64_t top_k,
+                                          int64_t num_experts, int64_t num_adapters,
+                                          int64_t rank, int64_t hidden_size);
 MI_API mi_status mi_moe_fc2_finalize_lora(const void* fc2, mi_dtype fc2_dtype, const void* act,
                                    int64_t padded_rows, int64_t inter_size,
                                    const int32_t* expanded_idx_to_permuted_idx,

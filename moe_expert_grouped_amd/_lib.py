@@ -22,6 +22,7 @@ EXPORTS = [
     "mi_moe_fc2_lora_delta_workspace_size",
     "mi_moe_fc2_lora_delta",
     "mi_moe_fc2_finalize_lora",
+    "mi_moe_fc2_finalize_workspace_size",
     "mi_moe_route_workspace_size",
     "mi_moe_route_permutation",
     "mi_moe_permute_rows",
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
             I64, I64, I64, I64, I64, I64,  # T, top_k, E, L, rank, H
             I32, F32, I32,        # lora_dtype, scale, out_dtype
             P, P, SZ, P]          # out, workspace, bytes, stream
+        L.mi_moe_fc2_finalize_workspace_size.restype = SZ
+        L.mi_moe_fc2_finalize_workspace_size.argtypes = [I64, I64, I64, I64, I64, I64]
         L.mi_moe_fc2_finalize_lora.restype = I32
         L.mi_moe_fc2_finalize_lora.argtypes = [
             P, I32,               # fc2, fc2_dtype

@@ -27,6 +27,7 @@ __all__ = [
     "moe_permute_rows",
     "route_workspace_bytes",
     "delta_workspace_bytes",
+    "finalize_workspace_bytes",
     "fill_w_ptr",
     "mm_nvfp4_lora",
     "grouped_mm_nvfp4",
@@ -163,6 +164,13 @@ def delta_workspace_bytes(num_tokens, top_k, num_experts, num_adapters, rank) ->
                                                                num_adapters, rank))
 
 
+def finalize_workspace_bytes(num_tokens, top_k, num_experts, num_adapters, rank,
+                             hidden_size) -> int:
+    """Workspace of the two-pass finalize (the delta's plus an fp32 [T, H] delta)."""
+    return int(_lib.lib().mi_moe_fc2_finalize_workspace_size(num_tokens, top_k, num_experts,
+                                                             num_adapters, rank, hidden_size))
+
+
 def bgmv_moe_gemm2_lora_delta(gemm1_activation_output: torch.Tensor,
                               expanded_idx_to_permuted_idx: torch.Tensor, w_ptr_a: torch.Tensor,
                               lora_stride_a: int, w_ptr_b: torch.Tensor, lora_stride_b: int,
@@ -235,7 +243,8 @@ def _delta_call(fc2, act, perm, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, 
         out = torch.empty((T, hidden_size), dtype=out_dtype, device=act.device)
     _need(out.shape == (T, hidden_size) and out.dtype == out_dtype and out.is_contiguous(),
           "bgmv_moe_gemm2_lora_delta: out must be a contiguous [T, H] tensor of out_dtype")
-    need = delta_workspace_bytes(T, top_k, E, num_adapters, rank)
+    need = delta_workspace_bytes(T, top_k, E, num_adapters, rank) if fc2 is None else \
+        finalize_workspace_bytes(T, top_k, E, num_adapters, rank, hidden_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=act.device)
     args = (_ptr(act), act.shape[0], act.shape[1], _ptr(perm), _ptr(w_ptr_a), int(lora_stride_a),

@@ -29,4 +29,4 @@ mi_status launch_status(const char* what) {
 
 extern "C" const char* mi_last_error(void) { return mi::g_last_error.c_str(); }
 
-extern "C" int mi_abi_version(void) { return 6; }
+extern "C" int mi_abi_version(void) { return 7; }

@@ -929,6 +929,27 @@ __device__ __forceinline__ void write_tile(const ExpandArgs& p, const Tile& tile
   }
 }
 
+// Finalize, second pass (when the workspace holds an fp32 [T, H] delta): one
+// thread per 8 columns of one token reads the token's fp32 delta and its
+// routed FC2 rows (whole rows across a wavefront, 16 or 32 bytes a lane) and
+// writes the combined output.  The same arithmetic as write_tile's: the delta,
+// then one FMA per routed slot in slot order, one rounding.
+__global__ __launch_bounds__(256) void finalize_combine_kernel(ExpandArgs p, const float* delta,
+                                                               int T) {
+  const long cpr = p.H / 8;  // 8-column items per token
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<long>(T) * cpr) return;
+  const int t = static_cast<int>(i / cpr);
+  const int col = static_cast<int>(i - t * cpr) * 8;
+  const float* d = delta + static_cast<long>(t) * p.H + col;
+  f32x4 v0 = gld<f32x4>(d), v1 = gld<f32x4>(d + 4);
+  for (int j0 = 0; j0 < p.top_k; j0 += FIN_KB) {
+    const Route rt = load_route(p, t, j0);
+    add_rows(rt, load_rows(p, rt, col), v0, v1);
+  }
+  store_out8(p, t, col, v0, v1);
+}
+
 // accumulator rows of EXP_CW floats; 16-byte chunk c of row tl sits at c ^ (tl & 31)
 __device__ __forceinline__ int acc_chunk(int tl, int c) {
   return tl * (EXP_CW / 4) + (c ^ (tl & 31));
@@ -1165,6 +1186,21 @@ extern "C" size_t mi_moe_fc2_lora_delta_workspace_size(int64_t num_tokens, int64
 
 namespace mi {
 namespace {
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+}  // namespace
+}  // namespace mi
+
+extern "C" size_t mi_moe_fc2_finalize_workspace_size(int64_t num_tokens, int64_t top_k,
+                                                     int64_t num_experts, int64_t num_adapters,
+                                                     int64_t rank, int64_t hidden_size) {
+  const size_t d = mi_moe_fc2_lora_delta_workspace_size(num_tokens, top_k, num_experts,
+                                                        num_adapters, rank);
+  if (d == 0 || hidden_size < 1) return 0;
+  return mi::align256(d) + static_cast<size_t>(num_tokens) * static_cast<size_t>(hidden_size) * 4;
+}
+
+namespace mi {
+namespace {
 
 // The delta and, when fc2 is given, the finalize: both entry points below.
 mi_status run_delta(const char* what, const void* act, int64_t padded_rows, int64_t inter_size,
@@ -1297,10 +1333,20 @@ mi_status run_delta(const char* what, const void* act, int64_t padded_rows, int6
   }
 
   const int nch = static_cast<int>(H / EXP_CW);
-  ExpandArgs ea{tok_list, tiles, counters, u2, blk_b, blk_tl, blk_f, tinfo, out, ly.cap,
+  // Finalize in two passes when the workspace also holds an fp32 [T, H] delta:
+  // the expand writes the delta there and finalize_combine_kernel reads whole
+  // FC2 rows.  Otherwise the expand's write-out adds the rows itself.
+  const size_t scratch_off = align256(ly.total);
+  const bool two_pass = fc2 != nullptr &&
+                        workspace_bytes >= scratch_off + static_cast<size_t>(T) * H * 4 &&
+                        T * (H / 8) < (1LL << 38);  // combine grid below 2^30 workgroups
+  float* scratch = two_pass ? reinterpret_cast<float*>(ws + scratch_off) : nullptr;
+  const int out_kind = out_dtype == MI_F32 ? 1 : (out_dtype == MI_F16 ? 2 : 0);
+  ExpandArgs ea{tok_list, tiles, counters, u2, blk_b, blk_tl, blk_f, tinfo,
+                two_pass ? static_cast<void*>(scratch) : out, ly.cap,
                 static_cast<int>(L), static_cast<int>(H), static_cast<int>(rank), ly.maxblk,
-                ntiles, nch, out_dtype == MI_F32 ? 1 : (out_dtype == MI_F16 ? 2 : 0),
-                fc2, perm, topk_weights,
+                ntiles, nch, two_pass ? 1 : out_kind,
+                two_pass ? nullptr : fc2, perm, topk_weights,
                 fc2_dtype == MI_F32 ? 1 : (fc2_dtype == MI_F16 ? 2 : 0),
                 static_cast<int>(top_k), static_cast<int>(padded_rows)};
   // whole runs of 8 tiles x nch chunks, rounded to a multiple of the 8 XCDs
@@ -1324,7 +1370,16 @@ mi_status run_delta(const char* what, const void* act, int64_t padded_rows, int6
     default: MI_REQUIRE(false, "bgmv_moe_gemm2_lora_delta: no expand variant (rank %lld)",
                         (long long)rank);
   }
-  return launch_status("bgmv_moe_gemm2_lora_delta (expand)");
+  st = launch_status("bgmv_moe_gemm2_lora_delta (expand)");
+  if (st != MI_OK || !two_pass) return st;
+  ExpandArgs fa = ea;
+  fa.out = out;
+  fa.out_kind = out_kind;
+  fa.fc2 = fc2;
+  const long items = T * (H / 8);
+  hipLaunchKernelGGL(finalize_combine_kernel, dim3(static_cast<unsigned>((items + 255) / 256)),
+                     dim3(256), 0, s, fa, static_cast<const float*>(scratch), static_cast<int>(T));
+  return launch_status("moe_fc2_finalize_lora (combine)");
 }
 
 }  // namespace

@@ -5,7 +5,8 @@ import pytest
 import torch
 
 import synth
-from moe_expert_grouped_amd import bgmv_moe_gemm2_lora_delta, moe_finalize_lora
+from moe_expert_grouped_amd import (bgmv_moe_gemm2_lora_delta, delta_workspace_bytes,
+                                    moe_finalize_lora)
 from oracle.finalize import moe_finalize
 from oracle.formats import f64_to_bf16_bits, f64_to_f16_bits
 from tests.parity import bits16, check_close, to_f64
@@ -23,15 +24,21 @@ def fc2_host(fc2):
     return bits16(fc2)
 
 
-def run_fin(case, tb, fc2, out_dtype=torch.bfloat16, **over):
+def run_fin(case, tb, fc2, out_dtype=torch.bfloat16, fused=False, **over):
+    """The finalize; ``fused`` gives it only the delta's workspace, which
+    selects the single-pass path (the default workspace selects two passes)."""
     fa, wa, sa, fb, wb, sb = tb
     kw = dict(perm=case.perm, lora_ids=case.lora_ids, scale=case.scale, num_adapters=case.L)
     kw.update(over)
     dev = case.act.device
+    ws = None
+    if fused:
+        ws = torch.empty(delta_workspace_bytes(case.T, case.top_k, case.E, kw["num_adapters"],
+                                               case.rank), dtype=torch.uint8, device=dev)
     out = moe_finalize_lora(fc2, case.act, kw["perm"], wa.to(dev), sa, wb.to(dev), sb,
                             case.topk_ids, case.topk_weights, kw["lora_ids"], case.rank, case.H,
                             num_adapters=kw["num_adapters"], lora_dtype=case.act.dtype,
-                            scale=kw["scale"], out_dtype=out_dtype)
+                            scale=kw["scale"], out_dtype=out_dtype, workspace=ws)
     torch.cuda.synchronize()
     return out
 
@@ -63,9 +70,11 @@ def test_integer_probe_bitwise(gpu, fc2_dtype, r, I):
     case, fc2 = int_case(201, fc2_dtype, r=r, I=I)
     tb = tables(case, scattered=True)
     ref = oracle_fin(case, tb, fc2)
-    assert np.array_equal(bits16(run_fin(case, tb, fc2)), f64_to_bf16_bits(ref))
-    assert np.array_equal(bits16(run_fin(case, tb, fc2, torch.float16)), f64_to_f16_bits(ref))
-    assert np.array_equal(to_f64(run_fin(case, tb, fc2, torch.float32)), ref)
+    for fused in (False, True):  # two passes, and the single-pass write-out
+        assert np.array_equal(bits16(run_fin(case, tb, fc2, fused=fused)), f64_to_bf16_bits(ref))
+        assert np.array_equal(bits16(run_fin(case, tb, fc2, torch.float16, fused=fused)),
+                              f64_to_f16_bits(ref))
+        assert np.array_equal(to_f64(run_fin(case, tb, fc2, torch.float32, fused=fused)), ref)
 
 
 def test_no_adapters_is_the_plain_combine(gpu):
@@ -96,6 +105,11 @@ def test_random_and_equal_to_delta_plus_combine(gpu):
     out = run_fin(case, tb, fc2)
     ref = oracle_fin(case, tb, fc2)
     check_close(to_f64(out), ref, "finalize medium")
+    # the two paths do the same arithmetic in the same order: bitwise equal
+    for dt, it in ((torch.bfloat16, torch.int16), (torch.float32, torch.int32)):
+        two = run_fin(case, tb, fc2, dt).view(it)
+        one = run_fin(case, tb, fc2, dt, fused=True).view(it)
+        assert torch.equal(two, one), f"two-pass and single-pass finalize differ ({dt})"
     # the unfused composition: delta (fp32) + the combine in torch (fp32)
     fa, wa, sa, fb, wb, sb = tb
     delta = bgmv_moe_gemm2_lora_delta(case.act, case.perm, wa.to(gpu), sa, wb.to(gpu), sb,
