@@ -240,3 +240,21 @@ def test_fp16_lora_far_from_one(gpu, act_mul, a_mul):
     err = np.abs(out - ref).max()
     assert err <= 1e-5 * np.abs(ref).max(), (err, np.abs(ref).max())
     check_close(to_f64(run_gpu(case, tb)), ref, "fp16 delta far from one")
+
+
+@pytest.mark.parametrize("T,top_k,E,L,r,I,H", [
+    (40, 32, 40, 3, 16, 64, 128),     # the largest top_k (tiles of 32 tokens)
+    (64, 4, 512, 2, 8, 64, 128),      # the largest expert count
+    (24, 3, 5, 2, 128, 64, 256),      # the largest rank (8 rank chunks of 16)
+    (96, 2, 3, 40, 8, 128, 128),      # many adapters, few tokens each
+])
+def test_integer_probe_at_the_limits(gpu, T, top_k, E, L, r, I, H):
+    """Every fp32 intermediate is exact, so the output is the exact delta
+    rounded once, at the largest top_k, expert count and rank the entry
+    point takes, and with many adapters."""
+    case = to_dev(synth.delta_int_probe(seed=T + E + r, T=T, top_k=top_k, E=E, I=I, H=H, L=L,
+                                        r=r), gpu)
+    tb = tables(case, scattered=True)
+    ref = run_oracle(case, tb)
+    assert np.array_equal(bits16(run_gpu(case, tb)), f64_to_bf16_bits(ref))
+    assert np.array_equal(to_f64(run_gpu(case, tb, torch.float32)), ref)

@@ -157,3 +157,21 @@ def test_fp16_random_ragged_fp16_out(gpu):
         out = grouped_mm_bf16(a.to(gpu), b.to(gpu), mi.to(gpu), out_dtype=torch.float16)
         torch.cuda.synchronize()
         check_close(to_f64(out)[written], ref[written], f"fp16 ragged avg={avg}")
+
+
+def test_limits_of_the_walk(gpu):
+    """1024 experts (the largest batch), most of them empty, one row in some,
+    n=256 (the smallest n), and a long K (k=8192) with a single-row group."""
+    rng = np.random.default_rng(11)
+    counts = np.zeros(1024, dtype=np.int64)
+    live = rng.choice(1024, 40, replace=False)
+    counts[live] = rng.integers(1, 300, 40)
+    counts[live[:5]] = 1
+    case = synth.grouped_int_probe(seed=12, counts=tuple(counts.tolist()), n=256, k=64)
+    ref, written = _oracle(case)
+    out = _run(case, gpu)
+    assert np.array_equal(bits16(out)[written], f64_to_bf16_bits(ref[written]))
+    big = synth.grouped_int_probe(seed=13, counts=(1, 0, 2), n=256, k=8192, lo=-1, hi=1)
+    ref, written = _oracle(big)
+    out32 = _run(big, gpu, torch.float32)
+    assert np.array_equal(to_f64(out32)[written], ref[written])
