@@ -887,10 +887,13 @@ __device__ __forceinline__ void add_rows(const Route& rt, const Rows8& x, f32x4&
 // are in flight together.
 template <typename DeltaFn>
 __device__ __forceinline__ void write_tile(const ExpandArgs& p, const Tile& tile, int h0,
-                                           DeltaFn delta) {
+                                           DeltaFn delta, const int* s_tok = nullptr) {
   const int tid = threadIdx.x;
   const int nit = tile.count * (EXP_CW / 8);
-  auto tok = [&](int i) { return gld<int>(p.tok_list + tile.start + i / (EXP_CW / 8)); };
+  // the tile's token ids, from LDS when the caller staged them there
+  auto tok = [&](int i) {
+    return s_tok ? s_tok[i / (EXP_CW / 8)] : gld<int>(p.tok_list + tile.start + i / (EXP_CW / 8));
+  };
   auto colof = [&](int i) { return h0 + (i % (EXP_CW / 8)) * 8; };
   if (p.fc2 == nullptr) {
     for (int i = tid; i < nit; i += NT_EXP) {
@@ -1113,6 +1116,7 @@ template <int NB, bool PART, bool F16>
 __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
   __shared__ __attribute__((aligned(16))) float s_acc[(EXP_TT + 16) * EXP_CW];  // + spare rows
   __shared__ const uint16_t* s_bp[MAX_BLOCKS];  // B_le of each block
+  __shared__ int s_tok[EXP_TT];                 // the tile's token ids
 
   // Workgroup order: the (column chunk, tile) pairs are taken in runs of
   // TB tiles -- all chunks of a run, tiles fastest -- and every XCD gets a
@@ -1125,23 +1129,42 @@ __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
   const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   const int run = lin / (TB * p.nch), rem = lin % (TB * p.nch);
   const int ch = rem / TB, ti = run * TB + rem % TB;
-  if (ti >= p.max_tiles || ti >= gld<int>(p.counters)) return;
+  if (ti >= p.max_tiles) return;
+  // the tile, its block count and its blocks' B_le addresses are read
+  // together (all lie inside the workspace whatever the tile count); the
+  // count decides afterwards whether the tile exists
+  const int ntile = gld<int>(p.counters);
   const Tile tile = load_tile(p.tiles + ti);
+  const int nblk0 = gld<int>(p.tinfo + 2 * ti);
+  const int dup0 = gld<int>(p.tinfo + 2 * ti + 1);
   const int tid = threadIdx.x;
+  const int64_t* bb = p.blk_b + static_cast<long>(ti) * p.maxblk;
+  int64_t bpre[(MAX_BLOCKS + NT_EXP - 1) / NT_EXP];
+#pragma unroll
+  for (int k = 0; k < (MAX_BLOCKS + NT_EXP - 1) / NT_EXP; ++k) {
+    const int i = tid + k * NT_EXP;
+    if (i < p.maxblk) bpre[k] = gld<int64_t>(bb + i);
+  }
+  if (ti >= ntile) return;
   const int h0 = ch * EXP_CW;
+  // the tile's token ids, for the write-out
+  for (int i = tid; i < tile.count; i += NT_EXP) s_tok[i] = gld<int>(p.tok_list + tile.start + i);
 
   if (tile.bucket >= p.L) {  // no adapter: a +0 delta (plus the combine when finalizing)
+    __syncthreads();  // s_tok
     write_tile(p, tile, h0, [](int, f32x4& v0, f32x4& v1) {
       v0 = f32x4{0.f, 0.f, 0.f, 0.f};
       v1 = f32x4{0.f, 0.f, 0.f, 0.f};
-    });
+    }, s_tok);
     return;
   }
-  const int nblk = gld<int>(p.tinfo + 2 * ti);
-  const bool dup = gld<int>(p.tinfo + 2 * ti + 1) != 0;
-  const int64_t* bb = p.blk_b + static_cast<long>(ti) * p.maxblk;
-  for (int i = tid; i < nblk; i += NT_EXP)
-    s_bp[i] = reinterpret_cast<const uint16_t*>(gld<int64_t>(bb + i));
+  const int nblk = nblk0;
+  const bool dup = dup0 != 0;
+#pragma unroll
+  for (int k = 0; k < (MAX_BLOCKS + NT_EXP - 1) / NT_EXP; ++k) {
+    const int i = tid + k * NT_EXP;
+    if (i < nblk) s_bp[i] = reinterpret_cast<const uint16_t*>(bpre[k]);
+  }
   for (int i = tid * 4; i < tile.count * EXP_CW; i += NT_EXP * 4)
     *reinterpret_cast<f32x4*>(s_acc + i) = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
@@ -1161,7 +1184,7 @@ __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
     const int tl = i / (EXP_CW / 8), c = (i % (EXP_CW / 8)) * 8;
     v0 = a[acc_chunk(tl, c / 4)];
     v1 = a[acc_chunk(tl, c / 4 + 1)];
-  });
+  }, s_tok);
 }
 
 int num_cus() {
