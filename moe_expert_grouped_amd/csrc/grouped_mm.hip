@@ -8,7 +8,12 @@
 // that table -- empty experts own no tile and no row is padded in memory
 // (the device-walk backend's behaviour described on the same page).
 //
-// Kernel structure
+// Two kernels, chosen from host sizes: grouped_mm_kernel (below) for groups
+// averaging fewer than 192 rows, grouped_mm_big_kernel (further down, with
+// its own notes) for larger ones; the big kernel also serves FC1, whose
+// epilogue applies the SwiGLU activation.
+//
+// grouped_mm_kernel structure
 //   * tile BM x BN, K step 64; WM x WN waves, each owning a (BM/WM) x (BN/WN)
 //     sub-tile of 32x32 v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulators);
 //   * global -> registers -> LDS, one barrier per K step; P K steps of global
