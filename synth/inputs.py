@@ -24,6 +24,8 @@ __all__ = [
     "bf16_ints",
     "route",
     "routing_ids",
+    "softmax_weights",
+    "distinct_topk",
     "zipf_counts",
     "sf_buffer_bytes",
     "GroupedCase",
