@@ -173,7 +173,8 @@ __global__ __launch_bounds__(256) void rp_rows_kernel(const uint8_t* __restrict_
 #pragma unroll
         for (int u = 0; u < ROWS_UNROLL; ++u) {
           const int64_t c = c0 + 64 * u + lane;
-          if (c < cpr) gst<u32x4>(dst + c * 16, d[u]);
+          // streaming stores: the permuted rows are not read again by this kernel
+          if (c < cpr) __builtin_nontemporal_store(d[u], reinterpret_cast<u32x4*>(dst + c * 16));
         }
       }
     }
