@@ -804,7 +804,9 @@ __device__ __forceinline__ void fc2_load8(const void* base, int kind, long off, 
     x1 = f32x4{static_cast<float>(h[4]), static_cast<float>(h[5]), static_cast<float>(h[6]),
                static_cast<float>(h[7])};
   } else {
-    const u32x4 v = gld<u32x4>(static_cast<const uint16_t*>(base) + off);
+    // streaming loads: each FC2 row piece is read once
+    const u32x4 v = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off));
     x0 = f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
                __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
     x1 = f32x4{__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
@@ -832,7 +834,8 @@ __device__ __forceinline__ void store_out8(const ExpandArgs& p, int t, int col, 
     w.y = pack_bf16x2(v0.z, v0.w);
     w.z = pack_bf16x2(v1.x, v1.y);
     w.w = pack_bf16x2(v1.z, v1.w);
-    gst<u32x4>(static_cast<uint16_t*>(p.out) + o, w);
+    // streaming store: the output is not read again here
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + o));
   }
 }
 
@@ -945,7 +948,9 @@ __global__ __launch_bounds__(256) void finalize_combine_kernel(ExpandArgs p, con
   const int t = static_cast<int>(i / cpr);
   const int col = static_cast<int>(i - t * cpr) * 8;
   const float* d = delta + static_cast<long>(t) * p.H + col;
-  f32x4 v0 = gld<f32x4>(d), v1 = gld<f32x4>(d + 4);
+  // streaming loads: the fp32 delta is read once
+  f32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(d));
+  f32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(d + 4));
   for (int j0 = 0; j0 < p.top_k; j0 += FIN_KB) {
     const Route rt = load_route(p, t, j0);
     add_rows(rt, load_rows(p, rt, col), v0, v1);
