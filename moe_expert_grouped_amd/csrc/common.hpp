@@ -97,5 +97,10 @@ template <typename T>
 __device__ __forceinline__ void gst(void* p, const T& v) {
   *(MI_GLOBAL T*)(p) = v;
 }
+// a streaming (non-temporal) global load, for data read once
+template <typename T>
+__device__ __forceinline__ T gld_nt(const void* p) {
+  return __builtin_nontemporal_load((const MI_GLOBAL T*)(p));
+}
 
 }  // namespace mi

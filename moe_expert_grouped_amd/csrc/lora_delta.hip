@@ -562,7 +562,7 @@ __global__ __launch_bounds__(64 * SHR_WAVES) void shrink_kernel(ShrinkArgs p) {
     if (st < nst) {
       const int k0 = st * KC;
 #pragma unroll
-      for (int j = 0; j < NLA; ++j) ra[j] = gld<u32x4>(asrc[j] + k0);
+      for (int j = 0; j < NLA; ++j) ra[j] = gld_nt<u32x4>(asrc[j] + k0);  // rows read once
 #pragma unroll
       for (int j = 0; j < NLB; ++j) rb[j] = gld<u32x4>(bsrc[j] + k0);
     }
@@ -719,7 +719,8 @@ __global__ __launch_bounds__(256, 2) void shrink_le_kernel(ShrinkLeArgs p) {
       auto gload = [&](u32x4 (&ra)[NLA], int s) {
         if (s < nst) {
 #pragma unroll
-          for (int jj = 0; jj < NLA; ++jj) ra[jj] = gld<u32x4>(asrc[jj] + s * SLE_KC);
+          for (int jj = 0; jj < NLA; ++jj)  // activation rows are read once
+            ra[jj] = gld_nt<u32x4>(asrc[jj] + s * SLE_KC);
         }
       };
       auto consume = [&](u32x4 (&ra)[NLA], int s) {
