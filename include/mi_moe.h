@@ -124,7 +124,8 @@ MI_API mi_status mi_grouped_mm_swiglu(const void* a, int64_t m_rows, int64_t k, 
  *
  *   act          lora_dtype [padded_rows, inter_size]  permuted post-activation rows;
  *                lora_dtype (MI_BF16 or MI_F16, "bf16/fp16" in the parameter list) is
- *                also the element type of both LoRA banks
+ *                also the element type of both LoRA banks.  May be NULL when
+ *                padded_rows == 0 (every slot is then inactive and nothing is read)
  *   expanded_idx_to_permuted_idx  int32 [num_tokens * top_k]; < 0 = inactive slot
  *   w_ptr_a      int64 [num_experts]: byte address (16-byte aligned) of A_down[0,e], a [rank, inter_size]
  *                block; adapter l starts lora_stride_a ELEMENTS later
@@ -170,7 +171,8 @@ MI_API mi_status mi_moe_fc2_lora_delta(const void* act, int64_t padded_rows, int
  * formed in fp32 (delta first, then the slots in order) and rounded once to
  * out_dtype; the delta is never rounded on its own.
  *   fc2          fc2_dtype [padded_rows, hidden_size]: the FC2 grouped-GEMM output in
- *                permuted row order (MI_BF16, MI_F16 or MI_F32), 16-byte aligned
+ *                permuted row order (MI_BF16, MI_F16 or MI_F32), 16-byte aligned;
+ *                not read (and may be NULL) when padded_rows == 0
  *   perm, topk_weights: as for the delta; a slot whose permuted row is < 0 or
  *                >= padded_rows is not routed here and contributes nothing (to the
  *                combine and to the delta); every other slot's row is combined with

@@ -1269,13 +1269,16 @@ mi_status run_delta(const char* what, const void* act, int64_t padded_rows, int6
   MI_REQUIRE(out_dtype == MI_BF16 || out_dtype == MI_F32 || out_dtype == MI_F16,
              "bgmv_moe_gemm2_lora_delta: out_dtype must be bf16, fp16 or fp32");
   if (T == 0) return MI_OK;
+  // with no activation rows every slot is inactive: the delta is +0 and the
+  // finalize has no FC2 row to combine, so neither act nor fc2 is read
+  if (padded_rows == 0) fc2 = nullptr;
   MI_REQUIRE(out != nullptr, "bgmv_moe_gemm2_lora_delta: out is null");
   MI_REQUIRE(aligned16(out), "bgmv_moe_gemm2_lora_delta: out must be 16-byte aligned");
   MI_REQUIRE(lora_ids != nullptr && topk_ids != nullptr && topk_weights != nullptr &&
                  perm != nullptr,
              "bgmv_moe_gemm2_lora_delta: index/weight tensors must be non-null");
   if (L > 0)
-    MI_REQUIRE(act != nullptr && w_ptr_a != nullptr && w_ptr_b != nullptr,
+    MI_REQUIRE((act != nullptr || padded_rows == 0) && w_ptr_a != nullptr && w_ptr_b != nullptr,
                "bgmv_moe_gemm2_lora_delta: act and the pointer tables must be non-null");
   MI_REQUIRE(aligned16(act), "bgmv_moe_gemm2_lora_delta: activation rows must be 16-byte aligned");
   const Layout ly = layout(T, top_k, E, L, rank);
@@ -1437,7 +1440,7 @@ extern "C" mi_status mi_moe_fc2_finalize_lora(
   mi::clear_error();
   MI_REQUIRE(fc2_dtype == MI_BF16 || fc2_dtype == MI_F16 || fc2_dtype == MI_F32,
              "moe_fc2_finalize_lora: fc2_out dtype must be bf16, fp16 or fp32");
-  if (T > 0) {
+  if (T > 0 && padded_rows > 0) {
     MI_REQUIRE(fc2 != nullptr, "moe_fc2_finalize_lora: fc2_out is null");
     MI_REQUIRE(mi::aligned16(fc2), "moe_fc2_finalize_lora: fc2_out must be 16-byte aligned");
   }
