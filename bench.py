@@ -50,6 +50,10 @@ def parse():
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                    "'--only nvfp4_raw,copy_probe' into the committed traffic summary")
+    p.add_argument("--pmc-table", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU: per-kernel HBM bytes from two rocprofv3 --pmc runs (FETCH_SIZE, "
+                   "WRITE_SIZE) of '--only grouped_gemm,lora_delta,copy_probe', calibrated on "
+                   "the copy probe")
     return p.parse_args()
 
 
@@ -137,10 +141,58 @@ def pmc_summary(fetch_dir, write_dir):
           f"(fetch scale {f_fac:.3f}, write scale {w_fac:.3f})")
 
 
+def pmc_table(fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE per dispatch of every library kernel of the
+    grouped-GEMM and delta run, scaled like pmc_summary, as a Markdown table."""
+    is_copy = lambda k: "at::native" in k and "neg_kernel" in k
+    fr, wr = _pmc_rows(fetch_dir), _pmc_rows(write_dir)
+    cp_f, _ = _pmc_avg(fr, "FETCH_SIZE", is_copy)
+    cp_w, _ = _pmc_avg(wr, "WRITE_SIZE", is_copy)
+    f_fac = COPY_PROBE_BYTES / (cp_f * 1024.0)
+    w_fac = COPY_PROBE_BYTES / (cp_w * 1024.0)
+
+    def short(k):
+        k = k.replace("void ", "").replace("mi::(anonymous namespace)::", "")
+        return k[:k.index("(")] if "(" in k else k
+
+    names = []
+    for r in fr:
+        if "mi::" in r["Kernel_Name"] and short(r["Kernel_Name"]) not in names:
+            names.append(short(r["Kernel_Name"]))
+    out = os.path.join(ROOT, "profiles", "grouped_gemm_c2_and_delta_c4_hbm_traffic.md")
+    with open(out, "w") as fh:
+        fh.write("# HBM traffic per kernel: grouped GEMM (E=8 x 128 rows, k=4096, n=2048) and "
+                 "the FC2 LoRA delta (T=8192, top_k=8, E=64, I=2048, H=4096, 8 adapters r=16)\n\n"
+                 "Commands (repo root, one MI355X; each pass its own run):\n\n```\n"
+                 "rocprofv3 --pmc FETCH_SIZE -d <FETCH_DIR> -o f --output-format csv -- python3 "
+                 "bench.py --only grouped_gemm,lora_delta,copy_probe --steps 3 --warmup 1 "
+                 "--no-cpu-baseline\n"
+                 "rocprofv3 --pmc WRITE_SIZE -d <WRITE_DIR> -o w --output-format csv -- python3 "
+                 "bench.py --only grouped_gemm,lora_delta,copy_probe --steps 3 --warmup 1 "
+                 "--no-cpu-baseline\n"
+                 "python3 bench.py --pmc-table <FETCH_DIR> <WRITE_DIR>\n```\n\n"
+                 "Counters are KiB per dispatch, scaled by the factors that map the same counters "
+                 f"on the copy probe (512 MiB read + 512 MiB written) to its size: fetch "
+                 f"{f_fac:.4f}, write {w_fac:.4f}.  They count what the L2 fetches from and "
+                 "writes to memory (the MALL included).  Algorithmic bytes per call: grouped GEMM "
+                 "146.8 MB, delta 384.7 MB (all four kernels).\n\n"
+                 "| kernel | dispatches | fetch MB | write MB | total MB |\n|---|---:|---:|---:|---:|\n")
+        for n in names:
+            pick = lambda k, n=n: "mi::" in k and short(k) == n
+            f, nd = _pmc_avg(fr, "FETCH_SIZE", pick)
+            w, _ = _pmc_avg(wr, "WRITE_SIZE", pick)
+            fb, wb = f * 1024.0 * f_fac / 1e6, w * 1024.0 * w_fac / 1e6
+            fh.write(f"| {n} | {nd} | {fb:.1f} | {wb:.1f} | {fb + wb:.1f} |\n")
+    print(f"wrote {out}")
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.pmc_table:
+        pmc_table(*args.pmc_table)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (the path is "
