@@ -247,6 +247,7 @@ def test_fp16_lora_far_from_one(gpu, act_mul, a_mul):
     (64, 4, 512, 2, 8, 64, 128),      # the largest expert count
     (24, 3, 5, 2, 128, 64, 256),      # the largest rank (8 rank chunks of 16)
     (96, 2, 3, 40, 8, 128, 128),      # many adapters, few tokens each
+    (16500, 2, 4, 2, 8, 64, 128),     # many tokens: 258 tiles over two adapters
 ])
 def test_integer_probe_at_the_limits(gpu, T, top_k, E, L, r, I, H):
     """Every fp32 intermediate is exact, so the output is the exact delta
