@@ -253,7 +253,7 @@ MI_API mi_status mi_moe_permute_rows(const void* x, int64_t num_tokens, int64_t 
  *   off      : out = bf16( alpha*acc [+ bias] )
  * acc = dequant(a) @ dequant(b)^T accumulated in fp32; one rounding to bf16.
  *
- *   a, b        uint8 [m, k/2], [n, k/2]: two E2M1 codes per byte, element 2i in
+ *   a, b        uint8 [m, k/2], [n, k/2]: E2M1 codes, a pair in each byte, element 2i in
  *               the low nibble
  *   a_sf, b_sf  UE4M3 scales, one per 16 elements along k, 128x4-tiled with rows
  *               padded to 128 (tile = 128 rows x 4 scale columns = 512 bytes,
@@ -267,7 +267,7 @@ MI_API mi_status mi_moe_permute_rows(const void* x, int64_t num_tokens, int64_t 
  *               path, bitwise identical to the off call.
  *   b_folded    prepared path: bf16 [n, rank] from mi_prepare_lora_fold, with its
  *               fold_flags word; bit 0 set (zero adapter) -> the off path.
- *   bias        bf16 [n] or NULL, added in fp32 before the single rounding
+ *   bias        bf16 [n] or NULL, summed in fp32, then the one rounding
  *   out         bf16 [m, n]
  * Requirements: m >= 1, n >= 1, k % 256 == 0 (k >= 256); rank % 8 == 0 and
  * 8 <= rank <= 128 when an adapter is given; not both adapter forms; a prepared

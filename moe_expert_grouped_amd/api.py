@@ -362,10 +362,11 @@ def prepare_nvfp4_lora_adapter(lora_b: torch.Tensor, lora_scale: torch.Tensor,
                                ) -> PreparedNvFp4LoraAdapter:
     """Fold one adapter for the prepared path.
 
-    ``out=None``: one device-to-host copy of (lora_scale, alpha) checks
-    ``alpha != 0`` and a finite ratio (ValueError otherwise), then the fold
-    kernel runs.  ``out=adapter``: in-place refold with no host read; alpha
-    must be the adapter's own alpha tensor and lora_b keeps its shape/device.
+    ``out=None``: lora_scale and alpha are read back to the host once; a zero
+    alpha or a ratio that is not finite raises ValueError, otherwise the fold
+    kernel runs.  ``out=adapter``: in-place refold with no host read; the
+    alpha tensor has to be the one the adapter was prepared with, and lora_b
+    keeps its shape and device.
     """
     _need(lora_b.dtype == torch.bfloat16 and lora_b.dim() == 2 and lora_b.is_contiguous(),
           "prepare_nvfp4_lora_adapter: lora_b must be contiguous bf16 [N, r]")
@@ -386,7 +387,7 @@ def prepare_nvfp4_lora_adapter(lora_b: torch.Tensor, lora_scale: torch.Tensor,
         flags = torch.zeros(1, dtype=torch.int32, device=lora_b.device)
         _fold(lora_b, lora_scale, alpha, b_folded, flags)
         return PreparedNvFp4LoraAdapter(lora_b, lora_scale, alpha, b_folded, flags)
-    _need(alpha is out.alpha, "prepare_nvfp4_lora_adapter: alpha must be out's own alpha tensor")
+    _need(alpha is out.alpha, "prepare_nvfp4_lora_adapter: alpha must be the tensor the adapter was prepared with")
     _need(lora_b.shape == out.b_folded.shape and lora_b.device == out.b_folded.device,
           "prepare_nvfp4_lora_adapter: lora_b must keep out's [N, r] shape and device")
     _fold(lora_b, lora_scale, alpha, out.b_folded, out.fold_flags)

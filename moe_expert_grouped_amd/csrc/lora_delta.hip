@@ -1255,6 +1255,10 @@ mi_status run_delta(const char* what, const void* act, int64_t padded_rows, int6
              "bgmv_moe_gemm2_lora_delta: I = gemm1_activation_output.shape[1] must be a positive "
              "multiple of 8 (got %lld)", (long long)inter_size);
   MI_REQUIRE(H >= 1 && H < (1 << 30), "bgmv_moe_gemm2_lora_delta: hidden_size out of range");
+  // one B_le block is addressed through a 32-bit buffer range
+  MI_REQUIRE_SUPPORTED(H * rank * 2 < (1LL << 32),
+                       "bgmv_moe_gemm2_lora_delta: one B_down block (hidden_size x rank bf16) "
+                       "must stay below 4 GiB (got %lld x %lld)", (long long)H, (long long)rank);
   MI_REQUIRE_SUPPORTED(H % EXP_CW == 0,
                        "bgmv_moe_gemm2_lora_delta: hidden_size must be a multiple of %d (got %lld)",
                        EXP_CW, (long long)H);

@@ -48,11 +48,21 @@ __device__ __forceinline__ long sf_tile_word(int row, int col4, int n_col_tiles)
          ((row & 127) >> 5) * 4;
 }
 
-// UE4M3 byte -> fp16 pair (s, s); exact (4 significant bits, 2^-9 .. 448).
-__device__ __forceinline__ f16x2 scale_pair(uint32_t byte) {
-  const float s = __builtin_amdgcn_cvt_f32_fp8(byte, 0);
-  const _Float16 h = static_cast<_Float16>(s);
-  return f16x2{h, h};
+// The scale decode shared by the GEMM K loops and the dequantiser: the four
+// UE4M3 bytes of one 32-bit scale word (scale columns 4c .. 4c+3 of a row) as
+// fp16, two bytes per conversion -- s01 = (byte 0, byte 1), s23 = (byte 2,
+// byte 3).  Exact: a UE4M3 value has at most 4 significant bits and lies in
+// 2^-9 .. 448, inside fp16's normal range.
+__device__ __forceinline__ void ue4m3x4_to_f16(uint32_t w, f16x2& s01, f16x2& s23) {
+  s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+}
+
+// Scale byte c (0..3) of the word as an fp16 pair (s, s): the multiplier of
+// decode8 below.
+__device__ __forceinline__ f16x2 scale_splat(f16x2 s01, f16x2 s23, int c) {
+  const f16x2 v = c < 2 ? s01 : s23;
+  return (c & 1) ? f16x2{v.y, v.y} : f16x2{v.x, v.x};
 }
 
 // 8 E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
@@ -142,23 +152,16 @@ __device__ __forceinline__ void nv_kloop(f32x16 (&acc)[4][4], const NvOps& op, i
     // the 4 UE4M3 scale bytes of each row as fp16, two per conversion (exact)
     f16x2 sa01[FM], sa23[FM], sb01[FN], sb23[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      sa01[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.sa[i], 1.0f, false);
-      sa23[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.sa[i], 1.0f, true);
-    }
+    for (int i = 0; i < FM; ++i) ue4m3x4_to_f16(st.sa[i], sa01[i], sa23[i]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      sb01[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.sb[j], 1.0f, false);
-      sb23[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(st.sb[j], 1.0f, true);
-    }
-    auto splat = [](f16x2 v, int hi) { return hi ? f16x2{v.y, v.y} : f16x2{v.x, v.x}; };
+    for (int j = 0; j < FN; ++j) ue4m3x4_to_f16(st.sb[j], sb01[j], sb23[j]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {  // scale block t: MFMA steps 2t, 2t+1
       f16x2 psa[FM], psb[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) psa[i] = splat(t < 2 ? sa01[i] : sa23[i], t & 1);
+      for (int i = 0; i < FM; ++i) psa[i] = scale_splat(sa01[i], sa23[i], t);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) psb[j] = splat(t < 2 ? sb01[j] : sb23[j], t & 1);
+      for (int j = 0; j < FN; ++j) psb[j] = scale_splat(sb01[j], sb23[j], t);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int s = 2 * t + u;  // code word s of the lane's 8
@@ -532,7 +535,9 @@ __global__ void fold_kernel(const uint16_t* __restrict__ lora_b, long count,
 }
 
 // ---------------------------------------------------------------------------
-// dequant: one thread per 8 codes of one row, the GEMM's decoder
+// dequant: one thread per 8 codes of one row, with the GEMM's decoder (the
+// same scale-word conversion, scale selection and code conversion as the K
+// loop)
 // ---------------------------------------------------------------------------
 __global__ void dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sf,
                                int rows, int k, uint16_t* __restrict__ out) {
@@ -542,9 +547,12 @@ __global__ void dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t*
   const int row = static_cast<int>(idx / words), w = static_cast<int>(idx % words);
   const int col = w / 2;  // 8 elements per word, 16 per scale
   const int n_col_tiles = (k / 16 + 3) / 4;
-  const uint32_t sbyte = sf[sf_tile_word(row, col >> 2, n_col_tiles) + (col & 3)];
+  const uint32_t sword =
+      *reinterpret_cast<const uint32_t*>(sf + sf_tile_word(row, col >> 2, n_col_tiles));
+  f16x2 s01, s23;
+  ue4m3x4_to_f16(sword, s01, s23);
   const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + static_cast<long>(row) * (k / 2) + w * 4);
-  const u32x4 h = decode8(cw, scale_pair(sbyte));
+  const u32x4 h = decode8(cw, scale_splat(s01, s23, col & 3));
   u32x4 o;
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -667,8 +675,9 @@ extern "C" mi_status mi_nvfp4_dequant_bf16(const uint8_t* codes, const uint8_t* 
   MI_REQUIRE(k >= 64 && k % 64 == 0 && k < (1LL << 31), "nvfp4_dequant: K %% 64 == 0 required");
   MI_REQUIRE(codes && sf && out, "nvfp4_dequant: null pointer argument");
   MI_REQUIRE(sf_bytes >= sf_needed(rows, k), "nvfp4_dequant: scale buffer too small");
-  MI_REQUIRE(aligned16(out) && (reinterpret_cast<uintptr_t>(codes) & 3) == 0,
-             "nvfp4_dequant: misaligned buffers");
+  MI_REQUIRE(aligned16(out) && (reinterpret_cast<uintptr_t>(codes) & 3) == 0 &&
+                 (reinterpret_cast<uintptr_t>(sf) & 3) == 0,
+             "nvfp4_dequant: out must be 16-byte aligned, codes and sf 4-byte aligned");
   const long threads = rows * (k / 8);
   const int block = 256;
   hipLaunchKernelGGL(dequant_kernel, dim3((threads + block - 1) / block), dim3(block), 0,

@@ -4,13 +4,15 @@
 - fp16: IEEE binary16 (1 sign, 5 exponent bits with bias 15, 10 mantissa
   bits; subnormals at exponent 0) -- the other input and output type the
   grouped_mm_bf16 page lists.
-- E2M1 (the NVFP4 element code, ``flashinfer.gemm.mm_nvfp4_lora`` --
-  "E2M1 codes packed two per byte"): 1 sign, 2 exponent (bias 1), 1 mantissa
-  bit; magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.  The pages only name the
-  format; the values follow the OCP microscaling definition.
-- UE4M3 (the NVFP4 block scale, same page -- "UE4M3 block scales of 16 along
-  K"): an E4M3 byte (4 exponent bits, bias 7, 3 mantissa bits, subnormal at
-  exponent 0, 0x7F = NaN) whose sign bit is zero.
+- E2M1 (the NVFP4 element code; ``flashinfer.gemm.mm_nvfp4_lora``,
+  parameters a and b, stores two such codes in each byte): 1 sign,
+  2 exponent (bias 1), 1 mantissa bit; magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+  The pages only name the format; the values follow the OCP microscaling
+  definition.
+- UE4M3 (the NVFP4 block scale; same page, parameters a_sf and b_sf: one
+  scale for every 16 consecutive elements along K): an E4M3 byte (4 exponent
+  bits, bias 7, 3 mantissa bits, subnormal at exponent 0, 0x7F = NaN) whose
+  sign bit is zero.
 
 All decoders are exact: every value of these formats is a float64.
 """

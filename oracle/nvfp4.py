@@ -5,7 +5,7 @@ prepared-path bullets and the parameter list):
 
     out = alpha * (dequant(a) @ dequant(b)^T) + lora_scale * (d @ lora_b^T) [+ bias]
 
-- ``a`` is uint8 ``[M, K/2]``, ``b`` uint8 ``[N, K/2]``: two E2M1 codes per
+- ``a`` is uint8 ``[M, K/2]``, ``b`` uint8 ``[N, K/2]``: E2M1 codes, a pair in each
   byte, row-major;
 - ``a_sf`` / ``b_sf``: one UE4M3 scale per 16 elements along K, in the
   128x4-tiled layout with rows padded to 128;

@@ -3,8 +3,9 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Follows ``flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta`` (parameter
-``expanded_idx_to_permuted_idx``: it maps the expanded index
-``token*top_k + slot`` to the permuted row, negative for an inactive slot) and
+``expanded_idx_to_permuted_idx``: entry ``token*top_k + slot`` holds that
+slot's row in the permuted buffer, or a negative value when the slot is
+inactive) and
 ``flashinfer.grouped_mm.grouped_mm_bf16`` (parameter ``m_indptr``: cumulative
 row counts of the groups, one group per expert).
 

@@ -40,8 +40,10 @@ __all__ = [
     "delta_int_probe",
     "nvfp4_lora_case",
     "nvfp4_probe",
+    "nvfp4_scale_probe",
     "Nvfp4GroupedCase",
     "nvfp4_grouped_case",
+    "nvfp4_grouped_scale_probe",
     "Fc1Case",
     "fc1_case",
 ]
@@ -443,6 +445,48 @@ def nvfp4_probe(kind: str, seed: int = 103, M=128, N=256, K=256, r=16) -> Nvfp4C
                      lora_b, lora_scale, bias, K)
 
 
+def _selector(rows: int, K: int) -> torch.Tensor:
+    """uint8 ``[rows, K/2]`` codes with E2M1 1.0 (code 0x2) at element
+    ``(i, i % K)`` of row i and zeros elsewhere."""
+    codes = torch.zeros((rows, K // 2), dtype=torch.uint8)
+    i = torch.arange(rows)
+    col = i % K
+    codes[i, col // 2] = torch.where(col % 2 == 0, torch.tensor(0x02, dtype=torch.uint8),
+                                     torch.tensor(0x20, dtype=torch.uint8))
+    return codes
+
+
+def nvfp4_scale_probe(side: str, seed: int = 104, M=300, N=512, K=512) -> Nvfp4Case:
+    """Probes of the GEMM's own scale decode.  One operand has random codes
+    and scale bytes uniform over every finite UE4M3 code 0x00..0x7E; the
+    other selects one element per output (E2M1 1.0 at scale 1.0), so every
+    output is a single exact product, alpha 1, no LoRA and no bias:
+
+    - ``a``: ``b`` row n selects element n, so ``out[m, n] = dequant(a)[m, n]``
+      for ``n < K``;
+    - ``b``: ``a`` row m selects element m, so ``out[m, n] = dequant(b)[n, m]``
+      for ``m < K``.
+    """
+    g = gen(seed)
+    one = 0x38
+    if side == "a":
+        a = torch.randint(0, 256, (M, K // 2), generator=g).to(torch.uint8)
+        a_sf = _scale_codes(sf_buffer_bytes(M, K), 0x00, 0x7E, g, "cpu")
+        b = _selector(N, K)
+        b_sf = torch.full((sf_buffer_bytes(N, K),), one, dtype=torch.uint8)
+    elif side == "b":
+        a = _selector(M, K)
+        a_sf = torch.full((sf_buffer_bytes(M, K),), one, dtype=torch.uint8)
+        b = torch.randint(0, 256, (N, K // 2), generator=g).to(torch.uint8)
+        b_sf = _scale_codes(sf_buffer_bytes(N, K), 0x00, 0x7E, g, "cpu")
+    else:
+        raise ValueError(side)
+    return Nvfp4Case(f"nvfp4-scale-probe-{side} M={M} N={N} K={K}", a, b, a_sf, b_sf,
+                     torch.tensor([1.0], dtype=torch.float32), bf16_normal((M, 16), 1.0, g),
+                     bf16_normal((N, 16), 0.02, g), torch.tensor([0.0], dtype=torch.float32),
+                     None, K)
+
+
 @dataclass
 class Nvfp4GroupedCase:
     name: str
@@ -485,6 +529,36 @@ def nvfp4_grouped_case(seed: int = 6, device="cpu", counts=None, E=128, T=4096, 
         alpha = 0.005 + 0.015 * torch.rand(E, generator=g, device=device, dtype=torch.float32)
     return Nvfp4GroupedCase(f"nvfp4-grouped E={E} cum_m={cum} n={n} k={k}", a, a_sf, b, b_sf,
                             alpha.to(torch.float32), m_indptr.to(device), k)
+
+
+def nvfp4_grouped_scale_probe(side: str, counts, n=512, k=512, seed=105) -> Nvfp4GroupedCase:
+    """The scale-decode probes of :func:`nvfp4_scale_probe` through the
+    grouped walk: ``a`` side -- a random codes with scales over every finite
+    UE4M3 code, each expert's b selects element n for output column n;
+    ``b`` side -- a's row i selects element ``i % k``, the experts' b have
+    random codes and scales over every finite code.  alpha 1 for every
+    expert, so each output is one exact product."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = len(counts)
+    m_indptr = torch.zeros(E + 1, dtype=torch.int32)
+    m_indptr[1:] = torch.from_numpy(np.cumsum(counts)).to(torch.int32)
+    cum = int(m_indptr[-1])
+    g = gen(seed)
+    a_bytes, per = sf_buffer_bytes(cum, k), sf_buffer_bytes(n, k)
+    if side == "a":
+        a = torch.randint(0, 256, (cum, k // 2), generator=g).to(torch.uint8)
+        a_sf = _scale_codes(a_bytes, 0x00, 0x7E, g, "cpu")
+        b = _selector(n, k).unsqueeze(0).repeat(E, 1, 1)
+        b_sf = torch.full((E * per,), 0x38, dtype=torch.uint8)
+    elif side == "b":
+        a = _selector(cum, k)
+        a_sf = torch.full((a_bytes,), 0x38, dtype=torch.uint8)
+        b = torch.randint(0, 256, (E, n, k // 2), generator=g).to(torch.uint8)
+        b_sf = _scale_codes(E * per, 0x00, 0x7E, g, "cpu")
+    else:
+        raise ValueError(side)
+    return Nvfp4GroupedCase(f"nvfp4-grouped-scale-probe-{side} E={E} cum_m={cum} n={n} k={k}",
+                            a, a_sf, b, b_sf, torch.ones(E, dtype=torch.float32), m_indptr, k)
 
 
 @dataclass

@@ -99,6 +99,11 @@ def test_delta_validation():
     assert "strides" in _err(_delta(sa=1001))
     with pytest.raises(NotImplementedError):
         _lib.check(_delta(H=200))
+    # a B_down block of 2^32 bytes or more does not fit the kernels' 32-bit range
+    with pytest.raises(NotImplementedError, match="below 4 GiB"):
+        _lib.check(_delta(H=1 << 27, r=16))
+    with pytest.raises(NotImplementedError, match="below 4 GiB"):
+        _lib.check(_delta(H=1 << 25, r=64))
     assert "lora_dtype must be bf16 or fp16" in _err(_delta(ldt=_lib.MI_F32))
     L = _lib.lib()
     fin = lambda fc2, fdt, **kw: L.mi_moe_fc2_finalize_lora(fc2, fdt, *dict(

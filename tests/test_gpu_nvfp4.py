@@ -59,6 +59,45 @@ def test_identity_probe_bitwise(gpu):
     assert np.array_equal(got[want != 0x8000], want[want != 0x8000])
 
 
+def _same_up_to_zero_sign(got, want):
+    """Bitwise equality, except that the GEMM may return +0 where the exact
+    value is -0 (it sums exact zeros onto each product)."""
+    nz = (want & 0x7FFF) != 0
+    assert np.array_equal(got[nz], want[nz])
+    assert np.all((got[~nz] & 0x7FFF) == 0)
+
+
+@pytest.mark.parametrize("side", ["a", "b"])
+def test_gemm_scale_decode_all_codes_bitwise(gpu, side):
+    """The K loop's own UE4M3 decode over every finite scale code 0x00..0x7E,
+    on either operand: each output is one exact product (the other operand
+    selects one element at scale 1.0), so it must equal the exact dequantised
+    value bitwise."""
+    case = synth.nvfp4_scale_probe(side)
+    sf = case.a_sf if side == "a" else case.b_sf
+    assert set(sf.unique().tolist()) == set(range(0x7F))  # every finite code drawn
+    c = _dev(case, gpu)
+    out = mm_nvfp4_lora(c.a, c.b, c.a_sf, c.b_sf, c.alpha)
+    torch.cuda.synchronize()
+    want = f64_to_bf16_bits(_base(case))
+    M, N, K = case.M, case.N, case.K
+    if side == "a":
+        deq = NV.dequant(_np(case.a), _np(case.a_sf), K)[:, :N]
+    else:
+        deq = NV.dequant(_np(case.b), _np(case.b_sf), K)[:, :M].T
+    _same_up_to_zero_sign(want, f64_to_bf16_bits(deq))  # the probe is the identity it claims
+    _same_up_to_zero_sign(bits16(out), want)
+
+
+def test_zero_codes_scaled_probe(gpu):
+    """All codes zero with scales over every finite code: the product is +0
+    everywhere (no scale decodes to NaN or Inf)."""
+    c = _dev(synth.nvfp4_probe("zero_codes_scaled", M=200, N=512, K=512), gpu)
+    out = mm_nvfp4_lora(c.a, c.b, c.a_sf, c.b_sf, c.alpha)
+    torch.cuda.synchronize()
+    assert np.all(bits16(out) == 0)
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 256, 256), (300, 520, 512), (1, 1, 256)])
 def test_exact_probe_bitwise(gpu, M, N, K):
     case = _dev(synth.nvfp4_probe("exact", M=M, N=N, K=K), gpu)
@@ -223,3 +262,26 @@ def test_full_size_sampled(gpu):
     check_close(sel(prep), ref_prep, "prepared full")
     print(f"\nSQNR raw {sqnr_db(sel(raw), ref_raw):.1f} dB, prepared vs raw-formula "
           f"{sqnr_db(sel(prep), ref_raw):.1f} dB")
+    # the zero-adapter forms at this shape: bitwise the adapter-off output over
+    # the whole [4096, 8192] result
+    zero = torch.zeros(1, dtype=torch.float32, device=gpu)
+    negz = torch.tensor([-0.0], dtype=torch.float32, device=gpu)
+    ad0 = prepare_nvfp4_lora_adapter(case.lora_b, zero, case.alpha)
+    forms = {
+        "raw s=0": lambda o: mm_nvfp4_lora(case.a, case.b, case.a_sf, case.b_sf, case.alpha,
+                                           case.d, case.lora_b, zero, bias=case.bias, out=o),
+        "raw s=-0": lambda o: mm_nvfp4_lora(case.a, case.b, case.a_sf, case.b_sf, case.alpha,
+                                            case.d, case.lora_b, negz, bias=case.bias, out=o),
+        "s=None": lambda o: mm_nvfp4_lora(case.a, case.b, case.a_sf, case.b_sf, case.alpha,
+                                          case.d, case.lora_b, None, bias=case.bias, out=o),
+        "prepared s=0": lambda o: mm_nvfp4_lora(case.a, case.b, case.a_sf, case.b_sf,
+                                                case.alpha, case.d, lora_adapter=ad0,
+                                                bias=case.bias, out=o),
+    }
+    offv = off.view(torch.int16)
+    buf = torch.empty_like(off)
+    for name, fn in forms.items():
+        buf.fill_(7.0)
+        fn(buf)
+        torch.cuda.synchronize()
+        assert torch.equal(buf.view(torch.int16), offv), name

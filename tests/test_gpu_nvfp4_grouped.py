@@ -44,6 +44,24 @@ def test_exact_probe_bitwise(gpu, counts, n, k):
     assert np.array_equal(to_f64(out32)[written], ref[written])
 
 
+@pytest.mark.parametrize("side", ["a", "b"])
+def test_scale_decode_all_codes_bitwise(gpu, side):
+    """The grouped K loop's UE4M3 decode over every finite scale code, on the
+    activation side and on the expert-weight side: each output is one exact
+    product, so it must equal the oracle bitwise (up to the sign of zero)."""
+    c = synth.nvfp4_grouped_scale_probe(side, counts=(0, 130, 1, 300, 0, 129))
+    sf = c.a_sf if side == "a" else c.b_sf
+    assert set(sf.unique().tolist()) == set(range(0x7F))
+    ref, written = oracle_grouped(*np_case(c), c.k)
+    want = f64_to_bf16_bits(ref[written])
+    got = bits16(run(c, gpu))[written]
+    nz = (want & 0x7FFF) != 0
+    assert np.array_equal(got[nz], want[nz])
+    assert np.all((got[~nz] & 0x7FFF) == 0)
+    out32 = to_f64(run(c, gpu, torch.float32))[written]
+    assert np.array_equal(out32, ref[written])
+
+
 def test_rows_outside_groups_untouched(gpu):
     c = synth.nvfp4_grouped_case(seed=3, counts=(5, 0, 40), n=256, k=256, exact=True)
     g = synth.gen(9)

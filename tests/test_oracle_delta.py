@@ -164,3 +164,22 @@ def test_pointer_table_and_stride_semantics():
     flat_b, wb, sb = scattered_bank(case.B, seed=2)
     tables = ((oracle_bank(flat_a), wa, sa), (oracle_bank(flat_b), wb, sb))
     assert np.array_equal(run_oracle(case, tables=tables), run_oracle(case))
+
+
+def test_token_subset_equals_rows_of_the_whole():
+    """The ``tokens=`` path (what the at-scale GPU tests sample through) gives
+    the rows of the all-token result and of the literal loops, in the order
+    asked, repeats and tokens without adapter included."""
+    case = small_case(13)
+    full = run_oracle(case)
+    lit = literal_loops(case)
+    S = [5, 0, 3, 3, 1]
+    (wa, sa), (wb, sb) = contiguous_tables(case.A), contiguous_tables(case.B)
+    sub = moe_fc2_lora_delta(bits16(case.act), case.perm.numpy(), oracle_bank(case.A), wa.numpy(),
+                             sa, oracle_bank(case.B), wb.numpy(), sb, case.topk_ids.numpy(),
+                             case.topk_weights.numpy(), case.lora_ids.numpy(), case.rank, case.H,
+                             case.scale, tokens=S)
+    assert sub.shape == (len(S), case.H)
+    assert np.array_equal(sub, full[S])
+    assert np.allclose(sub, lit[S], rtol=1e-12, atol=1e-14)
+    assert not sub[4].any()  # token 1 has no adapter

@@ -66,3 +66,15 @@ def test_fp32_rows_equal_bf16_rows_of_the_same_values():
     assert np.array_equal(a, b)
     h = moe_finalize(bits16(fc2.half()), "f16", perm.numpy(), w.numpy(), delta)
     assert np.allclose(h, a, rtol=1e-3, atol=1e-3)
+
+
+def test_token_subset_equals_rows_of_the_whole():
+    """``tokens=`` (used by the sampled GPU tests) returns the rows of the
+    all-token combine and of the literal loops, in the order asked."""
+    fc2, perm, w, delta = tiny(7)
+    full = moe_finalize(bits16(fc2), "bf16", perm.numpy(), w.numpy(), delta)
+    lit = literal(fc2, perm, w, delta)
+    S = [6, 2, 2, 0]
+    sub = moe_finalize(bits16(fc2), "bf16", perm.numpy(), w.numpy(), delta[S], tokens=S)
+    assert np.array_equal(sub, full[S])
+    assert np.allclose(sub, lit[S], rtol=1e-13, atol=1e-13)
