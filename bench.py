@@ -250,6 +250,9 @@ def trace_summary(out_md, trace_dir, command):
     kernels that run twice per step (a cold and a warm call, or raw and
     prepared), the eager dispatches are also split by their position in the
     step."""
+    import re
+    m_s, m_w = re.search(r"--steps\s+(\d+)", command), re.search(r"--warmup\s+(\d+)", command)
+    eager = (int(m_s.group(1)) if m_s else 20) + (int(m_w.group(1)) if m_w else 3)
     rows = _csv_rows(trace_dir, "*kernel_trace.csv")
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     per, lib = {}, set()
@@ -263,20 +266,22 @@ def trace_summary(out_md, trace_dir, command):
                  "Command (repo root, one MI355X):\n\n```\n"
                  f"rocprofv3 --kernel-trace --stats -d <DIR> -o trace --output-format csv -- "
                  f"{command}\npython3 bench.py --trace-summary <OUT_MD> <DIR> '<COMMAND>'\n```\n\n"
-                 "Every dispatch of the run, in microseconds (the trace's end minus start "
-                 "timestamps).  `all` counts every dispatch of the kernel; for kernels that run "
-                 "twice in a step, `1st`/`2nd` split the dispatches by their order (cold then "
-                 "warm for the grouped GEMMs and the delta; raw then prepared for the NVFP4 "
-                 "kernel), over the whole run.\n\n"
-                 "| kernel | dispatches | mean | min | max | 1st of pair mean | 2nd of pair mean |\n"
+                 "Durations in microseconds (the trace's end minus start timestamps).  "
+                 "`dispatches`, `mean`, `min`, `max` cover every dispatch of the kernel in the "
+                 f"run (the {eager} eager steps, the graph replays and the ops timed outside "
+                 "the step).  The step calls the grouped GEMMs and the delta twice (cold: after "
+                 "a 1 GiB scratch write, then warm) and the NVFP4 kernel twice (raw, then "
+                 f"prepared): `step 1st` / `step 2nd` are the means over the first {eager} pairs "
+                 "of dispatches of such a kernel, i.e. the eager steps' first and second call.\n\n"
+                 "| kernel | dispatches | mean | min | max | step 1st | step 2nd |\n"
                  "|---|---:|---:|---:|---:|---:|---:|\n")
         for k in sorted(per, key=lambda k: -sum(per[k])):
             v = np.asarray(per[k])
             if not (k in lib or v.mean() > 50):
                 continue
             first = second = ""
-            if len(v) >= 2:
-                first, second = f"{v[0::2].mean():.1f}", f"{v[1::2].mean():.1f}"
+            if len(v) >= 2 * eager:
+                first, second = f"{v[:2 * eager:2].mean():.1f}", f"{v[1:2 * eager:2].mean():.1f}"
             fh.write(f"| {k[:90]} | {len(v)} | {v.mean():.1f} | {v.min():.1f} | {v.max():.1f} | "
                      f"{first} | {second} |\n")
     print(f"wrote {out_md}")

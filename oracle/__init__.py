@@ -25,6 +25,9 @@ passage of the source pages it follows (cited by page title and section):
   ``mm_nvfp4_lora`` operand format) -> :mod:`oracle.nvfp4_grouped`
 - FC1 gate/up grouped GEMM with its SwiGLU activation
   (``prims_ts_fp4_block_scale_moe`` parameters) -> :mod:`oracle.fc1`
+- NVFP4 quantisation, the producer of the operands ``mm_nvfp4_lora`` takes
+  (the paragraph after its formula, and its ``alpha`` parameter)
+  -> :mod:`oracle.fp4_quantize`
 
 Inputs are numpy arrays; bf16 tensors are passed as their uint16 bit patterns.
 
@@ -37,4 +40,4 @@ convention and are pinned only to that convention (two independent codings
 and hand-worked offsets).
 """
 from . import formats, grouped_mm, lora_delta, nvfp4, fold, finalize, permute  # noqa: F401
-from . import nvfp4_grouped, fc1  # noqa: F401
+from . import nvfp4_grouped, fc1, fp4_quantize  # noqa: F401
