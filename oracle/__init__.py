@@ -28,6 +28,8 @@ passage of the source pages it follows (cited by page title and section):
 - NVFP4 quantisation, the producer of the operands ``mm_nvfp4_lora`` takes
   (the paragraph after its formula, and its ``alpha`` parameter)
   -> :mod:`oracle.fp4_quantize`
+- FC1 (gate/up) LoRA delta, the ``gemm1_lora_delta`` the delta page's
+  description names -> :mod:`oracle.fc1_lora_delta`
 
 Inputs are numpy arrays; bf16 tensors are passed as their uint16 bit patterns.
 
@@ -40,4 +42,4 @@ convention and are pinned only to that convention (two independent codings
 and hand-worked offsets).
 """
 from . import formats, grouped_mm, lora_delta, nvfp4, fold, finalize, permute  # noqa: F401
-from . import nvfp4_grouped, fc1, fp4_quantize  # noqa: F401
+from . import nvfp4_grouped, fc1, fp4_quantize, fc1_lora_delta  # noqa: F401
