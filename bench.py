@@ -75,7 +75,7 @@ def parse():
                    "'copy_probe' (not part of the step) is a 512 MiB fp32 negation (read + "
                    "write) that calibrates the HBM byte counters; extra-op names ("
                    "'grouped_gemm_c3_alone', 'finalize', 'permute', 'nvfp4_grouped', "
-                   "'fc1_swiglu') time the ops outside the step")
+                   "'fp4_quantize', 'fc1_lora_delta', 'fc1_swiglu') time the ops outside the step")
     p.add_argument("--pmc-summary", nargs=3, metavar=("OP", "FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                    "'--only OP,copy_probe' into the committed traffic summary of OP "
@@ -632,6 +632,45 @@ def extra_ops(args, only, dev, stream, mi, synth, dc, wa, wb, sa, sb, perm_h, d_
             "(cum_m=32768), n=7168, k=2048, per-expert alpha, bf16 out; the fp16 MFMA peak is "
             "the denominator", 2.0 * ng.a.shape[0] * nn * kk)
         del ng, ngo
+    if want("fp4_quantize"):
+        # NVFP4 quantisation of the skewed MoE FC2 activations [32768, 2048] bf16
+        xq = synth.bf16_normal((32768, 2048), 1.0, synth.gen(79, dev), dev)
+        gq = torch.tensor([448.0 * 6.0 / float(xq.float().abs().max())], dtype=torch.float32,
+                          device=dev)
+        qc = torch.empty((32768, 1024), dtype=torch.uint8, device=dev)
+        qs = torch.empty(256 * 32 * 512, dtype=torch.uint8, device=dev)
+        qms = time_alone(lambda: mi.fp4_quantize(xq, gq, codes=qc, sf=qs))
+        extra["fp4_quantize"] = entry(
+            qms, 2.0 * xq.numel() + qc.numel() + qs.numel(),
+            "NVFP4 quantisation of bf16 [32768, 2048] (the skewed MoE FC2 activations): codes "
+            "and 128x4 UE4M3 scales")
+        del xq, qc, qs
+    if want("fc1_lora_delta"):
+        # FC1 LoRA delta on the delta workload's routing (T=8192, top_k=8, E=64,
+        # 8 adapters r=16): hidden 4096 in, 4096 gate/up columns out
+        f1 = synth.delta_at_scale(device=dev, I=4096, H=4096)
+        fwa, fwb = mi.fill_w_ptr(f1.A), mi.fill_w_ptr(f1.B)
+        fsa, fsb = f1.E * f1.rank * f1.I, f1.E * f1.H * f1.rank
+        f1o = torch.zeros((f1.act.shape[0], f1.H), dtype=torch.bfloat16, device=dev)
+        f1w = torch.empty(mi.delta_workspace_bytes(f1.T, f1.top_k, f1.E, f1.L, f1.rank),
+                          dtype=torch.uint8, device=dev)
+        f1ms = time_alone(lambda: mi.moe_fc1_lora_delta(
+            f1.act, f1.perm, fwa, fsa, fwb, fsb, f1.topk_ids, f1.lora_ids, f1.rank, f1.H,
+            num_adapters=f1.L, scale=f1.scale, out=f1o, workspace=f1w))
+        pr = f1.perm.cpu().numpy().reshape(f1.T, f1.top_k)
+        lid = f1.lora_ids.cpu().numpy()
+        eid = f1.topk_ids.cpu().numpy()
+        act_m = (pr >= 0) & (lid[:, None] >= 0)
+        keys = {(int(l), int(e)) for l, e in zip(np.broadcast_to(lid[:, None], eid.shape)[act_m],
+                                                 eid[act_m])}
+        n_act, n_rows = int(act_m.sum()), int((pr >= 0).sum())
+        f1bytes = 2.0 * f1.I * n_act + 2.0 * (f1.rank * f1.I + f1.H * f1.rank) * len(keys) + \
+            2.0 * f1.H * n_rows + 8.0 * f1.T * f1.top_k + 4.0 * f1.T
+        extra["fc1_lora_delta"] = entry(
+            f1ms, f1bytes, "FC1 LoRA delta, delta workload routing (T=8192, top_k=8, E=64, 8 "
+            "adapters r=16), hidden 4096 -> 4096 gate/up columns, one bf16 row per routed slot",
+            n_act * (2.0 * f1.rank * f1.I + 2.0 * f1.H * f1.rank))
+        del f1, f1o, f1w
     if want("fc1_swiglu"):
         fc = synth.fc1_case(device=dev)
         fco = torch.empty((fc.a.shape[0], fc.b.shape[1] // 2), dtype=torch.bfloat16, device=dev)

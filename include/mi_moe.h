@@ -8,6 +8,8 @@
  *                             (prims_ts_fp4_block_scale_moe, gemm1 parameters)
  *   - mi_moe_fc2_lora_delta   FC2 LoRA delta of a routed MoE
  *                             (flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta, formula)
+ *   - mi_moe_fc1_lora_delta   FC1 (gate/up) LoRA delta, one row per routed slot: the
+ *                             gemm1_lora_delta the delta page's description names
  *   - mi_moe_fc2_finalize_lora  the MoE finalize (routing-weighted combine of the FC2
  *                             rows) with that delta added, in one pass
  *                             (bgmv_moe_gemm2_lora_delta, description and return value)
@@ -21,6 +23,9 @@
  *   - mi_prepare_lora_fold    the prepared-path fold
  *                             (flashinfer.gemm.prepare_nvfp4_lora_adapter, description and `out=`)
  *   - mi_nvfp4_dequant_bf16   NVFP4 -> bf16 dequantisation with the GEMM's own decoder
+ *   - mi_fp4_quantize         bf16/fp16/fp32 -> NVFP4 codes + UE4M3 scales, the producer of
+ *                             the NVFP4 operands (mm_nvfp4_lora, the paragraph after the
+ *                             formula, and its alpha parameter)
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -158,6 +163,50 @@ MI_API mi_status mi_moe_fc2_lora_delta(const void* act, int64_t padded_rows, int
                                 const int32_t* lora_ids,
                                 int64_t num_tokens, int64_t top_k, int64_t num_experts,
                                 int64_t num_adapters, int64_t rank, int64_t hidden_size,
+                                mi_dtype lora_dtype, float scale, mi_dtype out_dtype,
+                                void* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * FC1 (gate/up) LoRA delta of a routed MoE: the gemm1_lora_delta that
+ * flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta (description) says FC1 runs
+ * with.  The pages give no formula for it; this library computes the FC1
+ * counterpart of the FC2 formula, one row per routed slot, with no routing
+ * weight and no combine:
+ *     out[p] = scale * B_up[l,e] @ (A_up[l,e] @ act[p])      p = perm[t*top_k+j]
+ * with e = topk_ids[t,j], l = lora_ids[t], act the permuted FC1 input (the rows
+ * the FC1 GEMM multiplies).  The result is the fc1_delta of
+ * mi_grouped_mm_swiglu, added before the activation.
+ *   act          lora_dtype [padded_rows, hidden_size], 16-byte aligned
+ *   perm         int32 [num_tokens * top_k]; < 0 = inactive slot
+ *   w_ptr_a      int64 [num_experts]: byte address of A_up[0,e], a [rank, hidden_size]
+ *                block; adapter l starts lora_stride_a ELEMENTS later (16-byte aligned)
+ *   w_ptr_b      int64 [num_experts]: byte address of B_up[0,e], an [out_features, rank]
+ *                block; adapter l starts lora_stride_b ELEMENTS later (16-byte aligned)
+ *   topk_ids     int32 [num_tokens, top_k];  lora_ids int32 [num_tokens], < 0 = none
+ *   out          out_dtype [padded_rows, out_features] (MI_BF16, MI_F16 or MI_F32),
+ *                16-byte aligned.  Row p of every slot with p in [0, padded_rows) is
+ *                written: the delta, or +0 when the token has no adapter (id outside
+ *                [0, num_adapters)) or the expert lies outside [0, num_experts).
+ *                Rows no slot points at are untouched.
+ *   workspace    at least mi_moe_fc1_lora_delta_workspace_size() bytes, 256-byte
+ *                aligned, no initialisation needed
+ * Rounding: the intermediate A_up @ act is fp32, carried as bf16 (or scaled fp16)
+ * hi + lo into the second product; one rounding to out_dtype.
+ * Requirements: as for mi_moe_fc2_lora_delta with hidden_size in the role of
+ * inter_size and out_features in the role of hidden_size (out_features % 128 ==
+ * 0); two slots pointing at the same row leave one of their deltas there.
+ */
+MI_API size_t mi_moe_fc1_lora_delta_workspace_size(int64_t num_tokens, int64_t top_k,
+                                            int64_t num_experts, int64_t num_adapters,
+                                            int64_t rank);
+MI_API mi_status mi_moe_fc1_lora_delta(const void* act, int64_t padded_rows, int64_t hidden_size,
+                                const int32_t* expanded_idx_to_permuted_idx,
+                                const int64_t* w_ptr_a, int64_t lora_stride_a,
+                                const int64_t* w_ptr_b, int64_t lora_stride_b,
+                                const int32_t* topk_ids, const int32_t* lora_ids,
+                                int64_t num_tokens, int64_t top_k, int64_t num_experts,
+                                int64_t num_adapters, int64_t rank, int64_t out_features,
                                 mi_dtype lora_dtype, float scale, mi_dtype out_dtype,
                                 void* out, void* workspace, size_t workspace_bytes,
                                 void* stream);
@@ -332,6 +381,32 @@ MI_API mi_status mi_prepare_lora_fold(const void* lora_b, int64_t n, int64_t ran
  */
 MI_API mi_status mi_nvfp4_dequant_bf16(const uint8_t* codes, const uint8_t* sf, size_t sf_bytes,
                                 int64_t rows, int64_t k, void* out, void* stream);
+
+/*
+ * NVFP4 quantiser: the producer of the operands mi_mm_nvfp4_lora and
+ * mi_grouped_mm_nvfp4 take (flashinfer.gemm.mm_nvfp4_lora, the paragraph after
+ * the formula: the layout fp4_quantize() writes; parameter alpha: the base
+ * scale divided by the two operands' global scales).  The pages do not spell
+ * out its steps; for every row and every block of 16 consecutive elements x_i
+ * along k, with g = global_scale[matrix], each step an IEEE fp32 operation
+ * rounded to nearest even:
+ *   amax = max |x_i|;   s = (amax * g) / 6
+ *   sf   = the UE4M3 code nearest to s, ties to the even code, >= 448 -> 0x7E
+ *   r    = g / value(sf), or 0 when value(sf) == 0
+ *   code = the E2M1 code nearest to x_i * r, ties to the even code, magnitudes
+ *          above 6 -> 6, sign bit = sign of x_i * r
+ * so dequant(codes, sf) / g approximates x (at most value(sf) / g per element).
+ *   x             x_dtype (MI_BF16, MI_F16 or MI_F32) [batch, rows, k], 16-byte aligned
+ *   global_scale  fp32 [batch], device: g of each matrix
+ *   codes         uint8 [batch, rows, k/2], element 2i in the low nibble; 4-byte aligned
+ *   sf            batch consecutive 128x4 scale buffers (as for mi_mm_nvfp4_lora), each
+ *                 ceil(rows/128) * (k/64) * 512 bytes; padding rows are written as 0;
+ *                 sf_bytes the total size (larger is fine); 4-byte aligned
+ * Requirements: batch >= 1, rows >= 0 (0 is a no-op), k % 64 == 0, k >= 64.
+ */
+MI_API mi_status mi_fp4_quantize(const void* x, int64_t batch, int64_t rows, int64_t k,
+                          mi_dtype x_dtype, const float* global_scale, uint8_t* codes,
+                          uint8_t* sf, size_t sf_bytes, void* stream);
 
 #ifdef __cplusplus
 }

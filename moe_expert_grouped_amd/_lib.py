@@ -22,6 +22,8 @@ EXPORTS = [
     "mi_moe_fc2_lora_delta_workspace_size",
     "mi_moe_fc2_lora_delta",
     "mi_moe_fc2_finalize_lora",
+    "mi_moe_fc1_lora_delta_workspace_size",
+    "mi_moe_fc1_lora_delta",
     "mi_moe_fc2_finalize_workspace_size",
     "mi_moe_route_workspace_size",
     "mi_moe_route_permutation",
@@ -30,6 +32,7 @@ EXPORTS = [
     "mi_grouped_mm_nvfp4",
     "mi_prepare_lora_fold",
     "mi_nvfp4_dequant_bf16",
+    "mi_fp4_quantize",
 ]
 
 _lib = None
@@ -74,6 +77,17 @@ def lib() -> ctypes.CDLL:
         L.mi_moe_fc2_finalize_lora.argtypes = [
             P, I32,               # fc2, fc2_dtype
             *L.mi_moe_fc2_lora_delta.argtypes]
+        L.mi_moe_fc1_lora_delta_workspace_size.restype = SZ
+        L.mi_moe_fc1_lora_delta_workspace_size.argtypes = [I64, I64, I64, I64, I64]
+        L.mi_moe_fc1_lora_delta.restype = I32
+        L.mi_moe_fc1_lora_delta.argtypes = [
+            P, I64, I64,          # act, padded_rows, hidden_size
+            P,                    # expanded_idx_to_permuted_idx
+            P, I64, P, I64,       # w_ptr_a, stride_a, w_ptr_b, stride_b
+            P, P,                 # topk_ids, lora_ids
+            I64, I64, I64, I64, I64, I64,  # T, top_k, E, L, rank, out_features
+            I32, F32, I32,        # lora_dtype, scale, out_dtype
+            P, P, SZ, P]          # out, workspace, bytes, stream
         L.mi_moe_route_workspace_size.restype = SZ
         L.mi_moe_route_workspace_size.argtypes = [I64, I64]
         L.mi_moe_route_permutation.restype = I32
@@ -89,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.mi_prepare_lora_fold.argtypes = [P, I64, I64, P, P, P, P, P]
         L.mi_nvfp4_dequant_bf16.restype = I32
         L.mi_nvfp4_dequant_bf16.argtypes = [P, P, SZ, I64, I64, P, P]
+        L.mi_fp4_quantize.restype = I32
+        L.mi_fp4_quantize.argtypes = [P, I64, I64, I64, I32, P, P, P, SZ, P]
         _lib = L
     return _lib
 

@@ -23,6 +23,7 @@ __all__ = [
     "grouped_mm_swiglu",
     "bgmv_moe_gemm2_lora_delta",
     "moe_finalize_lora",
+    "moe_fc1_lora_delta",
     "moe_route_permutation",
     "moe_permute_rows",
     "route_workspace_bytes",
@@ -35,6 +36,7 @@ __all__ = [
     "PreparedNvFp4LoraAdapter",
     "StaleAdapterError",
     "nvfp4_dequant",
+    "fp4_quantize",
     "sf_bytes_needed",
 ]
 
@@ -257,6 +259,53 @@ def _delta_call(fc2, act, perm, w_ptr_a, lora_stride_a, w_ptr_b, lora_stride_b, 
     else:
         fc2 = fc2.contiguous()
         check(_lib.lib().mi_moe_fc2_finalize_lora(_ptr(fc2), _DT[fc2.dtype], *args))
+    return out
+
+
+def moe_fc1_lora_delta(act: torch.Tensor, expanded_idx_to_permuted_idx: torch.Tensor,
+                       w_ptr_a: torch.Tensor, lora_stride_a: int, w_ptr_b: torch.Tensor,
+                       lora_stride_b: int, topk_ids: torch.Tensor, lora_ids: torch.Tensor,
+                       rank: int, out_features: int, *, num_adapters: int,
+                       lora_dtype: torch.dtype = torch.bfloat16, scale: float = 1.0,
+                       out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """FC1 (gate/up) LoRA delta ``[padded_rows, out_features]``: row
+    ``perm[t*top_k+j]`` is ``scale * B[l, e] @ (A[l, e] @ act[row])`` for
+    each routed slot, +0 for a slot without adapter; the ``fc1_delta`` of
+    :func:`grouped_mm_swiglu`.  A fresh ``out`` is zero-filled first, so rows
+    no slot points at are 0; a caller's ``out`` keeps them."""
+    _need(act.dim() == 2 and act.dtype == lora_dtype,
+          "moe_fc1_lora_delta: act must be [padded_rows, hidden] of lora_dtype")
+    _need(topk_ids.dim() == 2 and topk_ids.dtype == torch.int32 and lora_ids.dtype == torch.int32,
+          "moe_fc1_lora_delta: topk_ids must be int32 [T, top_k] and lora_ids int32 [T]")
+    T, top_k = topk_ids.shape
+    perm = expanded_idx_to_permuted_idx
+    _need(perm.numel() == T * top_k and perm.dtype == torch.int32 and lora_ids.numel() == T,
+          "moe_fc1_lora_delta: expanded_idx_to_permuted_idx must be int32 [T*top_k]")
+    _need(w_ptr_a.dtype == torch.int64 and w_ptr_b.dtype == torch.int64 and
+          w_ptr_a.numel() == w_ptr_b.numel(),
+          "moe_fc1_lora_delta: w_ptr_a / w_ptr_b must be int64 [1, num_experts]")
+    _need(lora_dtype in (torch.bfloat16, torch.float16) and out_dtype in _DT,
+          "moe_fc1_lora_delta: unsupported dtype")
+    _need_cuda("moe_fc1_lora_delta", act, perm, w_ptr_a, w_ptr_b, topk_ids, lora_ids, out,
+               workspace)
+    E = w_ptr_a.numel()
+    act = act.contiguous()
+    perm, topk_ids, lora_ids = perm.contiguous(), topk_ids.contiguous(), lora_ids.contiguous()
+    if out is None:
+        out = torch.zeros((act.shape[0], out_features), dtype=out_dtype, device=act.device)
+    _need(out.shape == (act.shape[0], out_features) and out.dtype == out_dtype and
+          out.is_contiguous(), "moe_fc1_lora_delta: out must be a contiguous "
+          "[padded_rows, out_features] tensor of out_dtype")
+    need = int(_lib.lib().mi_moe_fc1_lora_delta_workspace_size(T, top_k, E, num_adapters, rank))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=act.device)
+    check(_lib.lib().mi_moe_fc1_lora_delta(
+        _ptr(act), act.shape[0], act.shape[1], _ptr(perm), _ptr(w_ptr_a.contiguous()),
+        int(lora_stride_a), _ptr(w_ptr_b.contiguous()), int(lora_stride_b), _ptr(topk_ids),
+        _ptr(lora_ids), T, top_k, E, int(num_adapters), int(rank), int(out_features),
+        _DT[lora_dtype], float(scale), _DT[out_dtype], _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream(act.device)))
     return out
 
 
@@ -509,3 +558,32 @@ def nvfp4_dequant(codes: torch.Tensor, sf: torch.Tensor, k: int | None = None) -
     check(_lib.lib().mi_nvfp4_dequant_bf16(_ptr(codes.contiguous()), _ptr(sf), sf.numel(),
                                            codes.shape[0], k, _ptr(out), _stream(codes.device)))
     return out
+
+
+def fp4_quantize(x: torch.Tensor, global_scale: torch.Tensor, *, codes: torch.Tensor | None = None,
+                 sf: torch.Tensor | None = None):
+    """NVFP4 quantisation of ``x`` (bf16 / fp16 / fp32, ``[rows, K]`` or a batch
+    ``[B, rows, K]`` of matrices) with fp32 global scale(s) ``global_scale``
+    (one per matrix).  Returns ``(codes, sf)``: uint8 ``[..., rows, K/2]`` and
+    the 128x4 scale buffer(s) (one per matrix, concatenated), the operands
+    of :func:`mm_nvfp4_lora` / :func:`grouped_mm_nvfp4`."""
+    _need(x.dtype in _DT and x.dim() in (2, 3), "fp4_quantize: x must be a bf16, fp16 or fp32 "
+          "[rows, K] or [B, rows, K] tensor")
+    _need_cuda("fp4_quantize", x, global_scale, codes, sf)
+    batch = 1 if x.dim() == 2 else x.shape[0]
+    rows, k = x.shape[-2], x.shape[-1]
+    _need(global_scale.dtype == torch.float32 and global_scale.numel() == batch,
+          "fp4_quantize: global_scale must be fp32 with one value per matrix")
+    x = x.contiguous()
+    per = (-(-rows // 128)) * (k // 64) * 512
+    if codes is None:
+        codes = torch.empty((*x.shape[:-1], k // 2), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty(batch * per, dtype=torch.uint8, device=x.device)
+    _need(codes.dtype == torch.uint8 and codes.shape == (*x.shape[:-1], k // 2) and
+          codes.is_contiguous(), "fp4_quantize: codes must be contiguous uint8 [..., rows, K/2]")
+    _need(sf.dtype == torch.uint8 and sf.is_contiguous(), "fp4_quantize: sf must be contiguous uint8")
+    check(_lib.lib().mi_fp4_quantize(_ptr(x), batch, rows, k, _DT[x.dtype],
+                                     _ptr(global_scale.contiguous()), _ptr(codes), _ptr(sf),
+                                     sf.numel(), _stream(x.device)))
+    return codes, sf

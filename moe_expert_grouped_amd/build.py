@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmi_moe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["errors.cpp", "grouped_mm.hip", "lora_delta.hip", "nvfp4_lora.hip", "permute.hip"]
+SOURCES = ["errors.cpp", "grouped_mm.hip", "lora_delta.hip", "nvfp4_lora.hip", "permute.hip",
+           "fp4_quantize.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -253,7 +253,7 @@ __device__ void list_slots(const SlotSrc& s, const Tile& tile, SlotLists& L) {
     ws[k] = 0.f;
     if (xs[k] >= 0) {
       const int e = gld<int>(s.topk_ids + xs[k]), r = gld<int>(s.perm + xs[k]);
-      ws[k] = gld<float>(s.topk_weights + xs[k]);
+      ws[k] = s.topk_weights ? gld<float>(s.topk_weights + xs[k]) : 1.f;  // FC1: no weight
       if (e >= 0 && e < s.E && r >= 0 && r < s.padded_rows) es[k] = e;
       rs[k] = r;
     }
@@ -1193,6 +1193,140 @@ __global__ __launch_bounds__(NT_EXP, 2) void expand_kernel(ExpandArgs p) {
   }, s_tok);
 }
 
+// ---------------------------------------------------------------------------
+// FC1 LoRA delta: the same plan, list and shrink (unit routing weights), then
+// an expand without accumulation -- every active slot owns its output row
+//   out[perm[t*top_k+j]] = B_le @ u(t, j)        (u = scale * A_le @ act[row])
+// ---------------------------------------------------------------------------
+struct Fc1Args {
+  const int32_t* btile;
+  const int32_t* tex;
+  const uint16_t* u2;
+  const int64_t* w_ptr_b;
+  long stride_b;
+  const uint32_t* blk_tl;
+  const int32_t* blk_row;
+  const float* blk_f;
+  void* out;
+  long cap;
+  int E, L, R, OF, maxblk, nch, out_kind;  // OF: output width (B_le rows)
+};
+
+// 4 consecutive output columns of one row, rounded once (streaming stores:
+// the rows are written once and not read here)
+__device__ __forceinline__ void store_out4(void* out, int kind, long off, f32x4 v) {
+  if (kind == 1) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(out) + off));
+  } else if (kind == 2) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 h = {static_cast<_Float16>(v.x), static_cast<_Float16>(v.y),
+                  static_cast<_Float16>(v.z), static_cast<_Float16>(v.w)};
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x2, h),
+                                reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off));
+  } else {
+    const u32x2 w = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off));
+  }
+}
+
+// One workgroup per (adapter l, expert e, chunk of EXP_CW output columns).
+// Its 4 wavefronts hold that chunk of B_le in registers (each lane: 4 ranks of
+// one column per 16-column group and rank chunk, the expand's [B | B] operand)
+// and take the blocks of (l, e) from every tile of adapter l in turn: per
+// block, one v_mfma_f32_16x16x32 per column group and rank chunk on [B | B]
+// and the block's [u_hi ; u_lo] record, then each lane stores its slot's 4
+// consecutive columns.  B_le is read from memory once per chunk.
+template <int NB, bool PART, bool F16>
+__global__ __launch_bounds__(256) void fc1_expand_kernel(Fc1Args p) {
+  constexpr int NG = EXP_CW / 16;  // 16-column groups of the chunk
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ch = blockIdx.x % p.nch, le = blockIdx.x / p.nch;
+  const int l = le / p.E, e = le % p.E;
+  if (l >= p.L) return;
+  const int t0 = gld<int>(p.btile + l), t1 = gld<int>(p.btile + l + 1);
+  const int E1 = p.E + 1;
+  const int col = lane & 15, kq = lane >> 4;
+  const int h0 = ch * EXP_CW;
+
+  // this lane's B_le fragments: column h0 + 16 g + col, ranks 16 c + 4 kq .. + 3
+  const char* ble = reinterpret_cast<const char*>(gld<int64_t>(p.w_ptr_b + e) + 2 * p.stride_b * l);
+  const __amdgpu_buffer_rsrc_t brsrc =
+      buf_rsrc(uniform_ptr(ble), static_cast<uint32_t>(p.OF) * p.R * 2);
+  u32x2 fb[NG][NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    const int r4 = c * 16 + kq * 4;  // rank % 8 == 0: ranks r4 .. r4+3 all in or all out
+    const bool rin = r4 < p.R;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const uint32_t off = 2u * (static_cast<uint32_t>(h0 + 16 * g + col) * p.R +
+                                 (rin ? r4 : p.R - 4));
+      fb[g][c] = buf_ld64(brsrc, off, 0);
+      if (PART && !rin) fb[g][c] = u32x2{0, 0};
+    }
+  }
+
+  int j = 0;
+  for (int ti = t0; ti < t1; ++ti) {
+    const int b0 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e);
+    const int b1 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e + 1);
+    for (int bi = b0; bi < b1; ++bi, ++j) {
+      if ((j & 3) != wave) continue;
+      const long tb = static_cast<long>(ti) * p.maxblk + bi;
+      const uint16_t* rec = p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32;
+      u32x4 fu[NB];
+#pragma unroll
+      for (int c = 0; c < NB; ++c) fu[c] = gld<u32x4>(rec + c * 512 + lane * 8);
+      const int slot = col;
+      const uint32_t tlw = gld<uint32_t>(p.blk_tl + tb * 4 + (slot >> 2));
+      const bool real = ((tlw >> (8 * (slot & 3))) & 0xFFu) != 0xFFu;
+      const long row = gld<int>(p.blk_row + tb * 16 + slot);
+      const float fs = F16 ? gld<float>(p.blk_f + tb * 16 + slot) : 1.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+          const u32x4 a4 = u32x4{fb[g][c].x, fb[g][c].y, fb[g][c].x, fb[g][c].y};
+          if constexpr (F16)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a4),
+                                                         __builtin_bit_cast(f16x8, fu[c]), acc,
+                                                         0, 0, 0);
+          else
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a4),
+                                                          __builtin_bit_cast(bf16x8, fu[c]), acc,
+                                                          0, 0, 0);
+        }
+        if (F16) acc = acc * fs;  // the slot's 2^-k: exact
+        // lane (slot, kq) holds columns 16 g + 4 kq .. + 3 of its slot's row
+        if (real) store_out4(p.out, p.out_kind, row * p.OF + h0 + 16 * g + 4 * kq, acc);
+      }
+    }
+  }
+}
+
+// +0 rows of the FC1 delta: one wavefront per slot; a slot with a row in
+// [0, padded_rows) whose token has no adapter (id outside [0, L)) or whose
+// expert lies outside [0, E) gets a zero row (the expand writes the others)
+__global__ __launch_bounds__(256) void fc1_zero_rows_kernel(const int32_t* perm,
+                                                            const int32_t* topk_ids,
+                                                            const int32_t* lora_ids, long nslot,
+                                                            int top_k, int E, int L,
+                                                            int padded_rows, void* out,
+                                                            long row_bytes) {
+  const long sl = (static_cast<long>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (sl >= nslot) return;
+  const int r = gld<int>(perm + sl);
+  if (r < 0 || r >= padded_rows) return;
+  const int l = gld<int>(lora_ids + sl / top_k), e = gld<int>(topk_ids + sl);
+  if (l >= 0 && l < L && e >= 0 && e < E) return;
+  char* o = static_cast<char*>(out) + static_cast<long>(r) * row_bytes;
+  for (long b = lane * 16; b < row_bytes; b += 64 * 16)
+    __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, reinterpret_cast<u32x4*>(o + b));
+}
+
 int num_cus() {
   int dev = 0, v = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -1231,6 +1365,154 @@ extern "C" size_t mi_moe_fc2_finalize_workspace_size(int64_t num_tokens, int64_t
 namespace mi {
 namespace {
 
+// What the plan, list and shrink launches leave for an expand: the workspace
+// sections and the launch shape.
+struct Front {
+  Layout ly;
+  uint8_t* ws;
+  uint16_t* u2;
+  int32_t *tok_list, *counters, *tinfo, *btile, *tex, *blk_row;
+  Tile* tiles;
+  int64_t* blk_b;
+  uint32_t* blk_tl;
+  float* blk_f;
+  int ntiles, nb;
+  bool f16;
+};
+
+// Validation shared by the FC2 and FC1 deltas (messages name `what`), then
+// the plan, list and shrink launches.  `act` is [padded_rows, in_width] (I for
+// FC2, hidden for FC1); B_le is [out_width, rank] (H for FC2, 2I for FC1);
+// topk_weights may be NULL (unit weights).
+mi_status run_front(const char* what, const void* act, int64_t padded_rows, int64_t in_width,
+                    const int32_t* perm, const int64_t* w_ptr_a, int64_t lora_stride_a,
+                    const int64_t* w_ptr_b, int64_t lora_stride_b, const int32_t* topk_ids,
+                    const float* topk_weights, const int32_t* lora_ids, int64_t T, int64_t top_k,
+                    int64_t E, int64_t L, int64_t rank, int64_t out_width, mi_dtype lora_dtype,
+                    float scale, mi_dtype out_dtype, void* out, void* workspace,
+                    size_t workspace_bytes, hipStream_t s, Front& f) {
+  MI_REQUIRE(top_k >= 1 && top_k <= MAX_TOPK, "%s: top_k must be in [1, %d]", what, MAX_TOPK);
+  MI_REQUIRE(T >= 0 && T * top_k < (1LL << 24), "%s: num_tokens * top_k must be < 2^24", what);
+  MI_REQUIRE(E >= 1 && E <= MAX_EXPERTS, "%s: num_experts must be in [1, %d]", what,
+             MAX_EXPERTS);
+  MI_REQUIRE(L >= 0 && L <= MAX_ADAPTERS, "%s: num_adapters must be in [0, %d]", what,
+             MAX_ADAPTERS);
+  MI_REQUIRE(rank >= 8 && rank <= 128 && rank % 8 == 0,
+             "%s: rank must be a multiple of 8 in [8, 128] (got %lld)", what, (long long)rank);
+  MI_REQUIRE(in_width >= 8 && in_width % 8 == 0 && in_width < (1 << 30),
+             "%s: the activation width must be a positive multiple of 8 (got %lld)", what,
+             (long long)in_width);
+  MI_REQUIRE(out_width >= 1 && out_width < (1 << 30), "%s: output width out of range", what);
+  // one B_le block is addressed through a 32-bit buffer range
+  MI_REQUIRE_SUPPORTED(out_width * rank * 2 < (1LL << 32),
+                       "%s: one B block (%lld x %lld rank, 16-bit) must stay below 4 GiB", what,
+                       (long long)out_width, (long long)rank);
+  MI_REQUIRE_SUPPORTED(out_width % EXP_CW == 0, "%s: the output width must be a multiple of %d "
+                       "(got %lld)", what, EXP_CW, (long long)out_width);
+  MI_REQUIRE(lora_stride_a >= 0 && lora_stride_a % 8 == 0 && lora_stride_b >= 0 &&
+                 lora_stride_b % 8 == 0,
+             "%s: lora strides must be non-negative multiples of 8 elements (16-byte aligned "
+             "adapter blocks)", what);
+  MI_REQUIRE(padded_rows >= 0 && padded_rows < (1LL << 31), "%s: padded_rows out of range",
+             what);
+  MI_REQUIRE(lora_dtype == MI_BF16 || lora_dtype == MI_F16,
+             "%s: lora_dtype must be bf16 or fp16", what);
+  MI_REQUIRE(out_dtype == MI_BF16 || out_dtype == MI_F32 || out_dtype == MI_F16,
+             "%s: out_dtype must be bf16, fp16 or fp32", what);
+  if (T == 0) return MI_OK;
+  MI_REQUIRE(out != nullptr, "%s: out is null", what);
+  MI_REQUIRE(aligned16(out), "%s: out must be 16-byte aligned", what);
+  MI_REQUIRE(lora_ids != nullptr && topk_ids != nullptr && perm != nullptr,
+             "%s: index/weight tensors must be non-null", what);
+  if (L > 0)
+    MI_REQUIRE((act != nullptr || padded_rows == 0) && w_ptr_a != nullptr && w_ptr_b != nullptr,
+               "%s: act and the pointer tables must be non-null", what);
+  MI_REQUIRE(aligned16(act), "%s: activation rows must be 16-byte aligned", what);
+  f.ly = layout(T, top_k, E, L, rank);
+  const Layout& ly = f.ly;
+  MI_REQUIRE(workspace != nullptr && workspace_bytes >= ly.total,
+             "%s: workspace needs %zu bytes (got %zu)", what, ly.total, workspace_bytes);
+  MI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255) == 0,
+             "%s: workspace must be 256-byte aligned", what);
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  f.ws = ws;
+  f.u2 = reinterpret_cast<uint16_t*>(ws + ly.u2);
+  f.tok_list = reinterpret_cast<int32_t*>(ws + ly.tok_list);
+  f.tiles = reinterpret_cast<Tile*>(ws + ly.tiles);
+  f.counters = reinterpret_cast<int32_t*>(ws + ly.counters);
+  int64_t* blk_a = reinterpret_cast<int64_t*>(ws + ly.blk_a);
+  f.blk_b = reinterpret_cast<int64_t*>(ws + ly.blk_b);
+  f.blk_row = reinterpret_cast<int32_t*>(ws + ly.blk_row);
+  float* blk_w = reinterpret_cast<float*>(ws + ly.blk_w);
+  f.blk_f = reinterpret_cast<float*>(ws + ly.blk_f);
+  f.f16 = lora_dtype == MI_F16;
+  f.blk_tl = reinterpret_cast<uint32_t*>(ws + ly.blk_tl);
+  f.tinfo = reinterpret_cast<int32_t*>(ws + ly.tinfo);
+  const int tt = tile_tokens(top_k);
+  f.ntiles = static_cast<int>(max_tiles(T, top_k, L));
+  f.btile = reinterpret_cast<int32_t*>(ws + ly.btile);
+  f.tex = reinterpret_cast<int32_t*>(ws + ly.tex);
+  f.nb = rank_chunks(rank);
+  const int ntiles = f.ntiles, nb = f.nb;
+  const bool f16 = f.f16;
+  uint16_t* u2 = f.u2;
+  float* blk_f = f.blk_f;
+
+  PlanArgs pa{lora_ids, static_cast<int>(T), static_cast<int>(L), tt, f.tok_list, f.tiles,
+              f.counters, f.btile};
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, pa);
+  mi_status st = launch_status(what);
+  if (st != MI_OK || L == 0) return st;
+
+  const SlotSrc src{f.tok_list, perm, topk_ids, topk_weights, static_cast<int>(top_k),
+                    static_cast<int>(padded_rows), static_cast<int>(E)};
+  ListArgs la{src, f.tiles, f.counters, topk_weights, w_ptr_a, static_cast<long>(lora_stride_a),
+              w_ptr_b, static_cast<long>(lora_stride_b), blk_a, f.blk_b, f.blk_tl, f.blk_row,
+              blk_w, f.tinfo, f.tex, static_cast<int>(L), ly.maxblk, scale};
+  hipLaunchKernelGGL(list_kernel, dim3(ntiles), dim3(NT_DELTA), 0, s, la);
+  st = launch_status(what);
+  if (st != MI_OK) return st;
+
+  // A_le held in LDS when it fits: one workgroup per (adapter, expert, part)
+  const bool by_le = nb <= 2 && 16 * nb * in_width <= SLE_AMAX && in_width % 128 == 0;
+  if (by_le) {
+    const long le = L * E;
+    const int S = le >= 2L * num_cus() ? 1 : 2;  // parts: the tiles of an adapter split S ways
+    MI_REQUIRE(le * S < (1L << 31), "%s: problem too large", what);
+    ShrinkLeArgs sa{static_cast<const uint16_t*>(act), w_ptr_a, static_cast<long>(lora_stride_a),
+                    f.btile, f.tex, f.blk_row, blk_w, u2, blk_f, ly.cap,
+                    static_cast<int>(in_width), static_cast<int>(E), static_cast<int>(L),
+                    static_cast<int>(rank), ly.maxblk, S};
+    const dim3 g(static_cast<unsigned>(le * S)), b(256);
+    switch (nb * 2 + (f16 ? 1 : 0)) {
+      case 2: hipLaunchKernelGGL((shrink_le_kernel<1, false>), g, b, 0, s, sa); break;
+      case 3: hipLaunchKernelGGL((shrink_le_kernel<1, true>), g, b, 0, s, sa); break;
+      case 4: hipLaunchKernelGGL((shrink_le_kernel<2, false>), g, b, 0, s, sa); break;
+      default: hipLaunchKernelGGL((shrink_le_kernel<2, true>), g, b, 0, s, sa); break;
+    }
+  } else {
+    const int bpt = (ly.maxblk + SHR_WAVES - 1) / SHR_WAVES;  // shrink workgroups per tile
+    const long swg = static_cast<long>(ntiles) * bpt;
+    MI_REQUIRE(swg < (1L << 31), "%s: problem too large", what);
+    ShrinkArgs sa{static_cast<const uint16_t*>(act), f.tiles, f.counters, blk_a, f.blk_row, blk_w,
+                  f.tinfo, u2, blk_f, ly.cap, static_cast<int>(in_width), static_cast<int>(L),
+                  static_cast<int>(rank), ly.maxblk, bpt};
+    const dim3 sgrid(static_cast<unsigned>(swg)), sblock(64 * SHR_WAVES);
+    switch (nb * 2 + (f16 ? 1 : 0)) {
+      case 2: hipLaunchKernelGGL((shrink_kernel<1, false>), sgrid, sblock, 0, s, sa); break;
+      case 3: hipLaunchKernelGGL((shrink_kernel<1, true>), sgrid, sblock, 0, s, sa); break;
+      case 4: hipLaunchKernelGGL((shrink_kernel<2, false>), sgrid, sblock, 0, s, sa); break;
+      case 5: hipLaunchKernelGGL((shrink_kernel<2, true>), sgrid, sblock, 0, s, sa); break;
+      case 8: hipLaunchKernelGGL((shrink_kernel<4, false>), sgrid, sblock, 0, s, sa); break;
+      case 9: hipLaunchKernelGGL((shrink_kernel<4, true>), sgrid, sblock, 0, s, sa); break;
+      case 16: hipLaunchKernelGGL((shrink_kernel<8, false>), sgrid, sblock, 0, s, sa); break;
+      default: hipLaunchKernelGGL((shrink_kernel<8, true>), sgrid, sblock, 0, s, sa); break;
+    }
+  }
+  return launch_status(what);
+}
+
 // The delta and, when fc2 is given, the finalize: both entry points below.
 mi_status run_delta(const char* what, const void* act, int64_t padded_rows, int64_t inter_size,
                     const int32_t* perm, const int64_t* w_ptr_a, int64_t lora_stride_a,
@@ -1239,134 +1521,29 @@ mi_status run_delta(const char* what, const void* act, int64_t padded_rows, int6
                     int64_t E, int64_t L, int64_t rank, int64_t H, mi_dtype lora_dtype,
                     float scale, const void* fc2, mi_dtype fc2_dtype, mi_dtype out_dtype,
                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)what;
-  MI_REQUIRE(top_k >= 1 && top_k <= MAX_TOPK, "bgmv_moe_gemm2_lora_delta: top_k must be in [1, %d]",
-             MAX_TOPK);
-  MI_REQUIRE(T >= 0 && T * top_k < (1LL << 24),
-             "bgmv_moe_gemm2_lora_delta: num_tokens * top_k must be < 2^24");
-  MI_REQUIRE(E >= 1 && E <= MAX_EXPERTS,
-             "bgmv_moe_gemm2_lora_delta: num_experts must be in [1, %d]", MAX_EXPERTS);
-  MI_REQUIRE(L >= 0 && L <= MAX_ADAPTERS,
-             "bgmv_moe_gemm2_lora_delta: num_adapters must be in [0, %d]", MAX_ADAPTERS);
-  MI_REQUIRE(rank >= 8 && rank <= 128 && rank % 8 == 0,
-             "bgmv_moe_gemm2_lora_delta: rank must be a multiple of 8 in [8, 128] (got %lld)",
-             (long long)rank);
-  MI_REQUIRE(inter_size >= 8 && inter_size % 8 == 0 && inter_size < (1 << 30),
-             "bgmv_moe_gemm2_lora_delta: I = gemm1_activation_output.shape[1] must be a positive "
-             "multiple of 8 (got %lld)", (long long)inter_size);
-  MI_REQUIRE(H >= 1 && H < (1 << 30), "bgmv_moe_gemm2_lora_delta: hidden_size out of range");
-  // one B_le block is addressed through a 32-bit buffer range
-  MI_REQUIRE_SUPPORTED(H * rank * 2 < (1LL << 32),
-                       "bgmv_moe_gemm2_lora_delta: one B_down block (hidden_size x rank bf16) "
-                       "must stay below 4 GiB (got %lld x %lld)", (long long)H, (long long)rank);
-  MI_REQUIRE_SUPPORTED(H % EXP_CW == 0,
-                       "bgmv_moe_gemm2_lora_delta: hidden_size must be a multiple of %d (got %lld)",
-                       EXP_CW, (long long)H);
-  MI_REQUIRE(lora_stride_a >= 0 && lora_stride_a % 8 == 0 && lora_stride_b >= 0 &&
-                 lora_stride_b % 8 == 0,
-             "bgmv_moe_gemm2_lora_delta: lora strides must be non-negative multiples of 8 "
-             "elements (16-byte aligned adapter blocks)");
-  MI_REQUIRE(padded_rows >= 0 && padded_rows < (1LL << 31),
-             "bgmv_moe_gemm2_lora_delta: padded_rows out of range");
-  MI_REQUIRE(lora_dtype == MI_BF16 || lora_dtype == MI_F16,
-             "bgmv_moe_gemm2_lora_delta: lora_dtype must be bf16 or fp16");
-  MI_REQUIRE(out_dtype == MI_BF16 || out_dtype == MI_F32 || out_dtype == MI_F16,
-             "bgmv_moe_gemm2_lora_delta: out_dtype must be bf16, fp16 or fp32");
-  if (T == 0) return MI_OK;
+  MI_REQUIRE(topk_weights != nullptr || T == 0, "%s: topk_weights is null", what);
+  hipStream_t s = static_cast<hipStream_t>(stream);
   // with no activation rows every slot is inactive: the delta is +0 and the
   // finalize has no FC2 row to combine, so neither act nor fc2 is read
   if (padded_rows == 0) fc2 = nullptr;
-  MI_REQUIRE(out != nullptr, "bgmv_moe_gemm2_lora_delta: out is null");
-  MI_REQUIRE(aligned16(out), "bgmv_moe_gemm2_lora_delta: out must be 16-byte aligned");
-  MI_REQUIRE(lora_ids != nullptr && topk_ids != nullptr && topk_weights != nullptr &&
-                 perm != nullptr,
-             "bgmv_moe_gemm2_lora_delta: index/weight tensors must be non-null");
-  if (L > 0)
-    MI_REQUIRE((act != nullptr || padded_rows == 0) && w_ptr_a != nullptr && w_ptr_b != nullptr,
-               "bgmv_moe_gemm2_lora_delta: act and the pointer tables must be non-null");
-  MI_REQUIRE(aligned16(act), "bgmv_moe_gemm2_lora_delta: activation rows must be 16-byte aligned");
-  const Layout ly = layout(T, top_k, E, L, rank);
-  MI_REQUIRE(workspace != nullptr && workspace_bytes >= ly.total,
-             "bgmv_moe_gemm2_lora_delta: workspace needs %zu bytes (got %zu)", ly.total,
-             workspace_bytes);
-  MI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255) == 0,
-             "bgmv_moe_gemm2_lora_delta: workspace must be 256-byte aligned");
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint16_t* u2 = reinterpret_cast<uint16_t*>(ws + ly.u2);
-  int32_t* tok_list = reinterpret_cast<int32_t*>(ws + ly.tok_list);
-  Tile* tiles = reinterpret_cast<Tile*>(ws + ly.tiles);
-  int32_t* counters = reinterpret_cast<int32_t*>(ws + ly.counters);
-  int64_t* blk_a = reinterpret_cast<int64_t*>(ws + ly.blk_a);
-  int64_t* blk_b = reinterpret_cast<int64_t*>(ws + ly.blk_b);
-  int32_t* blk_row = reinterpret_cast<int32_t*>(ws + ly.blk_row);
-  float* blk_w = reinterpret_cast<float*>(ws + ly.blk_w);
-  float* blk_f = reinterpret_cast<float*>(ws + ly.blk_f);
-  const bool f16 = lora_dtype == MI_F16;
-  uint32_t* blk_tl = reinterpret_cast<uint32_t*>(ws + ly.blk_tl);
-  int32_t* tinfo = reinterpret_cast<int32_t*>(ws + ly.tinfo);
-  const int tt = tile_tokens(top_k);
-  const int ntiles = static_cast<int>(max_tiles(T, top_k, L));
-
-  int32_t* btile = reinterpret_cast<int32_t*>(ws + ly.btile);
-  int32_t* tex = reinterpret_cast<int32_t*>(ws + ly.tex);
-  PlanArgs pa{lora_ids, static_cast<int>(T), static_cast<int>(L), tt, tok_list, tiles, counters,
-              btile};
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, pa);
-  mi_status st = launch_status("bgmv_moe_gemm2_lora_delta (plan)");
-  if (st != MI_OK) return st;
-
-  const SlotSrc src{tok_list, perm, topk_ids, topk_weights, static_cast<int>(top_k),
-                    static_cast<int>(padded_rows), static_cast<int>(E)};
-  const int nb = rank_chunks(rank);
-  if (L > 0) {
-    ListArgs la{src, tiles, counters, topk_weights, w_ptr_a, static_cast<long>(lora_stride_a),
-                w_ptr_b, static_cast<long>(lora_stride_b), blk_a, blk_b, blk_tl, blk_row, blk_w,
-                tinfo, tex, static_cast<int>(L), ly.maxblk, scale};
-    hipLaunchKernelGGL(list_kernel, dim3(ntiles), dim3(NT_DELTA), 0, s, la);
-    st = launch_status("bgmv_moe_gemm2_lora_delta (list)");
-    if (st != MI_OK) return st;
-
-    // A_le held in LDS when it fits: one workgroup per (adapter, expert, part)
-    const bool by_le = nb <= 2 && 16 * nb * inter_size <= SLE_AMAX && inter_size % 128 == 0;
-    if (by_le) {
-      const long le = L * E;
-      const int S = le >= 2L * num_cus() ? 1 : 2;  // parts: the tiles of an adapter split S ways
-      MI_REQUIRE(le * S < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
-      ShrinkLeArgs sa{static_cast<const uint16_t*>(act), w_ptr_a, static_cast<long>(lora_stride_a),
-                      btile, tex, blk_row, blk_w, u2, blk_f, ly.cap,
-                      static_cast<int>(inter_size), static_cast<int>(E), static_cast<int>(L),
-                      static_cast<int>(rank), ly.maxblk, S};
-      const dim3 g(static_cast<unsigned>(le * S)), b(256);
-      switch (nb * 2 + (f16 ? 1 : 0)) {
-        case 2: hipLaunchKernelGGL((shrink_le_kernel<1, false>), g, b, 0, s, sa); break;
-        case 3: hipLaunchKernelGGL((shrink_le_kernel<1, true>), g, b, 0, s, sa); break;
-        case 4: hipLaunchKernelGGL((shrink_le_kernel<2, false>), g, b, 0, s, sa); break;
-        default: hipLaunchKernelGGL((shrink_le_kernel<2, true>), g, b, 0, s, sa); break;
-      }
-    } else {
-      const int bpt = (ly.maxblk + SHR_WAVES - 1) / SHR_WAVES;  // shrink workgroups per tile
-      const long swg = static_cast<long>(ntiles) * bpt;
-      MI_REQUIRE(swg < (1L << 31), "bgmv_moe_gemm2_lora_delta: problem too large");
-      ShrinkArgs sa{static_cast<const uint16_t*>(act), tiles, counters, blk_a, blk_row, blk_w, tinfo,
-                    u2, blk_f, ly.cap, static_cast<int>(inter_size), static_cast<int>(L),
-                    static_cast<int>(rank), ly.maxblk, bpt};
-      const dim3 sgrid(static_cast<unsigned>(swg)), sblock(64 * SHR_WAVES);
-      switch (nb * 2 + (f16 ? 1 : 0)) {
-        case 2: hipLaunchKernelGGL((shrink_kernel<1, false>), sgrid, sblock, 0, s, sa); break;
-        case 3: hipLaunchKernelGGL((shrink_kernel<1, true>), sgrid, sblock, 0, s, sa); break;
-        case 4: hipLaunchKernelGGL((shrink_kernel<2, false>), sgrid, sblock, 0, s, sa); break;
-        case 5: hipLaunchKernelGGL((shrink_kernel<2, true>), sgrid, sblock, 0, s, sa); break;
-        case 8: hipLaunchKernelGGL((shrink_kernel<4, false>), sgrid, sblock, 0, s, sa); break;
-        case 9: hipLaunchKernelGGL((shrink_kernel<4, true>), sgrid, sblock, 0, s, sa); break;
-        case 16: hipLaunchKernelGGL((shrink_kernel<8, false>), sgrid, sblock, 0, s, sa); break;
-        default: hipLaunchKernelGGL((shrink_kernel<8, true>), sgrid, sblock, 0, s, sa); break;
-      }
-    }
-    st = launch_status("bgmv_moe_gemm2_lora_delta (shrink)");
-    if (st != MI_OK) return st;
-  }
+  Front f;
+  mi_status st = run_front(what, act, padded_rows, inter_size, perm, w_ptr_a, lora_stride_a,
+                           w_ptr_b, lora_stride_b, topk_ids, topk_weights, lora_ids, T, top_k, E,
+                           L, rank, H, lora_dtype, scale, out_dtype, out, workspace,
+                           workspace_bytes, s, f);
+  if (st != MI_OK || T == 0) return st;
+  const Layout& ly = f.ly;
+  uint8_t* ws = f.ws;
+  const int ntiles = f.ntiles, nb = f.nb;
+  const bool f16 = f.f16;
+  uint16_t* u2 = f.u2;
+  int32_t* tok_list = f.tok_list;
+  Tile* tiles = f.tiles;
+  int32_t* counters = f.counters;
+  int64_t* blk_b = f.blk_b;
+  uint32_t* blk_tl = f.blk_tl;
+  float* blk_f = f.blk_f;
+  int32_t* tinfo = f.tinfo;
 
   const int nch = static_cast<int>(H / EXP_CW);
   // Finalize in two passes when the workspace also holds an fp32 [T, H] delta:
@@ -1418,6 +1595,58 @@ mi_status run_delta(const char* what, const void* act, int64_t padded_rows, int6
   return launch_status("moe_fc2_finalize_lora (combine)");
 }
 
+
+// FC1 LoRA delta: the shared front end, then the expand by (adapter, expert)
+// and the +0 rows of the slots without adapter or with an invalid expert.
+mi_status run_fc1(const void* act, int64_t padded_rows, int64_t hidden, const int32_t* perm,
+                  const int64_t* w_ptr_a, int64_t lora_stride_a, const int64_t* w_ptr_b,
+                  int64_t lora_stride_b, const int32_t* topk_ids, const int32_t* lora_ids,
+                  int64_t T, int64_t top_k, int64_t E, int64_t L, int64_t rank, int64_t OF,
+                  mi_dtype lora_dtype, float scale, mi_dtype out_dtype, void* out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "moe_fc1_lora_delta";
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Front f;
+  mi_status st = run_front(what, act, padded_rows, hidden, perm, w_ptr_a, lora_stride_a, w_ptr_b,
+                           lora_stride_b, topk_ids, nullptr, lora_ids, T, top_k, E, L, rank, OF,
+                           lora_dtype, scale, out_dtype, out, workspace, workspace_bytes, s, f);
+  if (st != MI_OK || T == 0 || padded_rows == 0) return st;
+  const int out_kind = out_dtype == MI_F32 ? 1 : (out_dtype == MI_F16 ? 2 : 0);
+  const long esize = out_dtype == MI_F32 ? 4 : 2;
+  if (L > 0) {
+    const int nch = static_cast<int>(OF / EXP_CW);
+    const long wg = L * E * nch;
+    MI_REQUIRE(wg < (1L << 31), "%s: problem too large", what);
+    Fc1Args fa{f.btile, f.tex, f.u2, w_ptr_b, static_cast<long>(lora_stride_b), f.blk_tl,
+               f.blk_row, f.blk_f, out, f.ly.cap, static_cast<int>(E), static_cast<int>(L),
+               static_cast<int>(rank), static_cast<int>(OF), f.ly.maxblk, nch, out_kind};
+    const bool part = rank != 16 * f.nb;
+    const dim3 g(static_cast<unsigned>(wg)), b(256);
+    switch (f.nb * 4 + (part ? 2 : 0) + (f.f16 ? 1 : 0)) {
+#define MI_FC1_CASE(NB_, PART_, F16_)                                                  \
+  case NB_ * 4 + (PART_ ? 2 : 0) + (F16_ ? 1 : 0):                                      \
+    hipLaunchKernelGGL((fc1_expand_kernel<NB_, PART_, F16_>), g, b, 0, s, fa); break;
+      MI_FC1_CASE(1, false, false) MI_FC1_CASE(1, false, true)
+      MI_FC1_CASE(1, true, false) MI_FC1_CASE(1, true, true)
+      MI_FC1_CASE(2, false, false) MI_FC1_CASE(2, false, true)
+      MI_FC1_CASE(2, true, false) MI_FC1_CASE(2, true, true)
+      MI_FC1_CASE(4, false, false) MI_FC1_CASE(4, false, true)
+      MI_FC1_CASE(4, true, false) MI_FC1_CASE(4, true, true)
+      MI_FC1_CASE(8, false, false) MI_FC1_CASE(8, false, true)
+      MI_FC1_CASE(8, true, false) MI_FC1_CASE(8, true, true)
+#undef MI_FC1_CASE
+      default: MI_REQUIRE(false, "%s: no expand variant (rank %lld)", what, (long long)rank);
+    }
+    st = launch_status(what);
+    if (st != MI_OK) return st;
+  }
+  const long nslot = T * top_k;
+  hipLaunchKernelGGL(fc1_zero_rows_kernel, dim3(static_cast<unsigned>((nslot + 3) / 4)), dim3(256),
+                     0, s, perm, topk_ids, lora_ids, nslot, static_cast<int>(top_k),
+                     static_cast<int>(E), static_cast<int>(L), static_cast<int>(padded_rows), out,
+                     OF * esize);
+  return launch_status(what);
+}
 }  // namespace
 }  // namespace mi
 
@@ -1452,4 +1681,22 @@ extern "C" mi_status mi_moe_fc2_finalize_lora(
                        lora_stride_a, w_ptr_b, lora_stride_b, topk_ids, topk_weights, lora_ids, T,
                        top_k, E, L, rank, H, lora_dtype, scale, fc2, fc2_dtype, out_dtype, out,
                        workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t mi_moe_fc1_lora_delta_workspace_size(int64_t num_tokens, int64_t top_k,
+                                                       int64_t num_experts, int64_t num_adapters,
+                                                       int64_t rank) {
+  return mi_moe_fc2_lora_delta_workspace_size(num_tokens, top_k, num_experts, num_adapters, rank);
+}
+
+extern "C" mi_status mi_moe_fc1_lora_delta(
+    const void* act, int64_t padded_rows, int64_t hidden_size, const int32_t* perm,
+    const int64_t* w_ptr_a, int64_t lora_stride_a, const int64_t* w_ptr_b, int64_t lora_stride_b,
+    const int32_t* topk_ids, const int32_t* lora_ids, int64_t T, int64_t top_k, int64_t E,
+    int64_t L, int64_t rank, int64_t out_features, mi_dtype lora_dtype, float scale,
+    mi_dtype out_dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  mi::clear_error();
+  return mi::run_fc1(act, padded_rows, hidden_size, perm, w_ptr_a, lora_stride_a, w_ptr_b,
+                     lora_stride_b, topk_ids, lora_ids, T, top_k, E, L, rank, out_features,
+                     lora_dtype, scale, out_dtype, out, workspace, workspace_bytes, stream);
 }

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert syms == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(L, s), s
-    assert L.mi_abi_version() == 7
+    assert L.mi_abi_version() == 8
 
 
 def _err(status):
@@ -182,3 +182,41 @@ def test_swiglu_validation():
     assert "16-byte aligned" in _err(g(out=FAKE + 8))
     assert "null" in _err(g(mi=NULL))
     assert g(m=0, a=NULL, out=NULL) == 0
+
+
+def test_fp4_quantize_validation():
+    L = _lib.lib()
+    q = lambda **kw: L.mi_fp4_quantize(*{**dict(
+        x=FAKE, batch=1, rows=300, k=512, dt=_lib.MI_BF16, g=FAKE, codes=FAKE, sf=FAKE,
+        sfb=1 << 30, stream=NULL), **kw}.values())
+    assert "multiple of 64" in _err(q(k=96))
+    assert "multiple of 64" in _err(q(k=0))
+    assert "batch" in _err(q(batch=0))
+    assert "bf16, fp16 or fp32" in _err(q(dt=7))
+    assert "sf holds" in _err(q(sfb=3 * 8 * 512 - 1))
+    assert q(sfb=3 * 8 * 512, rows=0, x=NULL, codes=NULL, sf=NULL) == 0  # no rows: no-op
+    assert "null" in _err(q(g=NULL))
+    assert "16-byte aligned" in _err(q(x=FAKE + 8))
+    assert "4-byte aligned" in _err(q(sf=FAKE + 2))
+
+
+def test_fc1_delta_validation():
+    L = _lib.lib()
+    f = lambda **kw: L.mi_moe_fc1_lora_delta(*{**dict(
+        act=FAKE, padded_rows=64, hidden=128, perm=FAKE, wa=FAKE, sa=1024, wb=FAKE, sb=1024,
+        ids=FAKE, lids=FAKE, T=16, k=2, E=4, L=2, r=16, out_features=256, ldt=_lib.MI_BF16,
+        scale=2.0, odt=_lib.MI_BF16, out=FAKE, ws=FAKE, wsb=1 << 30, stream=NULL),
+        **kw}.values())
+    assert "moe_fc1_lora_delta" in _err(f(r=12)) and "rank" in _err(f(r=12))
+    assert "top_k" in _err(f(k=0))
+    assert "workspace" in _err(f(wsb=16))
+    assert "strides" in _err(f(sb=1001))
+    with pytest.raises(NotImplementedError):
+        _lib.check(f(out_features=200))
+    with pytest.raises(NotImplementedError, match="below 4 GiB"):
+        _lib.check(f(out_features=1 << 27))
+    assert "activation width" in _err(f(hidden=12))
+    assert "16-byte aligned" in _err(f(out=FAKE + 8))
+    assert f(T=0, act=NULL, perm=NULL, ids=NULL, lids=NULL, out=NULL, ws=NULL) == 0
+    assert L.mi_moe_fc1_lora_delta_workspace_size(8192, 8, 64, 8, 16) == \
+        L.mi_moe_fc2_lora_delta_workspace_size(8192, 8, 64, 8, 16)
