@@ -168,6 +168,34 @@ MI_API mi_status mi_moe_fc2_lora_delta(const void* act, int64_t padded_rows, int
                                 void* stream);
 
 /*
+ * mi_moe_fc2_lora_delta for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and result, with the workspace taken from a
+ * fixed array inside the library instead of a caller buffer.  The array holds
+ * MI_DELTA_SCRATCH_BYTES (32 MiB) on every GPU the library runs on, until the
+ * process ends; its device address is looked up once per device
+ * (hipGetSymbolAddress) on the first call there, with that device current.
+ * The call allocates nothing and clears nothing (the kernels write every
+ * scratch entry they read).  Problems whose
+ * mi_moe_fc2_lora_delta_workspace_size() exceeds the array return
+ * MI_EUNSUPPORTED.  Every call on one GPU uses the same array: calls that
+ * overlap on one device (different streams, or threads without ordering)
+ * race and give undefined results.
+ */
+#define MI_DELTA_SCRATCH_BYTES (32u << 20)
+MI_API mi_status mi_moe_fc2_lora_delta_noalloc(const void* act, int64_t padded_rows,
+                                        int64_t inter_size,
+                                        const int32_t* expanded_idx_to_permuted_idx,
+                                        const int64_t* w_ptr_a, int64_t lora_stride_a,
+                                        const int64_t* w_ptr_b, int64_t lora_stride_b,
+                                        const int32_t* topk_ids, const float* topk_weights,
+                                        const int32_t* lora_ids, int64_t num_tokens,
+                                        int64_t top_k, int64_t num_experts,
+                                        int64_t num_adapters, int64_t rank,
+                                        int64_t hidden_size, mi_dtype lora_dtype, float scale,
+                                        mi_dtype out_dtype, void* out, void* stream);
+
+/*
  * FC1 (gate/up) LoRA delta of a routed MoE: the gemm1_lora_delta that
  * flashinfer.fused_moe.bgmv_moe_gemm2_lora_delta (description) says FC1 runs
  * with.  The pages give no formula for it; this library computes the FC1

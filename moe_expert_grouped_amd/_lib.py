@@ -21,6 +21,7 @@ EXPORTS = [
     "mi_grouped_mm_swiglu",
     "mi_moe_fc2_lora_delta_workspace_size",
     "mi_moe_fc2_lora_delta",
+    "mi_moe_fc2_lora_delta_noalloc",
     "mi_moe_fc2_finalize_lora",
     "mi_moe_fc1_lora_delta_workspace_size",
     "mi_moe_fc1_lora_delta",
@@ -71,6 +72,10 @@ def lib() -> ctypes.CDLL:
             I64, I64, I64, I64, I64, I64,  # T, top_k, E, L, rank, H
             I32, F32, I32,        # lora_dtype, scale, out_dtype
             P, P, SZ, P]          # out, workspace, bytes, stream
+        L.mi_moe_fc2_lora_delta_noalloc.restype = I32
+        L.mi_moe_fc2_lora_delta_noalloc.argtypes = [
+            P, I64, I64, P, P, I64, P, I64, P, P, P,
+            I64, I64, I64, I64, I64, I64, I32, F32, I32, P, P]
         L.mi_moe_fc2_finalize_workspace_size.restype = SZ
         L.mi_moe_fc2_finalize_workspace_size.argtypes = [I64, I64, I64, I64, I64, I64]
         L.mi_moe_fc2_finalize_lora.restype = I32

@@ -49,7 +49,15 @@
 //             wavefront in block order: the summation order per token is fixed
 //             and the result is bitwise repeatable.  Tokens without adapter
 //             get +0 rows.
+#include <mutex>
+
 #include "common.hpp"
+
+// Scratch of the allocation-free delta entry point: one fixed array per GPU
+// (each device the library runs on holds its own copy until the process
+// ends).  Host code never passes this name to a kernel; it uses the device
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MI_DELTA_SCRATCH_BYTES];
 
 namespace mi {
 namespace {
@@ -1384,13 +1392,12 @@ struct Front {
 // the plan, list and shrink launches.  `act` is [padded_rows, in_width] (I for
 // FC2, hidden for FC1); B_le is [out_width, rank] (H for FC2, 2I for FC1);
 // topk_weights may be NULL (unit weights).
-mi_status run_front(const char* what, const void* act, int64_t padded_rows, int64_t in_width,
-                    const int32_t* perm, const int64_t* w_ptr_a, int64_t lora_stride_a,
-                    const int64_t* w_ptr_b, int64_t lora_stride_b, const int32_t* topk_ids,
-                    const float* topk_weights, const int32_t* lora_ids, int64_t T, int64_t top_k,
-                    int64_t E, int64_t L, int64_t rank, int64_t out_width, mi_dtype lora_dtype,
-                    float scale, mi_dtype out_dtype, void* out, void* workspace,
-                    size_t workspace_bytes, hipStream_t s, Front& f) {
+mi_status check_front(const char* what, const void* act, int64_t padded_rows, int64_t in_width,
+                      const int32_t* perm, const int64_t* w_ptr_a, int64_t lora_stride_a,
+                      const int64_t* w_ptr_b, int64_t lora_stride_b, const int32_t* topk_ids,
+                      const int32_t* lora_ids, int64_t T, int64_t top_k, int64_t E, int64_t L,
+                      int64_t rank, int64_t out_width, mi_dtype lora_dtype, mi_dtype out_dtype,
+                      void* out) {
   MI_REQUIRE(top_k >= 1 && top_k <= MAX_TOPK, "%s: top_k must be in [1, %d]", what, MAX_TOPK);
   MI_REQUIRE(T >= 0 && T * top_k < (1LL << 24), "%s: num_tokens * top_k must be < 2^24", what);
   MI_REQUIRE(E >= 1 && E <= MAX_EXPERTS, "%s: num_experts must be in [1, %d]", what,
@@ -1428,6 +1435,20 @@ mi_status run_front(const char* what, const void* act, int64_t padded_rows, int6
     MI_REQUIRE((act != nullptr || padded_rows == 0) && w_ptr_a != nullptr && w_ptr_b != nullptr,
                "%s: act and the pointer tables must be non-null", what);
   MI_REQUIRE(aligned16(act), "%s: activation rows must be 16-byte aligned", what);
+  return MI_OK;
+}
+
+mi_status run_front(const char* what, const void* act, int64_t padded_rows, int64_t in_width,
+                    const int32_t* perm, const int64_t* w_ptr_a, int64_t lora_stride_a,
+                    const int64_t* w_ptr_b, int64_t lora_stride_b, const int32_t* topk_ids,
+                    const float* topk_weights, const int32_t* lora_ids, int64_t T, int64_t top_k,
+                    int64_t E, int64_t L, int64_t rank, int64_t out_width, mi_dtype lora_dtype,
+                    float scale, mi_dtype out_dtype, void* out, void* workspace,
+                    size_t workspace_bytes, hipStream_t s, Front& f) {
+  mi_status st0 = check_front(what, act, padded_rows, in_width, perm, w_ptr_a, lora_stride_a,
+                              w_ptr_b, lora_stride_b, topk_ids, lora_ids, T, top_k, E, L, rank,
+                              out_width, lora_dtype, out_dtype, out);
+  if (st0 != MI_OK || T == 0) return st0;
   f.ly = layout(T, top_k, E, L, rank);
   const Layout& ly = f.ly;
   MI_REQUIRE(workspace != nullptr && workspace_bytes >= ly.total,
@@ -1699,4 +1720,67 @@ extern "C" mi_status mi_moe_fc1_lora_delta(
   return mi::run_fc1(act, padded_rows, hidden_size, perm, w_ptr_a, lora_stride_a, w_ptr_b,
                      lora_stride_b, topk_ids, lora_ids, T, top_k, E, L, rank, out_features,
                      lora_dtype, scale, out_dtype, out, workspace, workspace_bytes, stream);
+}
+
+namespace mi {
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES];  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up once per device
+// (hipGetSymbolAddress: no allocation).
+mi_status scratch_address(const char* what, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) {
+    set_error("%s: no usable current device (%s)", what, hipGetErrorString(e));
+    return MI_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      set_error("%s: hipGetSymbolAddress of the scratch array failed (%s)", what,
+                hipGetErrorString(e));
+      return MI_EHIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MI_OK;
+}
+
+}  // namespace
+}  // namespace mi
+
+extern "C" mi_status mi_moe_fc2_lora_delta_noalloc(
+    const void* act, int64_t padded_rows, int64_t inter_size, const int32_t* perm,
+    const int64_t* w_ptr_a, int64_t lora_stride_a, const int64_t* w_ptr_b, int64_t lora_stride_b,
+    const int32_t* topk_ids, const float* topk_weights, const int32_t* lora_ids, int64_t T,
+    int64_t top_k, int64_t E, int64_t L, int64_t rank, int64_t H, mi_dtype lora_dtype, float scale,
+    mi_dtype out_dtype, void* out, void* stream) {
+  using namespace mi;
+  const char* what = "moe_fc2_lora_delta_noalloc";
+  clear_error();
+  mi_status st = check_front(what, act, padded_rows, inter_size, perm, w_ptr_a, lora_stride_a,
+                             w_ptr_b, lora_stride_b, topk_ids, lora_ids, T, top_k, E, L, rank, H,
+                             lora_dtype, out_dtype, out);
+  if (st != MI_OK || T == 0) return st;
+  MI_REQUIRE(topk_weights != nullptr, "%s: topk_weights is null", what);
+  const size_t need = layout(T, top_k, E, L, rank).total;
+  MI_REQUIRE_SUPPORTED(need <= MI_DELTA_SCRATCH_BYTES,
+                       "%s: this problem needs %zu bytes of scratch; the fixed array holds %zu "
+                       "(use mi_moe_fc2_lora_delta with a workspace)", what, need,
+                       static_cast<size_t>(MI_DELTA_SCRATCH_BYTES));
+  void* ws = nullptr;
+  st = scratch_address(what, &ws);
+  if (st != MI_OK) return st;
+  // the delta writes every workspace entry it reads, so nothing needs clearing
+  return run_delta(what, act, padded_rows, inter_size, perm, w_ptr_a, lora_stride_a, w_ptr_b,
+                   lora_stride_b, topk_ids, topk_weights, lora_ids, T, top_k, E, L, rank, H,
+                   lora_dtype, scale, nullptr, MI_BF16, out_dtype, out, ws,
+                   MI_DELTA_SCRATCH_BYTES, stream);
 }

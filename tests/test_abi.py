@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert syms == set(_lib.EXPORTS)
     for s in syms:
         assert hasattr(L, s), s
-    assert L.mi_abi_version() == 8
+    assert L.mi_abi_version() == 9
 
 
 def _err(status):
