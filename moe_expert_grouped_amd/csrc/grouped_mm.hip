@@ -309,7 +309,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_mm_kernel(
 // (144 bytes): the 32 rows of a fragment read and the 8 chunks of a row write
 // both spread over all banks.
 // ---------------------------------------------------------------------------
-constexpr int GB_BN = 256, GB_BK = 64, GB_P = 2;
+constexpr int GB_BN = 256, GB_BK = 64;
+constexpr int GB_P = 2;   // K steps of global loads in flight, 256-row tiles
+constexpr int GB_PH = 2;  // the same for 128-row tiles
 constexpr int GB_RS = GB_BK + 8;                 // padded LDS row (16-bit elements)
 constexpr int GB_STAGE = (256 + GB_BN) * GB_RS;  // elements per LDS stage (largest tile)
 
@@ -457,7 +459,7 @@ struct GbGlu {
 // tile then covers 128 output columns c0 = n0/2 ..: each wavefront's b
 // fragments j < FN/2 are gate rows and j >= FN/2 the matching up rows, so one
 // lane holds both operands of every output it writes; out is [m_rows, I].
-template <int FN, bool F16, bool GLU, typename OutT>
+template <int FN, int P, bool F16, bool GLU, typename OutT>
 __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
                                         const uint16_t* __restrict__ b, OutT* __restrict__ out,
                                         uint16_t* smem, int e, int m0, int rows, int n0, int k,
@@ -511,7 +513,7 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
   struct Frag {
     u32x4 a[4], b[FN];
   };
-  u32x4 ra[GB_P][CPT_A], rb[GB_P][CPT_B];
+  u32x4 ra[P][CPT_A], rb[P][CPT_B];
   auto gload = [&](int p, int kt) {
     // stages past the end reload the last one: every step issues the same loads
     const uint32_t so = static_cast<uint32_t>(min(kt, KT - 1)) * (GB_BK * 2);
@@ -546,12 +548,12 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
 
   Frag f0, f1;
 #pragma unroll
-  for (int p = 0; p < GB_P; ++p) {
+  for (int p = 0; p < P; ++p) {
     gload(p, p);
     __builtin_amdgcn_sched_barrier(0);  // slots in order: the loop's waits stay exact
   }
   lstore(0, smem);
-  gload(0, GB_P);
+  gload(0, P);
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   fload(f0, smem, 0);
@@ -566,7 +568,7 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
     __builtin_amdgcn_sched_barrier(0);
     fload(f0, st, 2);
     lstore(q, nx);
-    gload(q, kt + 1 + GB_P);
+    gload(q, kt + 1 + P);
     mma(f1);
     gb_interleave_copy<NR, NM, CPT_A + CPT_B>();
     __builtin_amdgcn_sched_barrier(0);
@@ -584,12 +586,15 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
   };
   // The loop body is straight-line code (all MFMAs unconditional: rows past
   // the group's end are zeros), so the compiler's wait counts stay exact.
+  // register slot (kt + 1) % P holds stage kt + 1
   int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    kstep(kt, 1);
-    kstep(kt + 1, 0);
+  for (; kt + P <= KT; kt += P) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) kstep(kt + q, (q + 1) % P);
   }
-  if (kt < KT) kstep(kt, 1);
+#pragma unroll
+  for (int q = 0; q < P - 1; ++q)
+    if (kt + q < KT) kstep(kt + q, (q + 1) % P);
 
   if (wm * 128 >= rows) return;  // all of this wavefront's rows lie past the group's end
   if constexpr (!GLU) {
@@ -693,7 +698,7 @@ __global__ __launch_bounds__(256, 1) void grouped_mm_big_kernel(
     const int m0 = __builtin_amdgcn_readfirstlane(s_row0[e] + (mt - s_full0[e]) * 256);
     const int end = max(s_row0[e + 1], s_row0[e]);
     const int rows = __builtin_amdgcn_readfirstlane(min(end - m0, 256));
-    gb_tile<4, F16, GLU, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n, gl);
+    gb_tile<4, GB_P, F16, GLU, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n, gl);
   } else {
     const long L = xcd * run_h + (slot - run_f);
     if (slot - run_f >= run_h || L >= total_h) return;
@@ -704,7 +709,7 @@ __global__ __launch_bounds__(256, 1) void grouped_mm_big_kernel(
     const int m0 = __builtin_amdgcn_readfirstlane(s_row0[e] + (s_full0[e + 1] - s_full0[e]) * 256);
     const int end = max(s_row0[e + 1], s_row0[e]);
     const int rows = __builtin_amdgcn_readfirstlane(end - m0);
-    gb_tile<2, F16, GLU, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n, gl);
+    gb_tile<2, GB_PH, F16, GLU, OutT>(a, b, out, smem, e, m0, rows, ni * GB_BN, k, n, gl);
   }
 }
 
