@@ -10,8 +10,11 @@
 //   even code, saturating at 448;  S = value(sf);  r = g / S (0 if S == 0);
 //   code_i = E2M1(x_i * r) nearest, ties to the even code, saturating at 6,
 //   sign bit from the sign of the product.
-// Both roundings are done here with integer and comparison logic (no
-// hardware conversion), so the codes follow the definition exactly.
+// The scale rounding is integer logic on the fp32 bit pattern; the element
+// rounding is v_cvt_scalef32_pk_fp4_f32 at scale 1.0, which rounds to the
+// nearest E2M1 value with ties to the even code, saturates at 6 and keeps the
+// sign -- the definition (checked bitwise against the oracle, midpoints and
+// saturation included, by the GPU tests).
 //
 // Work split: HBM-bound.  Lane j of a wavefront holds 8 consecutive elements
 // (one 16-byte load for 16-bit inputs), so each load instruction of a
@@ -45,14 +48,6 @@ __device__ __forceinline__ float ue4m3_value(uint32_t c) {
                 : __builtin_amdgcn_ldexpf(static_cast<float>(8 + M), E - 10);
 }
 
-// fp32 t -> E2M1 code: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even
-// code, saturating at 6; bit 3 = sign of t
-__device__ __forceinline__ uint32_t e2m1_rne_sat(float t) {
-  const float a = fabsf(t);
-  const uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-                     (a >= 3.5f) + (a > 5.f);
-  return m | ((__float_as_uint(t) >> 28) & 8u);
-}
 
 template <typename T>
 struct Chunk8;  // 8 consecutive input elements of one lane
@@ -91,8 +86,10 @@ struct QzArgs {
   uint8_t* codes;       // [batch, rows, k/2]
   uint8_t* sf;          // batch consecutive 128x4 buffers of sf_per bytes
   long chunks;          // batch * rows * k / 8
-  long per_batch;       // rows * k / 8 chunks of one matrix
-  int k, nct;           // nct: 128x4 tiles along K (k / 64)
+  uint32_t per_batch;   // rows * k / 8 chunks of one matrix (< 2^31)
+  uint32_t cpr;         // chunks per row (k / 8)
+  int nct;              // 128x4 tiles along K (k / 64)
+  int batched;          // batch > 1
   long sf_per;
 };
 
@@ -117,7 +114,7 @@ __global__ __launch_bounds__(QZ_THREADS) void fp4_quantize_kernel(QzArgs p) {
     // the whole wavefront reaches the shuffles; chunks past the end compute
     // on whatever their registers hold and store nothing
     const bool in = c[j] < p.chunks;
-    const long bi = in ? c[j] / p.per_batch : 0;
+    const uint32_t bi = (in && p.batched) ? static_cast<uint32_t>(c[j] / p.per_batch) : 0u;
     const float g = in ? gld<float>(p.gscale + bi) : 0.f;
     float xs[8], am = 0.f;
 #pragma unroll
@@ -129,9 +126,16 @@ __global__ __launch_bounds__(QZ_THREADS) void fp4_quantize_kernel(QzArgs p) {
     const uint32_t sfc = ue4m3_rne_sat(__fdiv_rn(__fmul_rn(am, g), 6.f));
     const float S = ue4m3_value(sfc);
     const float r = S == 0.f ? 0.f : __fdiv_rn(g, S);
+    // the 8 codes, element 2i in the low nibble of byte i
     uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= e2m1_rne_sat(__fmul_rn(xs[i], r)) << (4 * i);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __fmul_rn(xs[0], r), __fmul_rn(xs[1], r),
+                                                 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __fmul_rn(xs[2], r), __fmul_rn(xs[3], r),
+                                                 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __fmul_rn(xs[4], r), __fmul_rn(xs[5], r),
+                                                 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __fmul_rn(xs[6], r), __fmul_rn(xs[7], r),
+                                                 1.0f, 3);
     // scale word of lanes 8q .. 8q+7: the blocks of lanes 8q, 8q+2, 8q+4, 8q+6
     const int b8 = lane & ~7;
     const uint32_t sw = static_cast<uint32_t>(__shfl(static_cast<int>(sfc), b8)) |
@@ -141,9 +145,10 @@ __global__ __launch_bounds__(QZ_THREADS) void fp4_quantize_kernel(QzArgs p) {
     if (!in) continue;
     gst<uint32_t>(p.codes + c[j] * 4, w);
     if ((lane & 7) == 0) {
-      const long e0 = (c[j] - bi * p.per_batch) * 8;  // element index inside the matrix
-      const int row = static_cast<int>(e0 / p.k), col = static_cast<int>(e0 % p.k);
-      gst<uint32_t>(p.sf + bi * p.sf_per + sf_word_off(row, col >> 6, p.nct), sw);
+      // chunk index inside the matrix -> row and 64-element column group
+      const uint32_t cm = static_cast<uint32_t>(c[j] - static_cast<long>(bi) * p.per_batch);
+      const uint32_t row = cm / p.cpr, cg = (cm - row * p.cpr) >> 3;
+      gst<uint32_t>(p.sf + bi * p.sf_per + sf_word_off(static_cast<int>(row), cg, p.nct), sw);
     }
   }
 }
@@ -179,7 +184,8 @@ extern "C" mi_status mi_fp4_quantize(const void* x, int64_t batch, int64_t rows,
   MI_REQUIRE(x_dtype == MI_BF16 || x_dtype == MI_F16 || x_dtype == MI_F32,
              "fp4_quantize: x must be bf16, fp16 or fp32");
   const size_t per = qz_sf_bytes(rows, k);
-  MI_REQUIRE(batch * rows * k < (1LL << 40) && per * static_cast<size_t>(batch) < (1ULL << 40),
+  MI_REQUIRE(batch * rows * k < (1LL << 40) && per * static_cast<size_t>(batch) < (1ULL << 40) &&
+                 rows * (k / 8) < (1LL << 31),
              "fp4_quantize: problem too large");
   if (rows == 0) return MI_OK;
   MI_REQUIRE(x && global_scale && codes && sf, "fp4_quantize: null pointer argument");
@@ -196,9 +202,10 @@ extern "C" mi_status mi_fp4_quantize(const void* x, int64_t batch, int64_t rows,
   a.gscale = global_scale;
   a.codes = codes;
   a.sf = sf;
-  a.per_batch = rows * k / 8;
-  a.chunks = batch * a.per_batch;
-  a.k = static_cast<int>(k);
+  a.per_batch = static_cast<uint32_t>(rows * k / 8);
+  a.chunks = batch * static_cast<long>(a.per_batch);
+  a.cpr = static_cast<uint32_t>(k / 8);
+  a.batched = batch > 1;
   a.nct = static_cast<int>(k / 64);
   a.sf_per = static_cast<long>(per);
   const long waves = (a.chunks + 64 * QZ_SEG - 1) / (64 * QZ_SEG);

@@ -643,6 +643,7 @@ __global__ __launch_bounds__(64 * SHR_WAVES) void shrink_kernel(ShrinkArgs p) {
 // does once per block.
 constexpr int SLE_KC = 128;          // activation K elements per wave stage
 constexpr int SLE_AMAX = 16 * 2048;  // bf16 of A_le held in LDS: 16 * NB * I <= SLE_AMAX
+constexpr int SLE_AMAX_BIG = 16 * 4096;  // the one-workgroup-per-CU variant (128 KB of A_le)
 
 struct ShrinkLeArgs {
   const uint16_t* act;
@@ -658,13 +659,13 @@ struct ShrinkLeArgs {
   int I, E, L, rank, maxblk, S;
 };
 
-template <int NB, bool F16>  // NB: 1 or 2
-__global__ __launch_bounds__(256, 2) void shrink_le_kernel(ShrinkLeArgs p) {
+template <int NB, bool F16, int AMAX>  // NB: 1 or 2; AMAX: bf16 of A_le the LDS holds
+__global__ __launch_bounds__(256, AMAX > SLE_AMAX ? 1 : 2) void shrink_le_kernel(ShrinkLeArgs p) {
   constexpr int R16 = 16 * NB;       // A_le rows held (ranks past the rank repeat the last one)
   constexpr int CPR = SLE_KC / 8;    // 16-byte chunks per stage row
   constexpr int RPI = 64 / CPR;      // stage rows per coalesced load instruction
   constexpr int NLA = 16 / RPI;      // activation loads per lane per stage
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[SLE_AMAX];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[AMAX];
   __shared__ __attribute__((aligned(16))) uint16_t s_act[4][16 * SLE_KC];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1237,27 +1238,59 @@ __device__ __forceinline__ void store_out4(void* out, int kind, long off, f32x4 
   }
 }
 
-// One workgroup per (adapter l, expert e, chunk of EXP_CW output columns).
-// Its 4 wavefronts hold that chunk of B_le in registers (each lane: 4 ranks of
-// one column per 16-column group and rank chunk, the expand's [B | B] operand)
-// and take the blocks of (l, e) from every tile of adapter l in turn: per
-// block, one v_mfma_f32_16x16x32 per column group and rank chunk on [B | B]
-// and the block's [u_hi ; u_lo] record, then each lane stores its slot's 4
-// consecutive columns.  B_le is read from memory once per chunk.
-template <int NB, bool PART, bool F16>
+// 8 consecutive output columns of one row, rounded once (streaming stores:
+// the rows are written once and not read here)
+__device__ __forceinline__ void store_out8c(void* out, int kind, long off, f32x4 v0, f32x4 v1) {
+  if (kind == 1) {
+    __builtin_nontemporal_store(v0, reinterpret_cast<f32x4*>(static_cast<float*>(out) + off));
+    __builtin_nontemporal_store(v1, reinterpret_cast<f32x4*>(static_cast<float*>(out) + off + 4));
+  } else if (kind == 2) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const h8 h = {static_cast<_Float16>(v0.x), static_cast<_Float16>(v0.y),
+                  static_cast<_Float16>(v0.z), static_cast<_Float16>(v0.w),
+                  static_cast<_Float16>(v1.x), static_cast<_Float16>(v1.y),
+                  static_cast<_Float16>(v1.z), static_cast<_Float16>(v1.w)};
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h),
+                                reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + off));
+  } else {
+    const u32x4 w = {pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
+                     pack_bf16x2(v1.z, v1.w)};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + off));
+  }
+}
+
+constexpr int FC1_MAX_BLK = 256;  // blocks of one (adapter, expert) listed in LDS at once
+
+// One workgroup per (adapter l, expert e, chunk of CW output columns).
+// Wavefront 0 lists the blocks of (l, e) in the tiles of adapter l (tile,
+// block) into LDS; the four wavefronts then take them in turn.  Each
+// wavefront holds that chunk of B_le in registers (per lane: 4 ranks of one
+// column per 16-column group and rank chunk, the [B | B] operand of the FC2
+// expand); per block it runs one v_mfma_f32_16x16x32 per group and rank chunk
+// on [B | B] and the block's [u_hi ; u_lo] record.  The groups go in pairs
+// whose MFMA rows are permuted so that lane (slot, q) receives 8 consecutive
+// output columns of its slot's row from the pair and stores them as one
+// 16-byte piece (pair p covers columns 32p .. 32p+31 of the chunk: MFMA row i
+// of its first group is column 8(i/4) + i%4, of its second 8(i/4) + 4 + i%4).
+// B_le is read from memory once per chunk.
+template <int NB, bool PART, bool F16, int CW>
 __global__ __launch_bounds__(256) void fc1_expand_kernel(Fc1Args p) {
-  constexpr int NG = EXP_CW / 16;  // 16-column groups of the chunk
+  constexpr int NG = CW / 16;  // 16-column groups of the chunk (an even number)
+  __shared__ int s_blk[FC1_MAX_BLK];  // (tile << 12) | block of each listed block
+  __shared__ int s_nblk;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ch = blockIdx.x % p.nch, le = blockIdx.x / p.nch;
+  const int nch = p.OF / CW;
+  const int ch = blockIdx.x % nch, le = blockIdx.x / nch;
   const int l = le / p.E, e = le % p.E;
   if (l >= p.L) return;
   const int t0 = gld<int>(p.btile + l), t1 = gld<int>(p.btile + l + 1);
   const int E1 = p.E + 1;
   const int col = lane & 15, kq = lane >> 4;
-  const int h0 = ch * EXP_CW;
+  const int h0 = ch * CW;
 
-  // this lane's B_le fragments: column h0 + 16 g + col, ranks 16 c + 4 kq .. + 3
+  // this lane's B_le fragments: group g, MFMA row col -> output column
+  // h0 + 32 (g/2) + 8 (col/4) + 4 (g%2) + col%4, ranks 16 c + 4 kq .. + 3
   const char* ble = reinterpret_cast<const char*>(gld<int64_t>(p.w_ptr_b + e) + 2 * p.stride_b * l);
   const __amdgpu_buffer_rsrc_t brsrc =
       buf_rsrc(uniform_ptr(ble), static_cast<uint32_t>(p.OF) * p.R * 2);
@@ -1268,48 +1301,88 @@ __global__ __launch_bounds__(256) void fc1_expand_kernel(Fc1Args p) {
     const bool rin = r4 < p.R;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const uint32_t off = 2u * (static_cast<uint32_t>(h0 + 16 * g + col) * p.R +
-                                 (rin ? r4 : p.R - 4));
+      const int ocol = h0 + 32 * (g >> 1) + 8 * (col >> 2) + 4 * (g & 1) + (col & 3);
+      const uint32_t off = 2u * (static_cast<uint32_t>(ocol) * p.R + (rin ? r4 : p.R - 4));
       fb[g][c] = buf_ld64(brsrc, off, 0);
       if (PART && !rin) fb[g][c] = u32x2{0, 0};
     }
   }
 
-  int j = 0;
-  for (int ti = t0; ti < t1; ++ti) {
-    const int b0 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e);
-    const int b1 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e + 1);
-    for (int bi = b0; bi < b1; ++bi, ++j) {
-      if ((j & 3) != wave) continue;
-      const long tb = static_cast<long>(ti) * p.maxblk + bi;
-      const uint16_t* rec = p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32;
-      u32x4 fu[NB];
+  // the block list of (l, e): one lane per tile, a scan, then the entries
+  if (wave == 0) {
+    int n = 0;
+    for (int tb = t0; tb < t1; tb += 64) {
+      const int ti = tb + lane;
+      int b0 = 0, cnt = 0;
+      if (ti < t1) {
+        b0 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e);
+        cnt = gld<int>(p.tex + static_cast<long>(ti) * E1 + e + 1) - b0;
+      }
+      int incl = cnt;
 #pragma unroll
-      for (int c = 0; c < NB; ++c) fu[c] = gld<u32x4>(rec + c * 512 + lane * 8);
-      const int slot = col;
-      const uint32_t tlw = gld<uint32_t>(p.blk_tl + tb * 4 + (slot >> 2));
-      const bool real = ((tlw >> (8 * (slot & 3))) & 0xFFu) != 0xFFu;
-      const long row = gld<int>(p.blk_row + tb * 16 + slot);
-      const float fs = F16 ? gld<float>(p.blk_f + tb * 16 + slot) : 1.f;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      for (int i = 0; i < cnt; ++i) {
+        const int slot = n + incl - cnt + i;
+        if (slot < FC1_MAX_BLK) s_blk[slot] = ((ti - t0) << 12) | (b0 + i);
+      }
+      n += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) s_nblk = n;
+  }
+  __syncthreads();
+  const int nblk = s_nblk;
+
+  auto do_block = [&](int ti, int bi) {
+    const long tb = static_cast<long>(ti) * p.maxblk + bi;
+    const uint16_t* rec = p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32;
+    u32x4 fu[NB];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NB; ++c) fu[c] = gld<u32x4>(rec + c * 512 + lane * 8);
+    const int slot = col;
+    const uint32_t tlw = gld<uint32_t>(p.blk_tl + tb * 4 + (slot >> 2));
+    const bool real = ((tlw >> (8 * (slot & 3))) & 0xFFu) != 0xFFu;
+    const long row = gld<int>(p.blk_row + tb * 16 + slot);
+    const float fs = F16 ? gld<float>(p.blk_f + tb * 16 + slot) : 1.f;
+#pragma unroll
+    for (int gp = 0; gp < NG / 2; ++gp) {
+      f32x4 acc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
-          const u32x4 a4 = u32x4{fb[g][c].x, fb[g][c].y, fb[g][c].x, fb[g][c].y};
+          const u32x2 b2 = fb[2 * gp + h][c];
+          const u32x4 a4 = u32x4{b2.x, b2.y, b2.x, b2.y};
           if constexpr (F16)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a4),
-                                                         __builtin_bit_cast(f16x8, fu[c]), acc,
-                                                         0, 0, 0);
+            acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a4),
+                                                            __builtin_bit_cast(f16x8, fu[c]),
+                                                            acc[h], 0, 0, 0);
           else
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a4),
-                                                          __builtin_bit_cast(bf16x8, fu[c]), acc,
-                                                          0, 0, 0);
+            acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a4),
+                                                             __builtin_bit_cast(bf16x8, fu[c]),
+                                                             acc[h], 0, 0, 0);
         }
-        if (F16) acc = acc * fs;  // the slot's 2^-k: exact
-        // lane (slot, kq) holds columns 16 g + 4 kq .. + 3 of its slot's row
-        if (real) store_out4(p.out, p.out_kind, row * p.OF + h0 + 16 * g + 4 * kq, acc);
+        if (F16) acc[h] = acc[h] * fs;  // the slot's 2^-k: exact
       }
+      // lane (slot, kq): columns 32 gp + 8 kq .. + 7 of its slot's row
+      if (real) store_out8c(p.out, p.out_kind, row * p.OF + h0 + 32 * gp + 8 * kq, acc[0], acc[1]);
+    }
+  };
+  if (nblk <= FC1_MAX_BLK) {
+    for (int j = wave; j < nblk; j += 4) {
+      const int v = s_blk[j];
+      do_block(t0 + (v >> 12), v & 4095);
+    }
+  } else {  // more blocks than the list holds: walk the tiles directly
+    int j = 0;
+    for (int ti = t0; ti < t1; ++ti) {
+      const int b0 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e);
+      const int b1 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e + 1);
+      for (int bi = b0; bi < b1; ++bi, ++j)
+        if ((j & 3) == wave) do_block(ti, bi);
     }
   }
 }
@@ -1495,22 +1568,30 @@ mi_status run_front(const char* what, const void* act, int64_t padded_rows, int6
   st = launch_status(what);
   if (st != MI_OK) return st;
 
-  // A_le held in LDS when it fits: one workgroup per (adapter, expert, part)
-  const bool by_le = nb <= 2 && 16 * nb * in_width <= SLE_AMAX && in_width % 128 == 0;
+  // A_le held in LDS when it fits: one workgroup per (adapter, expert, part);
+  // up to 64 KB of A_le two workgroups per CU, up to 128 KB one
+  const bool by_le = nb <= 2 && 16 * nb * in_width <= SLE_AMAX_BIG && in_width % 128 == 0;
+  const bool big_a = 16 * nb * in_width > SLE_AMAX;
   if (by_le) {
     const long le = L * E;
-    const int S = le >= 2L * num_cus() ? 1 : 2;  // parts: the tiles of an adapter split S ways
+    // parts: the tiles of an adapter split S ways when the pairs alone would not
+    // fill every workgroup slot of the chip
+    const int S = le >= (big_a ? 1L : 2L) * num_cus() ? 1 : 2;
     MI_REQUIRE(le * S < (1L << 31), "%s: problem too large", what);
     ShrinkLeArgs sa{static_cast<const uint16_t*>(act), w_ptr_a, static_cast<long>(lora_stride_a),
                     f.btile, f.tex, f.blk_row, blk_w, u2, blk_f, ly.cap,
                     static_cast<int>(in_width), static_cast<int>(E), static_cast<int>(L),
                     static_cast<int>(rank), ly.maxblk, S};
     const dim3 g(static_cast<unsigned>(le * S)), b(256);
-    switch (nb * 2 + (f16 ? 1 : 0)) {
-      case 2: hipLaunchKernelGGL((shrink_le_kernel<1, false>), g, b, 0, s, sa); break;
-      case 3: hipLaunchKernelGGL((shrink_le_kernel<1, true>), g, b, 0, s, sa); break;
-      case 4: hipLaunchKernelGGL((shrink_le_kernel<2, false>), g, b, 0, s, sa); break;
-      default: hipLaunchKernelGGL((shrink_le_kernel<2, true>), g, b, 0, s, sa); break;
+    switch (nb * 4 + (f16 ? 2 : 0) + (big_a ? 1 : 0)) {
+      case 4: hipLaunchKernelGGL((shrink_le_kernel<1, false, SLE_AMAX>), g, b, 0, s, sa); break;
+      case 5: hipLaunchKernelGGL((shrink_le_kernel<1, false, SLE_AMAX_BIG>), g, b, 0, s, sa); break;
+      case 6: hipLaunchKernelGGL((shrink_le_kernel<1, true, SLE_AMAX>), g, b, 0, s, sa); break;
+      case 7: hipLaunchKernelGGL((shrink_le_kernel<1, true, SLE_AMAX_BIG>), g, b, 0, s, sa); break;
+      case 8: hipLaunchKernelGGL((shrink_le_kernel<2, false, SLE_AMAX>), g, b, 0, s, sa); break;
+      case 9: hipLaunchKernelGGL((shrink_le_kernel<2, false, SLE_AMAX_BIG>), g, b, 0, s, sa); break;
+      case 10: hipLaunchKernelGGL((shrink_le_kernel<2, true, SLE_AMAX>), g, b, 0, s, sa); break;
+      default: hipLaunchKernelGGL((shrink_le_kernel<2, true, SLE_AMAX_BIG>), g, b, 0, s, sa); break;
     }
   } else {
     const int bpt = (ly.maxblk + SHR_WAVES - 1) / SHR_WAVES;  // shrink workgroups per tile
@@ -1635,18 +1716,29 @@ mi_status run_fc1(const void* act, int64_t padded_rows, int64_t hidden, const in
   const int out_kind = out_dtype == MI_F32 ? 1 : (out_dtype == MI_F16 ? 2 : 0);
   const long esize = out_dtype == MI_F32 ? 4 : 2;
   if (L > 0) {
-    const int nch = static_cast<int>(OF / EXP_CW);
-    const long wg = L * E * nch;
+    // chunk width: 64 VGPRs of B fragments per lane (512 columns at rank <= 16)
+    const int cw = f.nb == 1 ? 512 : f.nb == 2 ? 256 : f.nb == 4 ? 128 : 64;
+    const int cwu = static_cast<int>(OF % cw == 0 ? cw : EXP_CW);  // OF % 128 == 0
+    const long wg = L * E * (OF / cwu);
     MI_REQUIRE(wg < (1L << 31), "%s: problem too large", what);
     Fc1Args fa{f.btile, f.tex, f.u2, w_ptr_b, static_cast<long>(lora_stride_b), f.blk_tl,
                f.blk_row, f.blk_f, out, f.ly.cap, static_cast<int>(E), static_cast<int>(L),
-               static_cast<int>(rank), static_cast<int>(OF), f.ly.maxblk, nch, out_kind};
+               static_cast<int>(rank), static_cast<int>(OF), f.ly.maxblk,
+               static_cast<int>(OF / cwu), out_kind};
     const bool part = rank != 16 * f.nb;
     const dim3 g(static_cast<unsigned>(wg)), b(256);
+    const bool full = cwu == cw;
     switch (f.nb * 4 + (part ? 2 : 0) + (f.f16 ? 1 : 0)) {
-#define MI_FC1_CASE(NB_, PART_, F16_)                                                  \
-  case NB_ * 4 + (PART_ ? 2 : 0) + (F16_ ? 1 : 0):                                      \
-    hipLaunchKernelGGL((fc1_expand_kernel<NB_, PART_, F16_>), g, b, 0, s, fa); break;
+#define MI_FC1_CASE(NB_, PART_, F16_)                                                        \
+  case NB_ * 4 + (PART_ ? 2 : 0) + (F16_ ? 1 : 0):                                            \
+    if (full)                                                                                 \
+      hipLaunchKernelGGL((fc1_expand_kernel<NB_, PART_, F16_,                                 \
+                                            NB_ == 1 ? 512 : NB_ == 2 ? 256 : NB_ == 4 ? 128 : 64>), \
+                         g, b, 0, s, fa);                                                     \
+    else                                                                                      \
+      hipLaunchKernelGGL((fc1_expand_kernel<NB_, PART_, F16_, (NB_ == 8 ? 64 : 128)>), g, b, 0, \
+                         s, fa);                                                              \
+    break;
       MI_FC1_CASE(1, false, false) MI_FC1_CASE(1, false, true)
       MI_FC1_CASE(1, true, false) MI_FC1_CASE(1, true, true)
       MI_FC1_CASE(2, false, false) MI_FC1_CASE(2, false, true)

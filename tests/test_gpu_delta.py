@@ -69,7 +69,9 @@ def test_tiny(gpu):
                                    (40, 64, 256), (48, 72, 128),
                                    # A_le held in LDS (rank <= 32, I % 128 == 0): the
                                    # shrink by (adapter, expert), up to its largest A_le
-                                   (16, 256, 256), (8, 384, 128), (32, 1024, 128)])
+                                   (16, 256, 256), (8, 384, 128), (32, 1024, 128),
+                                   # 64 to 128 KB of A_le: one workgroup per CU
+                                   (16, 4096, 128), (32, 2048, 256), (8, 3968, 128)])
 def test_integer_probe_bitwise_scattered_bank(gpu, r, I, H):
     case = to_dev(synth.delta_int_probe(r=r, I=I, H=H), gpu)
     tb = tables(case, scattered=True)
@@ -201,7 +203,7 @@ def test_fp16_output_integer_probe_bitwise(gpu):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("r,I,H", [(16, 64, 256), (8, 200, 128), (40, 64, 256), (48, 72, 128),
-                                   (64, 128, 256), (128, 64, 128)])
+                                   (64, 128, 256), (128, 64, 128), (16, 4096, 128)])
 def test_fp16_lora_integer_probe_bitwise(gpu, r, I, H):
     """Activation and banks in fp16: every intermediate of the integer probe
     is exact, so each output type is the exact value rounded once."""

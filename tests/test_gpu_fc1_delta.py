@@ -89,7 +89,8 @@ def test_integer_probe_bitwise(gpu, lora_dtype, scattered):
 
 
 @pytest.mark.parametrize("hidden,out_w,rank", [(256, 384, 16), (256, 256, 24), (192, 128, 64),
-                                               (2048, 256, 8), (320, 256, 128)])
+                                               (2048, 256, 8), (320, 256, 128), (4096, 640, 16),
+                                               (4096, 256, 32), (128, 1024, 16)])
 def test_random_within_tolerance(gpu, hidden, out_w, rank):
     """Rank 8..128 (one to eight 16-rank chunks, partial chunks masked) and
     both shrink paths (A_le in LDS when it fits, per tile otherwise)."""

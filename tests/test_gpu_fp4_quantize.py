@@ -85,6 +85,36 @@ def test_special_blocks(gpu):
         assert np.array_equal(sf, rsf), gval
 
 
+def test_element_rounding_sweep(gpu):
+    """Every block holds +-6 and g = 1, so its scale is 1.0 (code 0x38) and each
+    other element is rounded as it is: values within 8 ulps of every E2M1
+    midpoint and grid value (ties to the even code), both signs, and random
+    values up to 6 -- bitwise against the oracle."""
+    grid = [0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0]
+    vals = []
+    for v in grid:
+        b = np.float32(v).view(np.int32)
+        for d in range(-8, 9):
+            x = np.int32(b + d).view(np.float32) if v > 0 else np.float32(d * 1e-39)
+            if 0 <= x <= 6:
+                vals += [x, -x]
+    rng = np.random.default_rng(7)
+    vals += list(rng.uniform(-6, 6, 20000).astype(np.float32))
+    vals = np.asarray(vals, dtype=np.float32)
+    nblk = -(-len(vals) // 15)
+    pad = np.resize(vals, nblk * 15).reshape(nblk, 15)
+    blocks = np.concatenate([np.where(np.arange(nblk) % 2 == 0, 6.0, -6.0)[:, None], pad],
+                            axis=1).astype(np.float32)
+    rows = -(-nblk // 4)
+    x = np.resize(blocks, (rows * 4, 16)).reshape(rows, 64)
+    xt = torch.from_numpy(x)
+    codes, sf = _gpu(xt, torch.tensor([1.0]), gpu)
+    rc, rsf = Q.fp4_quantize(x, np.float32(1.0))
+    assert np.all(rsf[NV.sf_offset(np.arange(rows)[:, None], np.arange(4)[None, :], 64)] == 0x38)
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(sf, rsf)
+
+
 @pytest.mark.slow
 def test_full_size_skewed_activations_sampled(gpu):
     """The skewed MoE FC2 activations [32768, 2048] bf16 quantised in the
