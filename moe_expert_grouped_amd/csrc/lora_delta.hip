@@ -642,6 +642,7 @@ __global__ __launch_bounds__(64 * SHR_WAVES) void shrink_kernel(ShrinkArgs p) {
 // reads A_le from LDS instead of from the caches, which the per-tile shrink
 // does once per block.
 constexpr int SLE_KC = 128;          // activation K elements per wave stage
+constexpr int SLE_SD = 6;            // activation stages in flight per wavefront
 constexpr int SLE_AMAX = 16 * 2048;  // bf16 of A_le held in LDS: 16 * NB * I <= SLE_AMAX
 constexpr int SLE_AMAX_BIG = 16 * 4096;  // the one-workgroup-per-CU variant (128 KB of A_le)
 
@@ -723,23 +724,24 @@ __global__ __launch_bounds__(256, AMAX > SLE_AMAX ? 1 : 2) void shrink_le_kernel
       f32x4 acc[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // three register stages in flight: stage s + 3 is loaded while s feeds the MFMAs
-      u32x4 ra0[NLA], ra1[NLA], ra2[NLA];
-      auto gload = [&](u32x4 (&ra)[NLA], int s) {
+      // SLE_SD register stages in flight: stage s + SLE_SD is loaded while s
+      // feeds the MFMAs
+      u32x4 ra[SLE_SD][NLA];
+      auto gload = [&](u32x4 (&r)[NLA], int s) {
         if (s < nst) {
 #pragma unroll
           for (int jj = 0; jj < NLA; ++jj)  // activation rows are read once
-            ra[jj] = gld_nt<u32x4>(asrc[jj] + s * SLE_KC);
+            r[jj] = gld_nt<u32x4>(asrc[jj] + s * SLE_KC);
         }
       };
-      auto consume = [&](u32x4 (&ra)[NLA], int s) {
+      auto consume = [&](u32x4 (&r)[NLA], int s) {
 #pragma unroll
         for (int jj = 0; jj < NLA; ++jj) {
-          const int r = jj * RPI + lrow;
-          *reinterpret_cast<u32x4*>(st + r * SLE_KC + ((lch ^ (r % CPR)) << 3)) = ra[jj];
+          const int rw = jj * RPI + lrow;
+          *reinterpret_cast<u32x4*>(st + rw * SLE_KC + ((lch ^ (rw % CPR)) << 3)) = r[jj];
         }
         __builtin_amdgcn_wave_barrier();
-        gload(ra, s + 3);
+        gload(r, s + SLE_SD);
 #pragma unroll
         for (int s2 = 0; s2 < SLE_KC / 32; ++s2) {
           const int c = 4 * s2 + kq;
@@ -755,13 +757,12 @@ __global__ __launch_bounds__(256, AMAX > SLE_AMAX ? 1 : 2) void shrink_le_kernel
         }
         __builtin_amdgcn_wave_barrier();  // this stage's reads precede the next stage's writes
       };
-      gload(ra0, 0);
-      gload(ra1, 1);
-      gload(ra2, 2);
-      for (int s = 0; s < nst; s += 3) {
-        consume(ra0, s);
-        if (s + 1 < nst) consume(ra1, s + 1);
-        if (s + 2 < nst) consume(ra2, s + 2);
+#pragma unroll
+      for (int q = 0; q < SLE_SD; ++q) gload(ra[q], q);
+      for (int s = 0; s < nst; s += SLE_SD) {
+#pragma unroll
+        for (int q = 0; q < SLE_SD; ++q)
+          if (s + q < nst) consume(ra[q], s + q);
       }
       shrink_store<NB, F16>(acc, p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32,
                             p.blk_w + tb * 16, p.blk_f + tb * 16, p.rank);
