@@ -118,8 +118,9 @@ def test_element_rounding_sweep(gpu):
 @pytest.mark.slow
 def test_full_size_skewed_activations_sampled(gpu):
     """The skewed MoE FC2 activations [32768, 2048] bf16 quantised in the
-    launch the bench times; 24 sampled rows bitwise (codes and their scale
-    bytes), the rest checked to decode within the error bound."""
+    launch the bench times: 24 sampled rows (first, last and both sides of a
+    128-row tile edge among them) bitwise against the oracle, codes and their
+    scale bytes; two launches agree on every byte of both outputs."""
     x = synth.bf16_normal((32768, 2048), 1.0, synth.gen(3, gpu), gpu)
     gs = torch.tensor([448.0 * 6.0 / float(x.float().abs().max())], dtype=torch.float32,
                       device=gpu)
