@@ -8,10 +8,11 @@
 // that table -- empty experts own no tile and no row is padded in memory
 // (the device-walk backend's behaviour described on the same page).
 //
-// Two kernels, chosen from host sizes: grouped_mm_kernel (below) for groups
-// averaging fewer than 192 rows, grouped_mm_big_kernel (further down, with
-// its own notes) for larger ones; the big kernel also serves FC1, whose
-// epilogue applies the SwiGLU activation.
+// Three kernels, chosen from host sizes: grouped_mm_kernel (below) for groups
+// averaging fewer than 192 rows; for larger ones grouped_mm_dma_kernel when
+// n % 512 == 0 and grouped_mm_big_kernel otherwise (further down, each with
+// its own notes).  The big kernel also serves FC1, whose epilogue applies the
+// SwiGLU activation.
 //
 // grouped_mm_kernel structure
 //   * tile BM x BN, K step 64; WM x WN waves, each owning a (BM/WM) x (BN/WN)
@@ -668,6 +669,309 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// grouped_mm_dma_kernel: large groups, n % 512 == 0
+//
+// What bounds the big tiles is the CU's vector-memory path: every operand
+// byte of a tile is a request from the CU's L1 to L2, and the CU sustains
+// about 14 bytes of them per clock (the same rate that caps a plain streaming
+// read).  Per 64-wide K step a 256 x 256 tile loads 64 KB for 64 MFMA blocks
+// per wavefront, a 384 x 256 tile 80 KB for 96.  This kernel therefore cuts
+// each expert's rows into 384-row tiles, a last piece of 129..256 rows into a
+// 256-row tile and of at most 128 rows into a 128-row tile that is 512
+// columns wide (128 x 512 loads 80 KB per step for the work of 128 x 256 at
+// 48 KB, twice); all three load fewer bytes per MFMA than the 256 x 256 and
+// 128 x 256 tiles.
+//
+// Staging: the tile's a and b rows go straight from memory into LDS
+// (buffer_load ... lds: each instruction writes 1 KB, 8 rows of 128 bytes),
+// so no registers hold staged data -- the 384-row tile needs them for its
+// accumulators.  16-byte chunk c of LDS row R holds the row's chunk
+// c ^ gd_swz(R).  Two LDS stages of 80 KB: the loads of step kt+1 are issued at the
+// start of step kt and complete by its barrier (one step ahead is as fast as
+// two for these tiles).  Four wavefronts of 128 columns each (the 128 x 512
+// tile: 1 x 4) or 2 x 2 (the 384 and 256-row tiles: 192 or 128 rows each).
+// ---------------------------------------------------------------------------
+constexpr int GD_STAGE = 640 * 64;  // elements per LDS stage: 640 rows of 128 bytes
+constexpr int GD_WAVES = 8;         // two wavefronts per SIMD
+
+// Chunk swizzle of LDS row R: any 8 consecutive rows, and the even and the
+// odd rows of any 16, take 8 different values (a fragment read of 32 rows
+// spreads over all banks whether the LDS serves 8 or 16 lanes a cycle), and it
+// depends only on R % 32.
+__device__ __forceinline__ int gd_swz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+
+// an LDS address as the LDS-DMA builtin takes it
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ __forceinline__ lds_void_ptr lds_ptr(uint16_t* p) { return (lds_void_ptr)(p); }
+
+template <int WM, int WN, int FM, int FN, bool F16, typename OutT>
+__device__ __forceinline__ void gd_tile(const uint16_t* __restrict__ a,
+                                        const uint16_t* __restrict__ b, OutT* __restrict__ out,
+                                        uint16_t* smem, int e, int m0, int rows, int n0, int k,
+                                        int n) {
+  constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
+  constexpr int R = BM + BN;                 // LDS rows per stage
+  constexpr int NI = R / 64;                 // DMA instructions per wavefront per stage
+  constexpr int NIA = BM / 64;               // of which a rows
+  static_assert(WM * WN == GD_WAVES && R <= 640 && BM % 64 == 0, "tile");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int r = lane & 31, h = lane >> 5;
+  const int KT = k / GB_BK;
+  const uint32_t kbytes = static_cast<uint32_t>(k) * 2;
+
+  const __amdgpu_buffer_rsrc_t br =
+      buf_rsrc(b + (static_cast<long>(e) * n + n0) * k, static_cast<uint32_t>(BN) * kbytes);
+
+  // DMA instruction i of this wavefront fills LDS rows 8g .. 8g+7 with
+  // g = 8i + wave (i < NIA: a rows, else b rows 8g - BM ..).  Lane l takes row
+  // 8g + l/8 and its chunk (l%8) ^ gd_swz(8g + l/8) = (l%8) ^ (l/8) ^ (wave%4).
+  // Each a instruction has its own descriptor starting at its first row, whose
+  // range ends at the group's last row, so rows past the end read as zero (the
+  // range check covers the lane offset, which holds the row within the 8).
+  const int lr = lane >> 3, lc = lane & 7;
+  const uint32_t dvo = static_cast<uint32_t>(lr) * kbytes + ((lc ^ lr ^ (wave & 3)) << 4);
+  __amdgpu_buffer_rsrc_t ari[NIA];
+#pragma unroll
+  for (int i = 0; i < NIA; ++i) {
+    const int r0 = 8 * (8 * i + wave);
+    ari[i] = buf_rsrc(a + static_cast<long>(m0 + r0) * k,
+                      static_cast<uint32_t>(max(rows - r0, 0)) * kbytes);
+  }
+  auto dma = [&](uint16_t* st, int kt) {
+    const uint32_t so = static_cast<uint32_t>(min(kt, KT - 1)) * (GB_BK * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int g = 8 * i + wave;
+      uint16_t* dst = st + g * 512;  // 8 rows of 64 elements
+      if (i < NIA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ari[i], lds_ptr(dst), 16, dvo, so, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            br, lds_ptr(dst), 16, dvo, so + static_cast<uint32_t>(8 * g - BM) * kbytes, 0, 0);
+    }
+  };
+
+  // fragments: lane (r, h) reads 16-byte chunk 2s+h of row 32 B + r of each
+  // 32-row block B, at slot (2s+h) ^ gd_swz(r)
+  int fo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) fo[s] = r * 64 + (((2 * s + h) ^ gd_swz(r)) << 3);
+  struct Frag {
+    u32x4 a[FM], b[FN];
+  };
+  auto fload = [&](Frag& f, const uint16_t* st, int s) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int blk = wm * FM + i;
+      f.a[i] = *reinterpret_cast<const u32x4*>(st + blk * 32 * 64 + fo[s]);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int blk = BM / 32 + wn * FN + j;
+      f.b[j] = *reinterpret_cast<const u32x4*>(st + blk * 32 * 64 + fo[s]);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  // C[m][n] with m = output column (b row), n = output row (a row)
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<F16>(f.b[j], f.a[i], acc[i][j]);
+  };
+
+  uint16_t* const st0 = smem;
+  uint16_t* const st1 = smem + GD_STAGE;
+  dma(st0, 0);
+  __syncthreads();  // stage 0 in LDS; every wavefront is past the tile walk
+  auto kstep = [&](int kt, uint16_t* st, uint16_t* nx) {
+    dma(nx, kt + 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      Frag f;
+      fload(f, st, s);
+      mma(f);
+    }
+    // stage kt+1 has landed (each wavefront waits for its own loads) and every
+    // wavefront's reads of stage kt are done
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    kstep(kt, st0, st1);
+    kstep(kt + 1, st1, st0);
+  }
+  if (kt < KT) kstep(kt, st0, st1);
+
+  // acc[i][j][q]: tile row (wm FM + i) 32 + r, column (wn FN + j) 32 + 8 (q/4) + 4h + q%4
+  if (wm * 32 * FM >= rows) return;
+  const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(out + static_cast<long>(m0) * n,
+                                                static_cast<uint32_t>(rows) * n * sizeof(OutT));
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const uint32_t orow =
+        (static_cast<uint32_t>((wm * FM + i) * 32 + r) * n + n0 + wn * FN * 32 + 4 * h) *
+        sizeof(OutT);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                         acc[i][j][4 * g + 3]};
+        bstore_out4<OutT>(orsrc, orow + (j * 32 + 8 * g) * sizeof(OutT), v);
+      }
+    }
+  }
+}
+
+// Device-side walk of m_indptr by wavefront 0 for the three tile kinds: per
+// expert the clamped first row (s_row0[E] = end of the last expert), the
+// first 384-row tile (s_t3), 256-row tile (s_t2) and 128-row tile (s_t1).
+// An expert of m rows has q = m / 384 full tiles and r = m % 384 rows left:
+// r > 256 -> one more 384-row tile, 128 < r <= 256 -> a 256-row tile,
+// 0 < r <= 128 -> a 128-row tile.
+__device__ __forceinline__ void gd_counts(int m, int& c3, int& c2, int& c1) {
+  const int q = m / 384, r = m - 384 * q;
+  c3 = q + (r > 256);
+  c2 = (r > 128 && r <= 256);
+  c1 = (r > 0 && r <= 128);
+}
+__device__ __forceinline__ void gd_walk(const int32_t* __restrict__ m_indptr, int m_rows, int E,
+                                        int* s_t3, int* s_t2, int* s_t1, int* s_row0) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;
+  const int e0 = lane * per;
+  int n3 = 0, n2 = 0, n1 = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int s = min(max(m_indptr[e], 0), m_rows);
+      const int t = min(max(m_indptr[e + 1], s), m_rows);
+      s_row0[e] = s;
+      int c3, c2, c1;
+      gd_counts(t - s, c3, c2, c1);
+      n3 += c3;
+      n2 += c2;
+      n1 += c1;
+    }
+  }
+  int i3 = n3, i2 = n2, i1 = n1;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v3 = __shfl_up(i3, off, 64), v2 = __shfl_up(i2, off, 64),
+              v1 = __shfl_up(i1, off, 64);
+    if (lane >= off) {
+      i3 += v3;
+      i2 += v2;
+      i1 += v1;
+    }
+  }
+  int r3 = i3 - n3, r2 = i2 - n2, r1 = i1 - n1;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      s_t3[e] = r3;
+      s_t2[e] = r2;
+      s_t1[e] = r1;
+      const int s = s_row0[e];
+      const int t = min(max(m_indptr[e + 1], s), m_rows);
+      int c3, c2, c1;
+      gd_counts(t - s, c3, c2, c1);
+      r3 += c3;
+      r2 += c2;
+      r1 += c1;
+    }
+  }
+  if (lane == 63) {
+    s_t3[E] = i3;
+    s_t2[E] = i2;
+    s_t1[E] = i1;
+    s_row0[E] = min(max(m_indptr[E], 0), m_rows);
+  }
+}
+
+template <bool F16, typename OutT>
+__global__ __launch_bounds__(64 * GD_WAVES, 1) void grouped_mm_dma_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+    const int32_t* __restrict__ m_indptr, OutT* __restrict__ out, int m_rows, int k, int n,
+    int E) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * GD_STAGE];
+  // the walk's tables live in stage 1, which the first K step overwrites only
+  // after the barrier that follows stage 0's loads
+  int* const s_t3 = reinterpret_cast<int*>(smem + GD_STAGE);
+  int* const s_t2 = s_t3 + (GM_MAX_EXPERTS + 1);
+  int* const s_t1 = s_t2 + (GM_MAX_EXPERTS + 1);
+  int* const s_row0 = s_t1 + (GM_MAX_EXPERTS + 1);
+
+  if ((threadIdx.x >> 6) == 0) gd_walk(m_indptr, m_rows, E, s_t3, s_t2, s_t1, s_row0);
+  __syncthreads();
+
+  const int nt = n / 256, nt1 = n / 512;
+  const int c3 = s_t3[E], c2 = s_t2[E], c1 = s_t1[E];
+  const long tot3 = static_cast<long>(c3) * nt, tot2 = static_cast<long>(c2) * nt,
+             tot1 = static_cast<long>(c1) * nt1;
+  // The grid is an upper bound on the tiles; the dispatcher deals workgroup
+  // ids to the 8 XCDs in turn.  An XCD's first run3 workgroups take its run
+  // of the 384-row tiles, the next run2 its 256-row tiles, then run1 its
+  // 128-row tiles.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const long run3 = (tot3 + 7) / 8, run2 = (tot2 + 7) / 8, run1 = (tot1 + 7) / 8;
+  int kind, e, m0, rows, n0;
+  {
+    int mt, ni;
+    long L;
+    if (slot < run3) {
+      L = xcd * run3 + slot;
+      if (L >= tot3) return;
+      gb_order(L, c3, nt, mt, ni);
+      e = gb_owner(s_t3, E, mt);
+      m0 = s_row0[e] + (mt - s_t3[e]) * 384;
+      kind = 3;
+      n0 = ni * 256;
+    } else if (slot < run3 + run2) {
+      L = xcd * run2 + (slot - run3);
+      if (L >= tot2) return;
+      gb_order(L, c2, nt, mt, ni);
+      e = gb_owner(s_t2, E, mt);
+      m0 = s_row0[e] + (s_t3[e + 1] - s_t3[e]) * 384;
+      kind = 2;
+      n0 = ni * 256;
+    } else {
+      L = xcd * run1 + (slot - run3 - run2);
+      if (slot - run3 - run2 >= run1 || L >= tot1) return;
+      gb_order(L, c1, nt1, mt, ni);
+      e = gb_owner(s_t1, E, mt);
+      m0 = s_row0[e] + (s_t3[e + 1] - s_t3[e]) * 384;
+      kind = 1;
+      n0 = ni * 512;
+    }
+    const int end = max(s_row0[e + 1], s_row0[e]);
+    rows = min(end - m0, kind == 3 ? 384 : kind == 2 ? 256 : 128);
+  }
+  kind = __builtin_amdgcn_readfirstlane(kind);
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  n0 = __builtin_amdgcn_readfirstlane(n0);
+  if (kind == 3)
+    gd_tile<4, 2, 3, 4, F16, OutT>(a, b, out, smem, e, m0, rows, n0, k, n);
+  else if (kind == 2)
+    gd_tile<2, 4, 4, 2, F16, OutT>(a, b, out, smem, e, m0, rows, n0, k, n);
+  else
+    gd_tile<1, 8, 4, 2, F16, OutT>(a, b, out, smem, e, m0, rows, n0, k, n);
+}
+
 template <bool F16, bool GLU, typename OutT>
 __global__ __launch_bounds__(256, 1) void grouped_mm_big_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
@@ -764,6 +1068,23 @@ mi_status launch_grouped_big(const void* a, int64_t m_rows, int64_t k, const voi
 }
 
 template <bool F16, typename OutT>
+mi_status launch_grouped_dma(const void* a, int64_t m_rows, int64_t k, const void* b,
+                             int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
+                             hipStream_t stream) {
+  // upper bound on the tiles of the three kinds: every tile covers at least
+  // 128 rows of one expert or is its one partial tile, and at least 256
+  // columns' worth of n-panels
+  const long ub_tiles = ((m_rows + 127) / 128 + batch) * (n / 256);
+  const long G = ((ub_tiles + 7) / 8 + 4) * 8;
+  MI_REQUIRE(G < (1L << 31), "grouped_mm_bf16: problem too large");
+  hipLaunchKernelGGL((grouped_mm_dma_kernel<F16, OutT>), dim3(G), dim3(64 * GD_WAVES), 0, stream,
+                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), m_indptr,
+                     static_cast<OutT*>(out), static_cast<int>(m_rows), static_cast<int>(k),
+                     static_cast<int>(n), static_cast<int>(batch));
+  return launch_status("grouped_mm_bf16");
+}
+
+template <bool F16, typename OutT>
 mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void* b,
                            int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
                            hipStream_t stream) {
@@ -771,6 +1092,9 @@ mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void*
   // large average groups take 256x256 tiles; smaller groups stream b from HBM
   // and take 64x64 tiles, two workgroups per CU, with 4 K steps in flight.
   const int64_t avg = m_rows / batch;
+  if (avg >= 192 && n % 512 == 0 && static_cast<uint64_t>(k) * 2 * 512 < (1ULL << 32) &&
+      static_cast<uint64_t>(n) * 384 * sizeof(OutT) < (1ULL << 32))
+    return launch_grouped_dma<F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream);
   if (avg >= 192)
     return launch_grouped_big<F16, false, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
                                                GbGlu{});

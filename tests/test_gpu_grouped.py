@@ -34,9 +34,10 @@ def test_tiny_moe_fc2(gpu):
     ((0, 1, 17, 128, 0, 255), 256, 128),          # small groups: 64x64 tiles
     ((100, 0, 150, 177, 0, 229), 512, 192),       # medium: 64x64 tiles, several per group
     ((300, 0, 513, 1, 256, 0, 390), 256, 256),    # large: 256x256 tiles, ragged tails
-    # large, odd K-step count: last pieces of 128 / 129 / 255 / 1 / 0 / 128 / 88 / 232 rows
-    # (128-row tiles for pieces up to 128 rows, 256-row tiles above)
-    ((128, 129, 255, 257, 0, 384, 600, 1000), 512, 192),
+    # large, n not a multiple of 512 (256x256 tiles), odd K-step count: last
+    # pieces of 128 / 129 / 255 / 1 / 0 / 128 / 88 / 232 rows (128-row tiles
+    # for pieces up to 128 rows, 256-row tiles above)
+    ((128, 129, 255, 257, 0, 384, 600, 1000), 768, 192),
 ])
 def test_integer_probe_bitwise(gpu, counts, n, k):
     case = synth.grouped_int_probe(counts=counts, n=n, k=k)
@@ -47,6 +48,56 @@ def test_integer_probe_bitwise(gpu, counts, n, k):
     assert np.array_equal(got, want)
     out32 = _run(case, gpu, torch.float32)
     assert np.array_equal(to_f64(out32)[written], ref[written])
+
+
+@pytest.mark.parametrize("counts,n,k", [
+    # large groups with n % 512 == 0 (384-row tiles; a last piece of 129..256
+    # rows as a 256-row tile, of at most 128 rows as a 128 x 512 tile): pieces
+    # of 1, 127, 128, 129, 255, 256, 257, 383 rows; one K step only, an even
+    # and an odd step count
+    ((384, 385, 0, 640, 641, 767, 1, 128, 129, 256, 257, 383), 1024, 64),
+    ((500, 1, 0, 1151), 512, 128),
+    ((257, 0, 700, 64, 129, 1000), 1536, 320),
+])
+def test_integer_probe_bitwise_large_tiles(gpu, counts, n, k):
+    """Every output type, bf16 and fp16 operands, against the exact sums."""
+    from oracle.formats import f64_to_f16_bits
+    assert sum(counts) >= 192 * len(counts) and n % 512 == 0
+    case = synth.grouped_int_probe(seed=120 + k, counts=counts, n=n, k=k)
+    ref, written = _oracle(case)
+    assert np.array_equal(bits16(_run(case, gpu))[written], f64_to_bf16_bits(ref[written]))
+    assert np.array_equal(to_f64(_run(case, gpu, torch.float32))[written], ref[written])
+    a16, b16 = case.a.float().half(), case.b.float().half()
+    mi = case.m_indptr
+    ref16, w16 = grouped_mm(bits16(a16), bits16(b16), mi.numpy(), "f16")
+    out = grouped_mm_bf16(a16.to(gpu), b16.to(gpu), mi.to(gpu), out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(out)[w16], f64_to_f16_bits(ref16[w16]))
+
+
+def test_large_tiles_rows_outside_groups_untouched_and_many_experts(gpu):
+    """Large groups with n % 512 == 0: leading and trailing rows outside every
+    group keep their contents (the last group's tile reads past its rows);
+    300 experts, most empty, a few of one row, in one call."""
+    base = synth.grouped_int_probe(seed=21, counts=(400, 0, 433, 1), n=512, k=128)
+    cum = base.a.shape[0]
+    a = synth.bf16_ints((5 + cum + 9, 128), -3, 3, synth.gen(22))
+    case = synth.GroupedCase("offset large", a, base.b, base.m_indptr + 5)
+    sentinel = torch.full((a.shape[0], 512), -7.0, dtype=torch.bfloat16, device=gpu)
+    out = _run(case, gpu, out=sentinel)
+    ref, written = _oracle(case)
+    assert not written[:5].any() and not written[-9:].any() and written[5:5 + cum].all()
+    assert (to_f64(out)[~written] == -7.0).all()
+    assert np.array_equal(bits16(out)[written], f64_to_bf16_bits(ref[written]))
+    rng = np.random.default_rng(23)
+    counts = np.zeros(300, dtype=np.int64)
+    live = rng.choice(300, 80, replace=False)
+    counts[live] = rng.integers(300, 1700, 80)
+    counts[live[:4]] = 1
+    assert counts.sum() >= 192 * 300
+    many = synth.grouped_int_probe(seed=24, counts=tuple(counts.tolist()), n=512, k=64)
+    ref, written = _oracle(many)
+    assert np.array_equal(bits16(_run(many, gpu))[written], f64_to_bf16_bits(ref[written]))
 
 
 def test_rows_outside_groups_untouched(gpu):
