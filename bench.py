@@ -52,9 +52,9 @@ CSRC = os.path.join(ROOT, "moe_expert_grouped_amd", "csrc")
 # summary is used only while the kernel's source file is unchanged.
 TRAFFIC = {
     "grouped_gemm_c3": dict(
-        kernel="grouped_mm_big_kernel", src="grouped_mm.hip",
-        file="profiles/grouped_mm_big_kernel_e128_zipf_k2048_n7168_traffic.txt",
-        what="grouped_mm_big_kernel, skewed MoE FC2 (E=128, cum_m=32768 Zipf 1.1, k=2048, "
+        kernel="grouped_mm_dma_kernel", src="grouped_mm.hip",
+        file="profiles/grouped_mm_dma_kernel_e128_zipf_k2048_n7168_traffic.txt",
+        what="grouped_mm_dma_kernel, skewed MoE FC2 (E=128, cum_m=32768 Zipf 1.1, k=2048, "
              "n=7168, bf16 out), cold"),
     "nvfp4_raw": dict(
         kernel="nvfp4_lora_kernel", src="nvfp4_lora.hip",
@@ -441,8 +441,8 @@ def main():
     bounds = {"grouped_gemm_c3": "hbm", "grouped_gemm_c3_warm": "hbm", "grouped_gemm_c2": "hbm",
               "grouped_gemm_c2_warm": "hbm", "lora_delta": "hbm", "lora_delta_warm": "hbm",
               "fold": "hbm", "nvfp4_raw": "mfma", "nvfp4_prepared": "mfma", "copy_probe": "hbm"}
-    kernels = {"grouped_gemm_c3": "grouped_mm_big_kernel", "grouped_gemm_c3_warm":
-               "grouped_mm_big_kernel", "grouped_gemm_c2": "grouped_mm_kernel",
+    kernels = {"grouped_gemm_c3": "grouped_mm_dma_kernel", "grouped_gemm_c3_warm":
+               "grouped_mm_dma_kernel", "grouped_gemm_c2": "grouped_mm_kernel",
                "grouped_gemm_c2_warm": "grouped_mm_kernel", "lora_delta":
                "plan + list + shrink_le + expand kernels", "lora_delta_warm":
                "plan + list + shrink_le + expand kernels", "fold": "fold_kernel",
