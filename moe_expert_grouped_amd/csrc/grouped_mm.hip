@@ -675,8 +675,8 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
 // What bounds the big tiles is the CU's vector-memory path: every operand
 // byte of a tile is a request from the CU's L1 to L2, and the CU sustains
 // about 14 bytes of them per clock (the same rate that caps a plain streaming
-// read).  Per 64-wide K step a 256 x 256 tile loads 64 KB for 64 MFMA blocks
-// per wavefront, a 384 x 256 tile 80 KB for 96.  This kernel therefore cuts
+// read).  Per 64-wide K step a 256 x 256 tile loads 64 KB for 256 MFMAs
+// (32x32x16), a 384 x 256 tile 80 KB for 384.  This kernel therefore cuts
 // each expert's rows into 384-row tiles, a last piece of 129..256 rows into a
 // 256-row tile and of at most 128 rows into a 128-row tile that is 512
 // columns wide (128 x 512 loads 80 KB per step for the work of 128 x 256 at
@@ -687,10 +687,13 @@ __device__ __forceinline__ void gb_tile(const uint16_t* __restrict__ a,
 // (buffer_load ... lds: each instruction writes 1 KB, 8 rows of 128 bytes),
 // so no registers hold staged data -- the 384-row tile needs them for its
 // accumulators.  16-byte chunk c of LDS row R holds the row's chunk
-// c ^ gd_swz(R).  Two LDS stages of 80 KB: the loads of step kt+1 are issued at the
-// start of step kt and complete by its barrier (one step ahead is as fast as
-// two for these tiles).  Four wavefronts of 128 columns each (the 128 x 512
-// tile: 1 x 4) or 2 x 2 (the 384 and 256-row tiles: 192 or 128 rows each).
+// c ^ gd_swz(R).  Two LDS stages of 80 KB: the loads of step kt+1 are issued
+// at the start of step kt and complete by its barrier (one step ahead is as
+// fast as two for these tiles).  Eight wavefronts, two per SIMD: 4 x 2 of
+// 96 x 128 (384 x 256; four wavefronts of 192 x 128 would need 384
+// accumulator registers a lane, which the compiler spills), 2 x 4 of
+// 128 x 64 (256 x 256), 1 x 8 of 128 x 64 (128 x 512).  Fragments are
+// single-buffered; the SIMD's second wavefront covers the LDS latency.
 // ---------------------------------------------------------------------------
 constexpr int GD_STAGE = 640 * 64;  // elements per LDS stage: 640 rows of 128 bytes
 constexpr int GD_WAVES = 8;         // two wavefronts per SIMD
