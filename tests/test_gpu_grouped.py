@@ -67,6 +67,8 @@ def test_integer_probe_bitwise_large_tiles(gpu, counts, n, k):
     ref, written = _oracle(case)
     assert np.array_equal(bits16(_run(case, gpu))[written], f64_to_bf16_bits(ref[written]))
     assert np.array_equal(to_f64(_run(case, gpu, torch.float32))[written], ref[written])
+    assert np.array_equal(bits16(_run(case, gpu, torch.float16))[written],
+                          f64_to_f16_bits(ref[written]))
     a16, b16 = case.a.float().half(), case.b.float().half()
     mi = case.m_indptr
     ref16, w16 = grouped_mm(bits16(a16), bits16(b16), mi.numpy(), "f16")
