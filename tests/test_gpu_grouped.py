@@ -156,9 +156,14 @@ def test_zipf_full_size_sampled(gpu):
     for e in range(len(mi) - 1):
         if mi[e + 1] > mi[e]:
             rows.update({int(mi[e]), int(mi[e + 1]) - 1})
+            # both sides of every 384-row tile edge inside the expert
+            for r0 in range(int(mi[e]) + 384, int(mi[e + 1]), 384):
+                rows.update({r0 - 1, r0})
     rows.update(rng.integers(0, int(mi[-1]), 32).tolist())
     rows = sorted(rows)
-    cols = np.sort(rng.choice(7168, 96, replace=False))
+    # both sides of 256- and 512-column panel edges, plus random columns
+    edges = {0, 255, 256, 511, 512, 3583, 3584, 7167}
+    cols = np.sort(np.array(sorted(edges | set(rng.choice(7168, 96, replace=False).tolist()))))
     a_rows = bits16(case.a[rows])
     colt = torch.from_numpy(cols).to(gpu)
     ref = grouped_mm_rows(a_rows, lambda e, c: bits16(case.b[e].index_select(0, colt)), mi, rows,
