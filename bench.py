@@ -442,8 +442,8 @@ def main():
               "grouped_gemm_c2_warm": "hbm", "lora_delta": "hbm", "lora_delta_warm": "hbm",
               "fold": "hbm", "nvfp4_raw": "mfma", "nvfp4_prepared": "mfma", "copy_probe": "hbm"}
     kernels = {"grouped_gemm_c3": "grouped_mm_dma_kernel", "grouped_gemm_c3_warm":
-               "grouped_mm_dma_kernel", "grouped_gemm_c2": "grouped_mm_kernel",
-               "grouped_gemm_c2_warm": "grouped_mm_kernel", "lora_delta":
+               "grouped_mm_dma_kernel", "grouped_gemm_c2": "grouped_mm_dma64_kernel",
+               "grouped_gemm_c2_warm": "grouped_mm_dma64_kernel", "lora_delta":
                "plan + list + shrink_le + expand kernels", "lora_delta_warm":
                "plan + list + shrink_le + expand kernels", "fold": "fold_kernel",
                "nvfp4_raw": "nvfp4_lora_kernel", "nvfp4_prepared": "nvfp4_lora_kernel",

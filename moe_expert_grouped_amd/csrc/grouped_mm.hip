@@ -8,11 +8,12 @@
 // that table -- empty experts own no tile and no row is padded in memory
 // (the device-walk backend's behaviour described on the same page).
 //
-// Three kernels, chosen from host sizes: grouped_mm_kernel (below) for groups
-// averaging fewer than 192 rows; for larger ones grouped_mm_dma_kernel when
-// n % 512 == 0 and grouped_mm_big_kernel otherwise (further down, each with
-// its own notes).  The big kernel also serves FC1, whose epilogue applies the
-// SwiGLU activation.
+// Four kernels, chosen from host sizes: for groups averaging fewer than 192
+// rows grouped_mm_dma64_kernel (grouped_mm_kernel, below, where k is beyond
+// the 64x128 kernel's descriptor range); for larger ones grouped_mm_dma_kernel
+// when n % 512 == 0 and grouped_mm_big_kernel otherwise (further down, each
+// with its own notes).  The big kernel also serves FC1, whose epilogue
+// applies the SwiGLU activation.
 //
 // grouped_mm_kernel structure
 //   * tile BM x BN, K step 64; WM x WN waves, each owning a (BM/WM) x (BN/WN)
@@ -975,6 +976,191 @@ __global__ __launch_bounds__(64 * GD_WAVES, 1) void grouped_mm_dma_kernel(
     gd_tile<1, 8, 4, 2, F16, OutT>(a, b, out, smem, e, m0, rows, n0, k, n);
 }
 
+// ---------------------------------------------------------------------------
+// grouped_mm_dma64_kernel: small groups (average < 192 rows): 64 x 128 tiles,
+// one per workgroup.  These tiles stream b from memory and are bound by the
+// same per-CU L1 -> L2 request rate as the large ones: against 64 x 64 tiles
+// they request a quarter fewer operand bytes (a is read once per 128-wide
+// n-panel instead of per 64-wide one), with as many tiles as there are CUs on
+// the uniform E = 8 x 128-row workload.  a and b rows go straight into LDS
+// (the staging of the large-group kernel); four LDS stages of 24 KB, each its
+// own array, keep three K steps of loads in flight, which cold data from
+// memory needs (one step ahead was measured slower).  8 wavefronts of 32 x 32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void gd64_walk(const int32_t* __restrict__ m_indptr, int m_rows, int E,
+                                          int* s_t0, int* s_row0) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;
+  const int e0 = lane * per;
+  int c = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int s = min(max(m_indptr[e], 0), m_rows);
+      const int t = min(max(m_indptr[e + 1], s), m_rows);
+      s_row0[e] = s;
+      c += (t - s + 63) / 64;
+    }
+  }
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  int run = incl - c;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      s_t0[e] = run;
+      const int s = s_row0[e];
+      const int t = min(max(m_indptr[e + 1], s), m_rows);
+      run += (t - s + 63) / 64;
+    }
+  }
+  if (lane == 63) {
+    s_t0[E] = incl;
+    s_row0[E] = min(max(m_indptr[E], 0), m_rows);
+  }
+}
+
+
+// wait until at most N of this wavefront's loads are outstanding and its LDS
+// reads have returned, then barrier
+template <int N>
+__device__ __forceinline__ void gd_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));  // vmcnt(N) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+constexpr int GD4_STAGE = 192 * 64;  // 64 + 128 rows of 128 bytes
+
+// 64 x 128 tile, 8 wavefronts of 32 x 32, four LDS stages (each its own
+// array): the loads of step kt+3 are issued at the start of step kt and
+// waited for at the barrier that ends step kt+2 (vmcnt leaves the two later
+// stages in flight); the fragment reads of a stage need no load wait.  The
+// DMA mapping, swizzle and zero rows past the group are those of gd_tile.
+template <bool F16, typename OutT>
+__device__ __forceinline__ void gd4_tile(const uint16_t* __restrict__ a,
+                                         const uint16_t* __restrict__ b, OutT* __restrict__ out,
+                                         uint16_t* s0, uint16_t* s1, uint16_t* s2, uint16_t* s3,
+                                         int e, int m0, int rows, int n0, int k, int n) {
+  constexpr int WM = 2, WN = 4, BM = 64, BN = 128, R = BM + BN, NI = R / 64, NIA = BM / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int r = lane & 31, h = lane >> 5;
+  const int KT = k / GB_BK;
+  const uint32_t kbytes = static_cast<uint32_t>(k) * 2;
+  const __amdgpu_buffer_rsrc_t br =
+      buf_rsrc(b + (static_cast<long>(e) * n + n0) * k, static_cast<uint32_t>(BN) * kbytes);
+  const int lr = lane >> 3, lc = lane & 7;
+  const uint32_t dvo = static_cast<uint32_t>(lr) * kbytes + ((lc ^ lr ^ (wave & 3)) << 4);
+  __amdgpu_buffer_rsrc_t ari[NIA];
+#pragma unroll
+  for (int i = 0; i < NIA; ++i) {
+    const int r0 = 8 * (8 * i + wave);
+    ari[i] = buf_rsrc(a + static_cast<long>(m0 + r0) * k,
+                      static_cast<uint32_t>(max(rows - r0, 0)) * kbytes);
+  }
+  auto dma = [&](uint16_t* st, int kt) {
+    const uint32_t so = static_cast<uint32_t>(min(kt, KT - 1)) * (GB_BK * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int g = 8 * i + wave;
+      uint16_t* dst = st + g * 512;
+      if (i < NIA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ari[i], lds_ptr(dst), 16, dvo, so, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            br, lds_ptr(dst), 16, dvo, so + static_cast<uint32_t>(8 * g - BM) * kbytes, 0, 0);
+    }
+  };
+  int fo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) fo[s] = r * 64 + (((2 * s + h) ^ gd_swz(r)) << 3);
+  f32x16 acc;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+  auto kstep = [&](int kt, const uint16_t* cur, uint16_t* nx3) {
+    dma(nx3, kt + 3);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 fa = *reinterpret_cast<const u32x4*>(cur + wm * 32 * 64 + fo[s]);
+      const u32x4 fb = *reinterpret_cast<const u32x4*>(cur + (BM / 32 + wn) * 32 * 64 + fo[s]);
+      acc = mfma32<F16>(fb, fa, acc);
+    }
+    gd_wait_barrier<2 * NI>();
+  };
+  dma(s0, 0);
+  dma(s1, 1);
+  dma(s2, 2);
+  gd_wait_barrier<2 * NI>();
+  int kt = 0;
+  for (; kt + 4 <= KT; kt += 4) {
+    kstep(kt, s0, s3);
+    kstep(kt + 1, s1, s0);
+    kstep(kt + 2, s2, s1);
+    kstep(kt + 3, s3, s2);
+  }
+  if (kt < KT) kstep(kt++, s0, s3);
+  if (kt < KT) kstep(kt++, s1, s0);
+  if (kt < KT) kstep(kt++, s2, s1);
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  if (wm * 32 >= rows) return;
+  const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(out + static_cast<long>(m0) * n,
+                                                static_cast<uint32_t>(rows) * n * sizeof(OutT));
+  const uint32_t orow = (static_cast<uint32_t>(wm * 32 + r) * n + n0 + wn * 32 + 4 * h) * sizeof(OutT);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 v = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+    bstore_out4<OutT>(orsrc, orow + 8 * g * sizeof(OutT), v);
+  }
+}
+
+template <bool F16, typename OutT>
+__global__ __launch_bounds__(64 * GD_WAVES, 1) void grouped_mm_dma64_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+    const int32_t* __restrict__ m_indptr, OutT* __restrict__ out, int m_rows, int k, int n,
+    int E) {
+  __shared__ __attribute__((aligned(16))) uint16_t s0[GD4_STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s1[GD4_STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s2[GD4_STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t s3[GD4_STAGE];
+  int* const s_t0 = reinterpret_cast<int*>(s3);
+  int* const s_row0 = s_t0 + (GM_MAX_EXPERTS + 1);
+  if ((threadIdx.x >> 6) == 0) gd64_walk(m_indptr, m_rows, E, s_t0, s_row0);
+  __syncthreads();
+  const int nt = n / 128;
+  const int count = s_t0[E];
+  const long total = static_cast<long>(count) * nt;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const long run = (total + 7) / 8;
+  const long L = xcd * run + slot;
+  if (slot >= run || L >= total) return;
+  int mt, ni;
+  gb_order(L, count, nt, mt, ni);
+  const int e = __builtin_amdgcn_readfirstlane(gb_owner(s_t0, E, mt));
+  const int m0 = __builtin_amdgcn_readfirstlane(s_row0[e] + (mt - s_t0[e]) * 64);
+  const int end = max(s_row0[e + 1], s_row0[e]);
+  const int rows = __builtin_amdgcn_readfirstlane(min(end - m0, 64));
+  gd4_tile<F16, OutT>(a, b, out, s0, s1, s2, s3, e, m0, rows, ni * 128, k, n);
+}
+
+template <bool F16, typename OutT>
+mi_status launch_grouped_dma64(const void* a, int64_t m_rows, int64_t k, const void* b,
+                               int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
+                               hipStream_t stream) {
+  const long ub_tiles = ((m_rows + 63) / 64 + batch) * (n / 128);
+  const long G = ((ub_tiles + 7) / 8 + 2) * 8;
+  MI_REQUIRE(G < (1L << 31), "grouped_mm_bf16: problem too large");
+  hipLaunchKernelGGL((grouped_mm_dma64_kernel<F16, OutT>), dim3(G), dim3(64 * GD_WAVES), 0,
+                     stream, static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
+                     m_indptr, static_cast<OutT*>(out), static_cast<int>(m_rows),
+                     static_cast<int>(k), static_cast<int>(n), static_cast<int>(batch));
+  return launch_status("grouped_mm_bf16");
+}
+
 template <bool F16, bool GLU, typename OutT>
 __global__ __launch_bounds__(256, 1) void grouped_mm_big_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
@@ -1092,8 +1278,10 @@ mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void*
                            int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
                            hipStream_t stream) {
   // Tile shape from host-known sizes only (the counts live on the device):
-  // large average groups take 256x256 tiles; smaller groups stream b from HBM
-  // and take 64x64 tiles, two workgroups per CU, with 4 K steps in flight.
+  // large average groups take 384x256 / 256x256 / 128x512 tiles (n % 512 ==
+  // 0) or 256x256 tiles; smaller groups stream b from HBM and take 64x128
+  // tiles (64x64 ones, two workgroups per CU, where k is too long for the
+  // 128-row b descriptor).
   const int64_t avg = m_rows / batch;
   if (avg >= 192 && n % 512 == 0 && static_cast<uint64_t>(k) * 2 * 512 < (1ULL << 32) &&
       static_cast<uint64_t>(n) * 384 * sizeof(OutT) < (1ULL << 32))
@@ -1101,6 +1289,8 @@ mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void*
   if (avg >= 192)
     return launch_grouped_big<F16, false, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
                                                GbGlu{});
+  if (static_cast<uint64_t>(k) * 2 * 128 < (1ULL << 32))  // n % 256 == 0 already
+    return launch_grouped_dma64<F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream);
   return launch_grouped<64, 64, 64, 2, 2, 4, F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream, 2);
 }
 
