@@ -56,6 +56,11 @@ TRAFFIC = {
         file="profiles/grouped_mm_dma_kernel_e128_zipf_k2048_n7168_traffic.txt",
         what="grouped_mm_dma_kernel, skewed MoE FC2 (E=128, cum_m=32768 Zipf 1.1, k=2048, "
              "n=7168, bf16 out), cold"),
+    "grouped_gemm_c2": dict(
+        kernel="grouped_mm_dma64_kernel", src="grouped_mm.hip",
+        file="profiles/grouped_mm_dma64_kernel_e8_m128_k4096_n2048_traffic.txt",
+        what="grouped_mm_dma64_kernel, uniform grouped GEMM (E=8 x 128 rows, k=4096, "
+             "n=2048, bf16 out), cold"),
     "nvfp4_raw": dict(
         kernel="nvfp4_lora_kernel", src="nvfp4_lora.hip",
         file="profiles/nvfp4_lora_kernel_m4096_n8192_k8192_traffic.txt",
@@ -228,7 +233,13 @@ def pmc_table(out_md, fetch_dir, write_dir):
     for r in fr:
         if "mi::" in r["Kernel_Name"] and _short(r["Kernel_Name"]) not in names:
             names.append(_short(r["Kernel_Name"]))
-    with open(out_md, "a") as fh:
+    # keep the hand-written head of OUT_MD, replace any table a previous run wrote
+    marker = "Counters are KiB per dispatch,"
+    head = open(out_md).read() if os.path.exists(out_md) else ""
+    if marker in head:
+        head = head[:head.index(marker)].rstrip("\n") + "\n"
+    with open(out_md, "w") as fh:
+        fh.write(head)
         fh.write(f"\nCounters are KiB per dispatch, scaled by the factors that map the same "
                  f"counters on the copy probe (512 MiB read + 512 MiB written) to its size: "
                  f"fetch {f_fac:.4f}, write {w_fac:.4f}.  They count what the L2 fetches from "
