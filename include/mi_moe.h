@@ -88,7 +88,9 @@ MI_API int mi_abi_version(void);
  *   out       [m_rows, n] of out_dtype (MI_BF16, MI_F16 or MI_F32); only rows
  *             [m_indptr[0], m_indptr[batch]) are written, the rest untouched
  * Requirements: m_rows >= 0, batch >= 1, n % 256 == 0, k % 64 == 0 (the
- * device-walk backend's shape rule on the page), k >= 64.
+ * device-walk backend's shape rule on the page), k >= 64.  k >= 4194304 (2^22)
+ * returns MI_EUNSUPPORTED: the kernels address a 512-row panel of b through
+ * one 32-bit buffer range.
  */
 MI_API mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k,
                              mi_dtype ab_dtype, const void* b, int64_t batch,

@@ -52,6 +52,12 @@ def test_grouped_mm_validation():
     msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, _lib.MI_F32, FAKE, 2, 256, FAKE, FAKE,
                                     _lib.MI_BF16, NULL))
     assert "bf16 or fp16" in msg
+    # k past the buffer-descriptor range of a 512-row b panel is valid but unsupported
+    st = L.mi_grouped_mm_bf16(FAKE, 64, 1 << 22, _lib.MI_BF16, FAKE, 2, 256, FAKE, FAKE,
+                              _lib.MI_BF16, NULL)
+    assert st == _lib.MI_EUNSUPPORTED
+    with pytest.raises(NotImplementedError, match="k < 4194304"):
+        _lib.check(st)
     # an empty a is a no-op that returns before touching the device
     assert L.mi_grouped_mm_bf16(NULL, 0, 64, _lib.MI_BF16, FAKE, 2, 256, FAKE, NULL, _lib.MI_BF16, NULL) == 0
 
