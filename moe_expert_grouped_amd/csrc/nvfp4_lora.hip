@@ -122,7 +122,9 @@ struct NvOps {
 };
 
 // The K loop of one wavefront (NKC stages of 128, NKC even): acc = dequant(A
-// rows) x dequant(B rows)^T in fp32.
+// rows) x dequant(B rows)^T in fp32.  B is the MFMA's first operand, so
+// acc[i][j][q] is A row 32 i + lane % 32 and B row 32 j + 8 (q / 4) +
+// 4 (lane / 32) + q % 4: four consecutive output columns per lane and q / 4.
 __device__ __forceinline__ void nv_kloop(f32x16 (&acc)[4][4], const NvOps& op, int NKC) {
   constexpr int FM = 4, FN = 4;
 #pragma unroll
@@ -175,7 +177,7 @@ __device__ __forceinline__ void nv_kloop(f32x16 (&acc)[4][4], const NvOps& op, i
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, fa[i]), __builtin_bit_cast(f16x8, fb[j]), acc[i][j], 0,
+                __builtin_bit_cast(f16x8, fb[j]), __builtin_bit_cast(f16x8, fa[i]), acc[i][j], 0,
                 0, 0);
       }
     }
@@ -272,18 +274,32 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
     lb = p.b_folded;
   }
   const int kl = lane >> 5;  // which 8-rank half of a 16-rank step this lane feeds
+  // 4 consecutive bf16 columns per 8-byte store where the rows allow it
+  const bool vec = (p.n & 3) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 7) == 0;
+  const bool has_bias = p.bias != nullptr;
+  const bool raw_lora = lora && p.mode == 1;
 
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int rbase = m0 + wm * WTM + i * 32;
+  for (int j = 0; j < FN; ++j) {
+    const int cbase = n0 + wn * WTN + j * 32;
+    // the lane's columns cbase + 8 g + 4 kl + c: bias values (zero past the end)
+    float bv[4][4];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int cbase = n0 + wn * WTN + j * 32;
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int col = cbase + 8 * g + 4 * kl + c;
+        bv[g][c] = (has_bias && col < p.n) ? bf16_bits_to_f32(p.bias[col]) : 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rbase = m0 + wm * WTM + i * 32;
       f32x16 accl;
 #pragma unroll
       for (int q = 0; q < 16; ++q) accl[q] = 0.f;
       if (lora) {
-        // d rows rbase..+31 (clamped), lb rows cbase..+31 (clamped); K = rank
+        // d rows rbase..+31 (clamped), lb rows cbase..+31 (clamped); K = rank; lb
+        // is the first operand, as in the K loop
         const int dr = min(rbase + (lane & 31), p.m - 1);
         const int br = min(cbase + (lane & 31), p.n - 1);
         const uint16_t* dp = p.d + static_cast<long>(dr) * p.rank + kl * 8;
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
               fl = *reinterpret_cast<const u32x4*>(bp + r0);
             }
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, fd), __builtin_bit_cast(bf16x8, fl), acc[i][j], 0, 0, 0);
+                __builtin_bit_cast(bf16x8, fl), __builtin_bit_cast(bf16x8, fd), acc[i][j], 0, 0, 0);
           }
         } else {
           for (int r0 = 0; r0 < p.rank; r0 += 16) {
@@ -306,23 +322,32 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_lora_kernel(NvArgs p) {
               fl = *reinterpret_cast<const u32x4*>(bp + r0);
             }
             accl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, fd), __builtin_bit_cast(bf16x8, fl), accl, 0, 0, 0);
+                __builtin_bit_cast(bf16x8, fl), __builtin_bit_cast(bf16x8, fd), accl, 0, 0, 0);
           }
         }
       }
-      const int col = cbase + (lane & 31);
-      if (col < p.n) {
-        const bool has_bias = p.bias != nullptr;
-        const float bv = has_bias ? bf16_bits_to_f32(p.bias[col]) : 0.f;
-        const bool raw_lora = lora && p.mode == 1;
+      const int row = rbase + (lane & 31);
+      if (row < p.m) {
+        uint16_t* orow = p.out + static_cast<long>(row) * p.n;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int row = rbase + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-          if (row < p.m) {
+        for (int g = 0; g < 4; ++g) {
+          const int c0 = cbase + 8 * g + 4 * kl;
+          uint32_t w[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int q = 4 * g + c;
             float v = __fmul_rn(alpha, acc[i][j][q]);
             if (raw_lora) v = __fadd_rn(v, __fmul_rn(s_lora, accl[q]));
-            if (has_bias) v = __fadd_rn(v, bv);
-            p.out[static_cast<long>(row) * p.n + col] = static_cast<uint16_t>(f32_to_bf16_rne(v));
+            if (has_bias) v = __fadd_rn(v, bv[g][c]);
+            w[c] = f32_to_bf16_rne(v);
+          }
+          if (vec) {
+            if (c0 < p.n)  // n % 4 == 0: all four columns are in range
+              *reinterpret_cast<u32x2*>(orow + c0) = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (c0 + c < p.n) orow[c0 + c] = static_cast<uint16_t>(w[c]);
           }
         }
       }
@@ -358,6 +383,14 @@ __device__ __forceinline__ void nvg_store(uint16_t* p, float v) {
   *p = static_cast<uint16_t>(f32_to_bf16_rne(v));
 }
 __device__ __forceinline__ void nvg_store(float* p, float v) { *p = v; }
+// 4 consecutive outputs, one rounding each: 8 bytes (bf16) or 16 bytes (fp32)
+__device__ __forceinline__ void nvg_store4(uint16_t* p, f32x4 v) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                       f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+}
+__device__ __forceinline__ void nvg_store4(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
 
 template <typename OutT>
 __global__ __launch_bounds__(NV_NT, 1) void nvfp4_grouped_kernel(NvgArgs<OutT> p) {
@@ -490,17 +523,27 @@ __global__ __launch_bounds__(NV_NT, 1) void nvfp4_grouped_kernel(NvgArgs<OutT> p
   // ---- epilogue: alpha[e] * acc, one rounding; rows past the expert's end dropped ----
   if (m0 + wm * 128 >= m_end) return;
   const float alpha = p.alpha[e];
+  // 4 consecutive columns per store where out is aligned for it (n % 256 == 0)
+  const bool vec = (reinterpret_cast<uintptr_t>(p.out) & (4 * sizeof(OutT) - 1)) == 0;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int rbase = m0 + wm * 128 + i * 32;
+    const int row = m0 + wm * 128 + i * 32 + r32;
+    if (row >= m_end) continue;
+    OutT* orow = p.out + static_cast<long>(row) * p.n;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + r32;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = rbase + 8 * (q >> 2) + 4 * h + (q & 3);
-        if (row < m_end)
-          nvg_store(p.out + static_cast<long>(row) * p.n + col, __fmul_rn(alpha, acc[i][j][q]));
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = n0 + wn * 128 + j * 32 + 8 * g + 4 * h;
+        const f32x4 v = {__fmul_rn(alpha, acc[i][j][4 * g]), __fmul_rn(alpha, acc[i][j][4 * g + 1]),
+                         __fmul_rn(alpha, acc[i][j][4 * g + 2]),
+                         __fmul_rn(alpha, acc[i][j][4 * g + 3])};
+        if (vec) {
+          nvg_store4(orow + c0, v);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) nvg_store(orow + c0 + c, v[c]);
+        }
       }
     }
   }
