@@ -98,7 +98,8 @@ def test_zero_codes_scaled_probe(gpu):
     assert np.all(bits16(out) == 0)
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 256, 256), (300, 520, 512), (1, 1, 256)])
+@pytest.mark.parametrize("M,N,K", [(128, 256, 256), (300, 520, 512), (1, 1, 256), (33, 258, 256),
+                                   (70, 301, 256)])
 def test_exact_probe_bitwise(gpu, M, N, K):
     case = _dev(synth.nvfp4_probe("exact", M=M, N=N, K=K), gpu)
     out = mm_nvfp4_lora(case.a, case.b, case.a_sf, case.b_sf, case.alpha)
@@ -137,7 +138,7 @@ def _all_paths(case):
 
 
 @pytest.mark.parametrize("M,N,K,r", [(300, 520, 512, 16), (256, 256, 256, 8), (129, 384, 768, 32),
-                                     (64, 256, 256, 24)])
+                                     (64, 256, 256, 24), (70, 301, 256, 16)])
 def test_small_all_paths(gpu, M, N, K, r):
     case = _dev(synth.nvfp4_lora_case(seed=M + N, M=M, N=N, K=K, r=r), gpu)
     off, raw, prep, ad = _all_paths(case)
@@ -151,6 +152,23 @@ def test_small_all_paths(gpu, M, N, K, r):
     assert np.array_equal(bits16(ad.b_folded), fb)
     check_close(to_f64(prep), NV.mm_nvfp4_prepared(base, alpha, _bits(case.d), fb, zero, bias),
                 "prepared")
+
+
+def test_misaligned_out_matches_aligned_bitwise(gpu):
+    """An output that is not 8-byte aligned (a contiguous view one element
+    into its buffer) takes per-element stores; it must hold the same bits as
+    the aligned output, on every path (off, raw with bias, prepared)."""
+    case = _dev(synth.nvfp4_lora_case(seed=37, M=130, N=520, K=256), gpu)
+    off, raw, prep, ad = _all_paths(case)
+    for ref, kw in ((off, {}), (raw, dict(d=case.d, lora_b=case.lora_b, lora_scale=case.lora_scale)),
+                    (prep, dict(d=case.d, lora_adapter=ad))):
+        buf = torch.full((130 * 520 + 8,), float("nan"), dtype=torch.bfloat16, device=gpu)
+        out = buf[1:1 + 130 * 520].view(130, 520)
+        assert out.data_ptr() % 8 != 0
+        mm_nvfp4_lora(case.a, case.b, case.a_sf, case.b_sf, case.alpha, bias=case.bias, out=out, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        assert torch.isnan(buf[0]) and torch.isnan(buf[1 + 130 * 520:]).all()
 
 
 def test_zero_adapter_outputs_are_bitwise_adapter_off(gpu):

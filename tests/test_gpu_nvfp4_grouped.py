@@ -44,6 +44,27 @@ def test_exact_probe_bitwise(gpu, counts, n, k):
     assert np.array_equal(to_f64(out32)[written], ref[written])
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_misaligned_out_matches_aligned_bitwise(gpu, out_dtype):
+    """An output not aligned for 4-column stores (a contiguous view one element
+    into its buffer) takes per-element stores: the same bits as the aligned
+    output, rows outside the groups untouched."""
+    c = synth.nvfp4_grouped_case(seed=41, counts=(0, 130, 1, 300, 0, 129), n=512, k=256)
+    ref = run(c, gpu, out_dtype)
+    rows = c.a.shape[0]
+    buf = torch.full((rows * 512 + 8,), 7.0, dtype=out_dtype, device=gpu)
+    out = buf[1:1 + rows * 512].view(rows, 512)
+    assert out.data_ptr() % 8 != 0
+    out.copy_(ref)
+    written = np.zeros(rows, dtype=bool)
+    ind = c.m_indptr.numpy()
+    written[ind[0]:ind[-1]] = True
+    out[torch.from_numpy(written).to(gpu)] = float("nan")
+    run(c, gpu, out_dtype, out=out)
+    assert torch.equal(out, ref)
+    assert (buf[0] == 7.0).item() and bool((buf[1 + rows * 512:] == 7.0).all())
+
+
 @pytest.mark.parametrize("side", ["a", "b"])
 def test_scale_decode_all_codes_bitwise(gpu, side):
     """The grouped K loop's UE4M3 decode over every finite scale code, on the
