@@ -11,8 +11,9 @@
 // Three kernels, chosen from host sizes: for groups averaging fewer than 192
 // rows grouped_mm_dma64_kernel; for larger ones grouped_mm_dma_kernel when
 // n % 512 == 0 and grouped_mm_big_kernel otherwise (each with its own notes
-// below).  The big kernel also serves FC1, whose epilogue applies the SwiGLU
-// activation.
+// below).  FC1 takes the same two large-group kernels with the SwiGLU
+// activation in their epilogue (gate and up rows paired inside each
+// wavefront); it does not use the small-group kernel.
 #include "common.hpp"
 
 namespace mi {
@@ -455,11 +456,16 @@ __device__ __forceinline__ int gd_swz(int row) { return (row & 7) ^ ((row >> 3) 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 __device__ __forceinline__ lds_void_ptr lds_ptr(uint16_t* p) { return (lds_void_ptr)(p); }
 
-template <int WM, int WN, int FM, int FN, bool F16, typename OutT>
+// GLU (FC1): b[e] is [n = 2I, k], gate rows 0..I-1 and up rows I..2I-1, and
+// the tile covers BN/2 output columns c0 = n0/2 ..: LDS b block (wn FN + j)
+// holds gate rows c0 + wn 16 FN + 32 j .. for j < FN/2 and the matching up rows
+// for j >= FN/2, so one lane holds both operands of every output it writes
+// (the mapping of grouped_mm_big_kernel); out is [m_rows, I].
+template <int WM, int WN, int FM, int FN, bool F16, bool GLU, typename OutT>
 __device__ __forceinline__ void gd_tile(const uint16_t* __restrict__ a,
                                         const uint16_t* __restrict__ b, OutT* __restrict__ out,
                                         uint16_t* smem, int e, int m0, int rows, int n0, int k,
-                                        int n) {
+                                        int n, const GbGlu& gl) {
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   constexpr int R = BM + BN;                 // LDS rows per stage
   constexpr int NI = R / 64;                 // DMA instructions per wavefront per stage
@@ -473,8 +479,24 @@ __device__ __forceinline__ void gd_tile(const uint16_t* __restrict__ a,
   const int KT = k / GB_BK;
   const uint32_t kbytes = static_cast<uint32_t>(k) * 2;
 
+  const int inter = n / 2, c0 = n0 / 2;  // GLU: output width and first output column
   const __amdgpu_buffer_rsrc_t br =
-      buf_rsrc(b + (static_cast<long>(e) * n + n0) * k, static_cast<uint32_t>(BN) * kbytes);
+      buf_rsrc(b + (static_cast<long>(e) * n + (GLU ? c0 : n0)) * k,
+               static_cast<uint32_t>(GLU ? inter + BN / 2 : BN) * kbytes);
+  static_assert(!GLU || FN % 2 == 0, "GLU pairs gate and up fragments");
+  // b row (relative to the descriptor) of the first LDS row of b instruction
+  // i >= NIA: LDS b row R = 8 (8i + wave) - BM, block R/32 = wn FN + j
+  uint32_t bso[NI - NIA];
+#pragma unroll
+  for (int i = NIA; i < NI; ++i) {
+    const int R = 8 * (8 * i + wave) - BM;
+    int row = R;
+    if constexpr (GLU) {
+      const int blk = R >> 5, jj = blk % FN, wb = blk / FN;
+      row = (jj < FN / 2 ? 0 : inter) + wb * 16 * FN + (jj % (FN / 2)) * 32 + (R & 31);
+    }
+    bso[i - NIA] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(row) * kbytes);
+  }
 
   // DMA instruction i of this wavefront fills LDS rows 8g .. 8g+7 with
   // g = 8i + wave (i < NIA: a rows, else b rows 8g - BM ..).  Lane l takes row
@@ -500,8 +522,8 @@ __device__ __forceinline__ void gd_tile(const uint16_t* __restrict__ a,
       if (i < NIA)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ari[i], lds_ptr(dst), 16, dvo, so, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            br, lds_ptr(dst), 16, dvo, so + static_cast<uint32_t>(8 * g - BM) * kbytes, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(br, lds_ptr(dst), 16, dvo, so + bso[i - NIA], 0,
+                                                 0);
     }
   };
 
@@ -566,20 +588,72 @@ __device__ __forceinline__ void gd_tile(const uint16_t* __restrict__ a,
 
   // acc[i][j][q]: tile row (wm FM + i) 32 + r, column (wn FN + j) 32 + 8 (q/4) + 4h + q%4
   if (wm * 32 * FM >= rows) return;
-  const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(out + static_cast<long>(m0) * n,
-                                                static_cast<uint32_t>(rows) * n * sizeof(OutT));
+  if constexpr (!GLU) {
+    const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(out + static_cast<long>(m0) * n,
+                                                  static_cast<uint32_t>(rows) * n * sizeof(OutT));
+  #pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const uint32_t orow =
+          (static_cast<uint32_t>((wm * FM + i) * 32 + r) * n + n0 + wn * FN * 32 + 4 * h) *
+          sizeof(OutT);
+  #pragma unroll
+      for (int j = 0; j < FN; ++j) {
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                           acc[i][j][4 * g + 3]};
+          bstore_out4<OutT>(orsrc, orow + (j * 32 + 8 * g) * sizeof(OutT), v);
+        }
+      }
+    }
+  } else {
+    // gate acc[i][j], up acc[i][j + FN/2] (j < FN/2): tile row (wm FM + i) 32 + r,
+    // output column c0 + wn 16 FN + 32 j + 8 (q/4) + 4h + q%4; the SwiGLU of
+    // grouped_mm_big_kernel
+    const float alpha = gl.alpha ? gl.alpha[e] : 1.f;
+    const float beta = gl.beta ? gl.beta[e] : 0.f;
+    const float limit = gl.limit ? gl.limit[e] : __builtin_inff();
+    const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(
+        out + static_cast<long>(m0) * inter, static_cast<uint32_t>(rows) * inter * sizeof(OutT));
+    const bool has_delta = gl.delta != nullptr;
+    const __amdgpu_buffer_rsrc_t drsrc =
+        buf_rsrc(has_delta ? gl.delta + static_cast<long>(m0) * n : gl.delta,
+                 has_delta ? static_cast<uint32_t>(rows) * n * 2 : 0u);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const uint32_t orow =
-        (static_cast<uint32_t>((wm * FM + i) * 32 + r) * n + n0 + wn * FN * 32 + 4 * h) *
-        sizeof(OutT);
+    for (int i = 0; i < FM; ++i) {
+      const uint32_t trow = (wm * FM + i) * 32 + r;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+      for (int j = 0; j < FN / 2; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                         acc[i][j][4 * g + 3]};
-        bstore_out4<OutT>(orsrc, orow + (j * 32 + 8 * g) * sizeof(OutT), v);
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t col = c0 + wn * 16 * FN + j * 32 + 8 * g + 4 * h;
+          float hg[4], hu[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            hg[q] = acc[i][j][4 * g + q];
+            hu[q] = acc[i][j + FN / 2][4 * g + q];
+          }
+          if (has_delta) {
+            const u32x2 dg = buf_ld64(drsrc, (trow * n + col) * 2, 0);
+            const u32x2 du = buf_ld64(drsrc, (trow * n + inter + col) * 2, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t wg = dg[q >> 1], wu = du[q >> 1];
+              hg[q] += __uint_as_float((q & 1) ? (wg & 0xffff0000u) : (wg << 16));
+              hu[q] += __uint_as_float((q & 1) ? (wu & 0xffff0000u) : (wu << 16));
+            }
+          }
+          f32x4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float gg = fminf(hg[q], limit);
+            const float uu = fminf(fmaxf(hu[q], -limit), limit);
+            // logistic function from the hardware exp2 and reciprocal (a few ulp)
+            const float sig = __builtin_amdgcn_rcpf(1.f + __expf(-alpha * gg));
+            v[q] = gg * sig * (uu + beta);
+          }
+          bstore_out4<OutT>(orsrc, (trow * inter + col) * sizeof(OutT), v);
+        }
       }
     }
   }
@@ -651,11 +725,11 @@ __device__ __forceinline__ void gd_walk(const int32_t* __restrict__ m_indptr, in
   }
 }
 
-template <bool F16, typename OutT>
+template <bool F16, bool GLU, typename OutT>
 __global__ __launch_bounds__(64 * GD_WAVES, 1) void grouped_mm_dma_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
     const int32_t* __restrict__ m_indptr, OutT* __restrict__ out, int m_rows, int k, int n,
-    int E) {
+    int E, GbGlu gl) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * GD_STAGE];
   // the walk's tables live in stage 1, which the first K step overwrites only
   // after the barrier that follows stage 0's loads
@@ -715,11 +789,11 @@ __global__ __launch_bounds__(64 * GD_WAVES, 1) void grouped_mm_dma_kernel(
   rows = __builtin_amdgcn_readfirstlane(rows);
   n0 = __builtin_amdgcn_readfirstlane(n0);
   if (kind == 3)
-    gd_tile<4, 2, 3, 4, F16, OutT>(a, b, out, smem, e, m0, rows, n0, k, n);
+    gd_tile<4, 2, 3, 4, F16, GLU, OutT>(a, b, out, smem, e, m0, rows, n0, k, n, gl);
   else if (kind == 2)
-    gd_tile<2, 4, 4, 2, F16, OutT>(a, b, out, smem, e, m0, rows, n0, k, n);
+    gd_tile<2, 4, 4, 2, F16, GLU, OutT>(a, b, out, smem, e, m0, rows, n0, k, n, gl);
   else
-    gd_tile<1, 8, 4, 2, F16, OutT>(a, b, out, smem, e, m0, rows, n0, k, n);
+    gd_tile<1, 8, 4, 2, F16, GLU, OutT>(a, b, out, smem, e, m0, rows, n0, k, n, gl);
 }
 
 // ---------------------------------------------------------------------------
@@ -971,21 +1045,21 @@ mi_status launch_grouped_big(const void* a, int64_t m_rows, int64_t k, const voi
   return launch_status(GLU ? "grouped_mm_swiglu" : "grouped_mm_bf16");
 }
 
-template <bool F16, typename OutT>
+template <bool F16, bool GLU, typename OutT>
 mi_status launch_grouped_dma(const void* a, int64_t m_rows, int64_t k, const void* b,
                              int64_t batch, int64_t n, const int32_t* m_indptr, void* out,
-                             hipStream_t stream) {
+                             hipStream_t stream, const GbGlu& gl) {
   // upper bound on the tiles of the three kinds: every tile covers at least
   // 128 rows of one expert or is its one partial tile, and at least 256
   // columns' worth of n-panels
   const long ub_tiles = ((m_rows + 127) / 128 + batch) * (n / 256);
   const long G = ((ub_tiles + 7) / 8 + 4) * 8;
   MI_REQUIRE(G < (1L << 31), "grouped_mm_bf16: problem too large");
-  hipLaunchKernelGGL((grouped_mm_dma_kernel<F16, OutT>), dim3(G), dim3(64 * GD_WAVES), 0, stream,
-                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), m_indptr,
-                     static_cast<OutT*>(out), static_cast<int>(m_rows), static_cast<int>(k),
-                     static_cast<int>(n), static_cast<int>(batch));
-  return launch_status("grouped_mm_bf16");
+  hipLaunchKernelGGL((grouped_mm_dma_kernel<F16, GLU, OutT>), dim3(G), dim3(64 * GD_WAVES), 0,
+                     stream, static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
+                     m_indptr, static_cast<OutT*>(out), static_cast<int>(m_rows),
+                     static_cast<int>(k), static_cast<int>(n), static_cast<int>(batch), gl);
+  return launch_status(GLU ? "grouped_mm_swiglu" : "grouped_mm_bf16");
 }
 
 template <bool F16, typename OutT>
@@ -999,7 +1073,8 @@ mi_status dispatch_grouped(const void* a, int64_t m_rows, int64_t k, const void*
   // inside one buffer descriptor.
   const int64_t avg = m_rows / batch;
   if (avg >= 192 && n % 512 == 0 && static_cast<uint64_t>(n) * 384 * sizeof(OutT) < (1ULL << 32))
-    return launch_grouped_dma<F16, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream);
+    return launch_grouped_dma<F16, false, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
+                                                GbGlu{});
   if (avg >= 192)
     return launch_grouped_big<F16, false, OutT>(a, m_rows, k, b, batch, n, m_indptr, out, stream,
                                                GbGlu{});
@@ -1082,12 +1157,26 @@ extern "C" mi_status mi_grouped_mm_swiglu(const void* a, int64_t m_rows, int64_t
   const GbGlu gl{static_cast<const uint16_t*>(fc1_delta), alpha, beta, limit};
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool f16 = ab_dtype == MI_F16;
-  if (out_dtype == MI_BF16)
-    return f16 ? launch_grouped_big<true, true, Bf16Out>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl)
-               : launch_grouped_big<false, true, Bf16Out>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl);
-  if (out_dtype == MI_F16)
-    return f16 ? launch_grouped_big<true, true, _Float16>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl)
-               : launch_grouped_big<false, true, _Float16>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl);
-  return f16 ? launch_grouped_big<true, true, float>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl)
-             : launch_grouped_big<false, true, float>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl);
+  // large average groups with 512-wide panels (I % 256 == 0) take the
+  // direct-to-LDS tiles, the rest the register-staged 256 x 256 ones
+  const size_t osz = out_dtype == MI_F32 ? 4 : 2;
+  const bool dma = m_rows / batch >= 192 && n % 512 == 0 &&
+                   static_cast<uint64_t>(k) * 2 * 512 < (1ULL << 32) &&
+                   static_cast<uint64_t>(k) * 2 * (inter_size + 256) < (1ULL << 32) &&
+                   static_cast<uint64_t>(inter_size) * 384 * osz < (1ULL << 32);
+#define MI_SWIGLU_LAUNCH(F16_, OutT_)                                                          \
+  return dma ? launch_grouped_dma<F16_, true, OutT_>(a, m_rows, k, b, batch, n, m_indptr, out, s, \
+                                                     gl)                                         \
+             : launch_grouped_big<F16_, true, OutT_>(a, m_rows, k, b, batch, n, m_indptr, out, s, gl)
+  if (out_dtype == MI_BF16) {
+    if (f16) MI_SWIGLU_LAUNCH(true, Bf16Out);
+    MI_SWIGLU_LAUNCH(false, Bf16Out);
+  }
+  if (out_dtype == MI_F16) {
+    if (f16) MI_SWIGLU_LAUNCH(true, _Float16);
+    MI_SWIGLU_LAUNCH(false, _Float16);
+  }
+  if (f16) MI_SWIGLU_LAUNCH(true, float);
+  MI_SWIGLU_LAUNCH(false, float);
+#undef MI_SWIGLU_LAUNCH
 }

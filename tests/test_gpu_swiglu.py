@@ -40,6 +40,10 @@ def oracle(c):
     ((0, 1, 128, 129, 255, 300, 0, 40), 256, 192, dict(ints=True)),
     ((300, 0, 513, 1), 128, 256, dict(with_delta=True, act_params=True)),
     ((200, 260), 384, 320, dict(act_params=True)),
+    # average >= 192 rows and I % 256 == 0: the direct-to-LDS tiles -- 384-row
+    # tiles, 256-row tails (129 rows), 128-row tails on 512-wide panels (1, 40 rows)
+    ((0, 385, 1, 700, 129, 0, 300, 40), 256, 192, dict(with_delta=True, act_params=True)),
+    ((769, 0, 200), 512, 256, dict(ints=True)),
 ])
 def test_small_cases(gpu, counts, inter, k, kw):
     c = synth.fc1_case(seed=len(counts), counts=counts, hidden=k, inter=inter, **kw)
@@ -49,15 +53,17 @@ def test_small_cases(gpu, counts, inter, k, kw):
         check_close(to_f64(out)[written], ref[written], f"swiglu {c.name} {dt}")
 
 
-def test_rows_outside_groups_untouched(gpu):
-    base = synth.fc1_case(seed=5, counts=(5, 0, 40), hidden=128, inter=128, ints=True)
+@pytest.mark.parametrize("counts,inter", [((5, 0, 40), 128),      # register-staged tiles
+                                          ((5, 0, 600), 256)])    # direct-to-LDS tiles
+def test_rows_outside_groups_untouched(gpu, counts, inter):
+    base = synth.fc1_case(seed=5, counts=counts, hidden=128, inter=inter, ints=True)
     g = synth.gen(6)
     a = torch.cat([synth.bf16_ints((3, 128), -2, 2, g), base.a, synth.bf16_ints((7, 128), -2, 2, g)])
     c = synth.Fc1Case("offset rows", a, base.b, base.m_indptr + 3, None, None, None, None)
-    sentinel = torch.full((a.shape[0], 128), -7.0, dtype=torch.bfloat16, device=gpu)
+    sentinel = torch.full((a.shape[0], inter), -7.0, dtype=torch.bfloat16, device=gpu)
     out = run(c, gpu, out=sentinel)
     ref, written = oracle(c)
-    assert not written[:3].any() and not written[-7:].any() and written.sum() == 45
+    assert not written[:3].any() and not written[-7:].any() and written.sum() == sum(counts)
     assert (to_f64(out)[~written] == -7.0).all()
     check_close(to_f64(out)[written], ref[written], "swiglu offset rows")
 
@@ -110,9 +116,11 @@ def test_full_size_sampled(gpu):
     check_close(got, ref, "swiglu full size (sampled)")
 
 
-def test_fp16_operands(gpu):
+@pytest.mark.parametrize("counts,inter", [((150, 0, 300, 7), 128),          # register-staged
+                                          ((300, 0, 513, 1, 200), 256)])   # direct-to-LDS
+def test_fp16_operands(gpu, counts, inter):
     """fp16 a and b (the GEMM's other input type), every output type."""
-    c = synth.fc1_case(seed=13, counts=(150, 0, 300, 7), hidden=192, inter=128, act_params=True)
+    c = synth.fc1_case(seed=13, counts=counts, hidden=192, inter=inter, act_params=True)
     c16 = synth.Fc1Case("fp16 operands", c.a.to(torch.float16), c.b.to(torch.float16),
                         c.m_indptr, None, c.alpha, c.beta, c.limit)
     np_ = lambda t: t.cpu().numpy()
