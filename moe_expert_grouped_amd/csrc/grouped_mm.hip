@@ -947,6 +947,9 @@ __global__ __launch_bounds__(64 * GD_WAVES, 1) void grouped_mm_dma64_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t s1[GD4_STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t s2[GD4_STAGE];
   __shared__ __attribute__((aligned(16))) uint16_t s3[GD4_STAGE];
+  // the walk's tables live in the last stage, which the first K step's loads
+  // overwrite only after the barrier that follows the first three stages
+  static_assert(2 * (GM_MAX_EXPERTS + 1) * sizeof(int) <= GD4_STAGE * sizeof(uint16_t), "tables");
   int* const s_t0 = reinterpret_cast<int*>(s3);
   int* const s_row0 = s_t0 + (GM_MAX_EXPERTS + 1);
   if ((threadIdx.x >> 6) == 0) gd64_walk(m_indptr, m_rows, E, s_t0, s_row0);

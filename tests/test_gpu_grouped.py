@@ -31,8 +31,8 @@ def test_tiny_moe_fc2(gpu):
 
 
 @pytest.mark.parametrize("counts,n,k", [
-    ((0, 1, 17, 128, 0, 255), 256, 128),          # small groups: 64x64 tiles
-    ((100, 0, 150, 177, 0, 229), 512, 192),       # medium: 64x64 tiles, several per group
+    ((0, 1, 17, 128, 0, 255), 256, 128),          # small groups: 64x128 tiles, 2 K steps
+    ((100, 0, 150, 177, 0, 229), 512, 192),       # medium: 64x128 tiles, several per group
     ((300, 0, 513, 1, 256, 0, 390), 256, 256),    # large: 256x256 tiles, ragged tails
     # large, n not a multiple of 512 (256x256 tiles), odd K-step count: last
     # pieces of 128 / 129 / 255 / 1 / 0 / 128 / 88 / 232 rows (128-row tiles
@@ -180,7 +180,7 @@ def test_deterministic(gpu):
 
 
 @pytest.mark.parametrize("counts,n,k", [
-    ((0, 1, 17, 128, 0, 255), 256, 128),          # small groups: 64x64 tiles
+    ((0, 1, 17, 128, 0, 255), 256, 128),          # small groups: 64x128 tiles, 2 K steps
     ((300, 0, 513, 1, 256, 0, 390), 256, 256),    # large: 256x256 tiles
 ])
 def test_fp16_inputs_integer_probe_bitwise_every_output(gpu, counts, n, k):
