@@ -865,7 +865,7 @@ __device__ __forceinline__ void gd4_tile(const uint16_t* __restrict__ a,
                                          const uint16_t* __restrict__ b, OutT* __restrict__ out,
                                          uint16_t* s0, uint16_t* s1, uint16_t* s2, uint16_t* s3,
                                          int e, int m0, int rows, int n0, int k, int n) {
-  constexpr int WM = 2, WN = 4, BM = 64, BN = 128, R = BM + BN, NI = R / 64, NIA = BM / 64;
+  constexpr int WN = 4, BM = 64, BN = 128, R = BM + BN, NI = R / 64, NIA = BM / 64;  // 2 x 4 waves
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;

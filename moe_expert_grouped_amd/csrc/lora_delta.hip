@@ -1222,23 +1222,6 @@ struct Fc1Args {
   int E, L, R, OF, maxblk, nch, out_kind;  // OF: output width (B_le rows)
 };
 
-// 4 consecutive output columns of one row, rounded once (streaming stores:
-// the rows are written once and not read here)
-__device__ __forceinline__ void store_out4(void* out, int kind, long off, f32x4 v) {
-  if (kind == 1) {
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(out) + off));
-  } else if (kind == 2) {
-    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    const h4 h = {static_cast<_Float16>(v.x), static_cast<_Float16>(v.y),
-                  static_cast<_Float16>(v.z), static_cast<_Float16>(v.w)};
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x2, h),
-                                reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off));
-  } else {
-    const u32x2 w = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off));
-  }
-}
-
 // 8 consecutive output columns of one row, rounded once (streaming stores:
 // the rows are written once and not read here)
 __device__ __forceinline__ void store_out8c(void* out, int kind, long off, f32x4 v0, f32x4 v1) {
