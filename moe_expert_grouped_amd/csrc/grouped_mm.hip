@@ -865,6 +865,12 @@ constexpr int GD4_STAGE = 192 * 64;  // 64 + 128 rows of 128 bytes
 // waited for at the barrier that ends step kt+2 (vmcnt leaves the two later
 // stages in flight); the fragment reads of a stage need no load wait.  The
 // DMA mapping, swizzle and zero rows past the group are those of gd_tile.
+// b is loaded with the streaming (non-temporal) cache policy: weights that
+// come from memory (the usual case: other layers' weights pass through the
+// caches between two calls) stream faster -- uniform E=8 x 128 rows, k=4096,
+// n=2048: 67 -> 47 us -- but b is then not kept in the memory-side cache for
+// the next call, so back-to-back calls on cached weights take 45 instead of
+// 35 us.
 template <bool F16, typename OutT>
 __device__ __forceinline__ void gd4_tile(const uint16_t* __restrict__ a,
                                          const uint16_t* __restrict__ b, OutT* __restrict__ out,
@@ -896,9 +902,9 @@ __device__ __forceinline__ void gd4_tile(const uint16_t* __restrict__ a,
       uint16_t* dst = st + g * 512;
       if (i < NIA)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ari[i], lds_ptr(dst), 16, dvo, so, 0, 0);
-      else
+      else  // b: streaming (non-temporal) loads
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            br, lds_ptr(dst), 16, dvo, so + static_cast<uint32_t>(8 * g - BM) * kbytes, 0, 0);
+            br, lds_ptr(dst), 16, dvo, so + static_cast<uint32_t>(8 * g - BM) * kbytes, 0, 2);
     }
   };
   int fo[4];
