@@ -693,7 +693,8 @@ __global__ __launch_bounds__(256, AMAX > SLE_AMAX ? 1 : 2) void shrink_le_kernel
     for (int u = 0; u < 8; ++u) {  // past the end: reload the last chunk (not stored)
       const int c = min(c0 + u * 256 + tid, R16 * cpr - 1);
       const int r = c / cpr, cc = c - r * cpr;
-      v[u] = gld<u32x4>(Ale + static_cast<long>(min(r, p.rank - 1)) * p.I + cc * 8);
+      // streaming loads: each (adapter, expert) pair's A_le is read once, here
+      v[u] = gld_nt<u32x4>(Ale + static_cast<long>(min(r, p.rank - 1)) * p.I + cc * 8);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
