@@ -252,7 +252,7 @@ def pmc_table(out_md, fetch_dir, write_dir):
             w, _ = _pmc_avg(wr, "WRITE_SIZE", pick)
             fb, wb = f * 1024.0 * f_fac / 1e6, w * 1024.0 * w_fac / 1e6
             fh.write(f"| {n} | {nd} | {fb:.1f} | {wb:.1f} | {fb + wb:.1f} |\n")
-    print(f"appended to {out_md}")
+    print(f"wrote the table into {out_md}")
 
 
 def trace_summary(out_md, trace_dir, command):
