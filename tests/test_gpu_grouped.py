@@ -123,21 +123,22 @@ def test_uniform_full_size_bf16_and_fp32(gpu):
         check_close(to_f64(out), ref, f"uniform E=8 tpe=128 k=4096 n=2048 {dt}")
 
 
-def test_random_ragged_shapes_all_tile_configs(gpu):
-    g = np.random.default_rng(7)
-    for avg in (40, 130, 400):
+@pytest.mark.parametrize("n", [768, 1024])  # large groups: 256x256 tiles / direct-to-LDS tiles
+def test_random_ragged_shapes_all_tile_configs(gpu, n):
+    g = np.random.default_rng(7 + n)
+    for avg in (40, 130, 400, 700):
         E = 9
         counts = g.integers(0, 2 * avg, E)
         counts[g.integers(0, E)] = 0
         mi = torch.zeros(E + 1, dtype=torch.int32)
         mi[1:] = torch.from_numpy(np.cumsum(counts)).to(torch.int32)
-        gg = synth.gen(int(avg))
+        gg = synth.gen(int(avg) + n)
         a = synth.bf16_normal((int(mi[-1]), 320), 1.0, gg)
-        b = synth.bf16_normal((E, 768, 320), 320 ** -0.5, gg)
-        case = synth.GroupedCase(f"avg{avg}", a, b, mi)
+        b = synth.bf16_normal((E, n, 320), 320 ** -0.5, gg)
+        case = synth.GroupedCase(f"avg{avg} n{n}", a, b, mi)
         ref, written = _oracle(case)
         out = _run(case, gpu)
-        check_close(to_f64(out)[written], ref[written], f"ragged avg={avg}")
+        check_close(to_f64(out)[written], ref[written], f"ragged avg={avg} n={n}")
 
 
 @pytest.mark.slow
