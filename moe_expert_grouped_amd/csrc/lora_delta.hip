@@ -1087,9 +1087,12 @@ __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* cons
   float fs = ring[0].f;            // F16 only
   load(ring[0], D, bptr(D));
   for (int i0 = 0; i0 < nblk; i0 += D) {
+    // this round's refill addresses, made scalar once (not inside the steps,
+    // where each conversion would wait for the accumulator reads in flight)
     const uint16_t* bpr[D];
 #pragma unroll
-    for (int d = 0; d < D; ++d) bpr[d] = bptr(i0 + d + 1 + D);
+    for (int d = 0; d < D; ++d)
+      bpr[d] = reinterpret_cast<const uint16_t*>(uniform_ptr(bptr(i0 + d + 1 + D)));
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int i = i0 + d;
@@ -1101,6 +1104,8 @@ __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* cons
 #pragma unroll
         for (int g = 0; g < EXP_NCG; ++g) v[g] = *a[g];
       }
+      // the reads go first, so their latency runs under the next MFMAs and loads
+      __builtin_amdgcn_sched_barrier(0);
       Ring<NB>& rn = ring[(d + 1) % D];  // holds block i+1
       f32x4 accn[EXP_NCG];
       mma(rn, accn);
@@ -1124,6 +1129,9 @@ __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* cons
       for (int g = 0; g < EXP_NCG; ++g) acc[g] = accn[g];
       tl = tln;
       fs = fsn;
+      // ring steps stay in order: left free, the scheduler hoists the MFMAs of
+      // the whole round to its top, which then waits for every load in flight
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
