@@ -1328,17 +1328,29 @@ __global__ __launch_bounds__(256) void fc1_expand_kernel(Fc1Args p) {
   __syncthreads();
   const int nblk = s_nblk;
 
-  auto do_block = [&](int ti, int bi) {
+  // one block's operands: its u record fragments and this lane's slot (row,
+  // whether the slot is real, the fp16 factor)
+  struct Blk {
+    u32x4 fu[NB];
+    uint32_t tlw;
+    int row;
+    float fs;
+  };
+  const int slot = col;
+  auto fetch = [&](int ti, int bi) {
+    Blk q;
     const long tb = static_cast<long>(ti) * p.maxblk + bi;
     const uint16_t* rec = p.u2 + (static_cast<long>(ti) * p.cap + bi * 16) * NB * 32;
-    u32x4 fu[NB];
 #pragma unroll
-    for (int c = 0; c < NB; ++c) fu[c] = gld<u32x4>(rec + c * 512 + lane * 8);
-    const int slot = col;
-    const uint32_t tlw = gld<uint32_t>(p.blk_tl + tb * 4 + (slot >> 2));
-    const bool real = ((tlw >> (8 * (slot & 3))) & 0xFFu) != 0xFFu;
-    const long row = gld<int>(p.blk_row + tb * 16 + slot);
-    const float fs = F16 ? gld<float>(p.blk_f + tb * 16 + slot) : 1.f;
+    for (int c = 0; c < NB; ++c) q.fu[c] = gld<u32x4>(rec + c * 512 + lane * 8);
+    q.tlw = gld<uint32_t>(p.blk_tl + tb * 4 + (slot >> 2));
+    q.row = gld<int>(p.blk_row + tb * 16 + slot);
+    q.fs = F16 ? gld<float>(p.blk_f + tb * 16 + slot) : 1.f;
+    return q;
+  };
+  auto compute = [&](const Blk& q) {
+    const bool real = ((q.tlw >> (8 * (slot & 3))) & 0xFFu) != 0xFFu;
+    const long row = q.row;
 #pragma unroll
     for (int gp = 0; gp < NG / 2; ++gp) {
       f32x4 acc[2];
@@ -1351,23 +1363,30 @@ __global__ __launch_bounds__(256) void fc1_expand_kernel(Fc1Args p) {
           const u32x4 a4 = u32x4{b2.x, b2.y, b2.x, b2.y};
           if constexpr (F16)
             acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a4),
-                                                            __builtin_bit_cast(f16x8, fu[c]),
+                                                            __builtin_bit_cast(f16x8, q.fu[c]),
                                                             acc[h], 0, 0, 0);
           else
             acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a4),
-                                                             __builtin_bit_cast(bf16x8, fu[c]),
+                                                             __builtin_bit_cast(bf16x8, q.fu[c]),
                                                              acc[h], 0, 0, 0);
         }
-        if (F16) acc[h] = acc[h] * fs;  // the slot's 2^-k: exact
+        if (F16) acc[h] = acc[h] * q.fs;  // the slot's 2^-k: exact
       }
       // lane (slot, kq): columns 32 gp + 8 kq .. + 7 of its slot's row
       if (real) store_out8c(p.out, p.out_kind, row * p.OF + h0 + 32 * gp + 8 * kq, acc[0], acc[1]);
     }
   };
   if (nblk <= FC1_MAX_BLK) {
-    for (int j = wave; j < nblk; j += 4) {
-      const int v = s_blk[j];
-      do_block(t0 + (v >> 12), v & 4095);
+    // the next block's operands are loaded while this one is computed and
+    // stored (the last step reloads the last block; not computed)
+    if (wave < nblk) {
+      Blk cur = fetch(t0 + (s_blk[wave] >> 12), s_blk[wave] & 4095);
+      for (int j = wave; j < nblk; j += 4) {
+        const int v = s_blk[min(j + 4, nblk - 1)];
+        const Blk nxt = fetch(t0 + (v >> 12), v & 4095);
+        compute(cur);
+        cur = nxt;
+      }
     }
   } else {  // more blocks than the list holds: walk the tiles directly
     int j = 0;
@@ -1375,7 +1394,7 @@ __global__ __launch_bounds__(256) void fc1_expand_kernel(Fc1Args p) {
       const int b0 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e);
       const int b1 = gld<int>(p.tex + static_cast<long>(ti) * E1 + e + 1);
       for (int bi = b0; bi < b1; ++bi, ++j)
-        if ((j & 3) == wave) do_block(ti, bi);
+        if ((j & 3) == wave) compute(fetch(ti, bi));
     }
   }
 }
