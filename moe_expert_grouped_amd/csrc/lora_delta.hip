@@ -1000,7 +1000,7 @@ template <int NB, bool PART, bool DUP, bool F16>
 __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* const* s_bp,
                                               const char* u2t, const char* tlt, const char* ft,
                                               int nblk, int R, int H, int h0) {
-  constexpr int D = NB == 1 ? 8 : (NB == 2 ? 4 : (NB == 4 ? 2 : 1));  // ring depth
+  constexpr int D = NB == 1 ? 4 : (NB == 2 ? 4 : (NB == 4 ? 2 : 1));  // ring depth
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, kq = lane >> 4;
   // byte offsets of this lane inside a block's u record, B_le, token-row table
