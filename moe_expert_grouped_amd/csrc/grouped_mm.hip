@@ -161,6 +161,31 @@ __device__ __forceinline__ void bstore_out4<float>(__amdgpu_buffer_rsrc_t r, uin
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
 }
 
+// 4 outputs converted to OutT and packed (the conversions of bstore_out4)
+template <typename OutT>
+struct Packed4;
+template <>
+struct Packed4<Bf16Out> {
+  typedef u32x2 T;
+  __device__ static T pack(f32x4 v) {
+    typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(u32x2, __builtin_convertvector(v, b4));
+  }
+};
+template <>
+struct Packed4<_Float16> {
+  typedef u32x2 T;
+  __device__ static T pack(f32x4 v) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(u32x2, __builtin_convertvector(v, h4));
+  }
+};
+template <>
+struct Packed4<float> {
+  typedef u32x4 T;
+  __device__ static T pack(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
+};
+
 // Instruction interleave of a sub-step: the NR LDS reads of the next
 // fragments go out between the first NR of its NM MFMAs, so they complete
 // under this sub-step.
@@ -592,18 +617,49 @@ __device__ __forceinline__ void gd_tile(const uint16_t* __restrict__ a,
   if constexpr (!GLU) {
     const __amdgpu_buffer_rsrc_t orsrc = buf_rsrc(out + static_cast<long>(m0) * n,
                                                   static_cast<uint32_t>(rows) * n * sizeof(OutT));
-  #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const uint32_t orow =
-          (static_cast<uint32_t>((wm * FM + i) * 32 + r) * n + n0 + wn * FN * 32 + 4 * h) *
-          sizeof(OutT);
-  #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-  #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                           acc[i][j][4 * g + 3]};
-          bstore_out4<OutT>(orsrc, orow + (j * 32 + 8 * g) * sizeof(OutT), v);
+    // The outputs go through this wavefront's own share of the LDS stages
+    // (free after the K loop's last barrier): each lane writes its values in
+    // place (one tile row, 4 runs of 4 columns per 32 x 32 block), then reads
+    // back 16-byte pieces of whole rows, so each store instruction writes rows
+    // of contiguous 16-byte pieces instead of 32 rows of 16 bytes.  Rows past
+    // the group's end fall outside the buffer range and are dropped.
+    constexpr int ES = sizeof(OutT);
+    constexpr int WC = 32 * FN;                         // columns of the wavefront
+    constexpr int RB = WC * ES + 16;                    // padded LDS row, bytes
+    constexpr int REG = 2 * GD_STAGE * 2 / GD_WAVES;    // LDS bytes per wavefront
+    constexpr int PB = REG / (32 * RB) < FM ? REG / (32 * RB) : FM;  // 32-row blocks per pass
+    static_assert(PB >= 1, "epilogue stage");
+    constexpr int CPR = WC * ES / 16;                   // 16-byte pieces per row
+    static_assert(CPR <= 64 && 64 % CPR == 0, "pieces per row");
+    constexpr int RPI = 64 / CPR;                       // rows per read instruction
+    char* const reg = reinterpret_cast<char*>(smem) + wave * REG;
+    const uint32_t col0 = static_cast<uint32_t>(n0 + wn * FN * 32) * ES;
+    const int pr = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int i0 = 0; i0 < FM; i0 += PB) {
+#pragma unroll
+      for (int ii = 0; ii < PB; ++ii) {
+        if (i0 + ii < FM) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 v = {acc[i0 + ii][j][4 * g], acc[i0 + ii][j][4 * g + 1],
+                               acc[i0 + ii][j][4 * g + 2], acc[i0 + ii][j][4 * g + 3]};
+              *reinterpret_cast<typename Packed4<OutT>::T*>(
+                  reg + (ii * 32 + r) * RB + (j * 32 + 8 * g + 4 * h) * ES) =
+                  Packed4<OutT>::pack(v);
+            }
+        }
+      }
+      const int nr = (FM - i0 < PB ? FM - i0 : PB) * 32;  // rows of this pass
+#pragma unroll
+      for (int rr0 = 0; rr0 < PB * 32; rr0 += RPI) {
+        const int rr = rr0 + pr;
+        if (rr0 < nr) {
+          const u32x4 d = *reinterpret_cast<const u32x4*>(reg + rr * RB + pc * 16);
+          const uint32_t trow = static_cast<uint32_t>((wm * FM + i0) * 32 + rr);
+          __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, trow * n * ES + col0 + pc * 16, 0, 0);
         }
       }
     }
