@@ -97,11 +97,14 @@ __device__ __forceinline__ long sf_word_off(int row, int ct, int nct) {
   return (static_cast<long>(row >> 7) * nct + ct) * 512 + (row & 31) * 16 + ((row & 127) >> 5) * 4;
 }
 
-template <typename T>
-__global__ __launch_bounds__(QZ_THREADS) void fp4_quantize_kernel(QzArgs p) {
+// the quantiser's loads and arithmetic for one wavefront; TAB: r comes from
+// the workgroup's table s_r (its chunks all lie in matrix b0 of the batch)
+template <typename T, bool TAB>
+__device__ __forceinline__ void qz_wave(const QzArgs& p, const float* s_r, uint32_t b0) {
   const int lane = threadIdx.x & 63;
   const long wave = (static_cast<long>(blockIdx.x) * QZ_THREADS + threadIdx.x) >> 6;
   const T* x = static_cast<const T*>(p.x);
+  const float g0 = TAB ? gld<float>(p.gscale + b0) : 0.f;
   Chunk8<T> ch[QZ_SEG];
   long c[QZ_SEG];
 #pragma unroll
@@ -114,8 +117,9 @@ __global__ __launch_bounds__(QZ_THREADS) void fp4_quantize_kernel(QzArgs p) {
     // the whole wavefront reaches the shuffles; chunks past the end compute
     // on whatever their registers hold and store nothing
     const bool in = c[j] < p.chunks;
-    const uint32_t bi = (in && p.batched) ? static_cast<uint32_t>(c[j] / p.per_batch) : 0u;
-    const float g = in ? gld<float>(p.gscale + bi) : 0.f;
+    const uint32_t bi =
+        TAB ? b0 : ((in && p.batched) ? static_cast<uint32_t>(c[j] / p.per_batch) : 0u);
+    const float g = TAB ? g0 : (in ? gld<float>(p.gscale + bi) : 0.f);
     float xs[8], am = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -124,8 +128,13 @@ __global__ __launch_bounds__(QZ_THREADS) void fp4_quantize_kernel(QzArgs p) {
     }
     am = fmaxf(am, __shfl_xor(am, 1));  // the block's other 8 elements
     const uint32_t sfc = ue4m3_rne_sat(__fdiv_rn(__fmul_rn(am, g), 6.f));
-    const float S = ue4m3_value(sfc);
-    const float r = S == 0.f ? 0.f : __fdiv_rn(g, S);
+    float r;
+    if constexpr (TAB) {
+      r = s_r[sfc];
+    } else {
+      const float S = ue4m3_value(sfc);
+      r = S == 0.f ? 0.f : __fdiv_rn(g, S);
+    }
     // the 8 codes, element 2i in the low nibble of byte i
     uint32_t w = 0;
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, __fmul_rn(xs[0], r), __fmul_rn(xs[1], r),
@@ -150,6 +159,31 @@ __global__ __launch_bounds__(QZ_THREADS) void fp4_quantize_kernel(QzArgs p) {
       const uint32_t row = cm / p.cpr, cg = (cm - row * p.cpr) >> 3;
       gst<uint32_t>(p.sf + bi * p.sf_per + sf_word_off(static_cast<int>(row), cg, p.nct), sw);
     }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(QZ_THREADS) void fp4_quantize_kernel(QzArgs p) {
+  // r = g / S for every UE4M3 code, when the workgroup's chunks all lie in one
+  // matrix of the batch (always for batch 1): the same fp32 division per
+  // code, once per workgroup instead of once per block.  Built before any
+  // input load is issued, so the barrier waits for nothing in flight.
+  __shared__ float s_r[128];
+  constexpr long WGC = (QZ_THREADS / 64) * QZ_SEG * 64;  // chunks of a workgroup
+  const long w0 = static_cast<long>(blockIdx.x) * WGC;
+  const long w1 = min(w0 + WGC, p.chunks) - 1;
+  const uint32_t b0 = p.batched ? static_cast<uint32_t>(w0 / p.per_batch) : 0u;
+  const bool one = !p.batched || static_cast<uint32_t>(w1 / p.per_batch) == b0;
+  if (one) {
+    if (threadIdx.x < 128) {
+      const float g = gld<float>(p.gscale + b0);
+      const float S = ue4m3_value(threadIdx.x);
+      s_r[threadIdx.x] = S == 0.f ? 0.f : __fdiv_rn(g, S);
+    }
+    __syncthreads();
+    qz_wave<T, true>(p, s_r, b0);
+  } else {
+    qz_wave<T, false>(p, s_r, 0u);
   }
 }
 
