@@ -1087,7 +1087,7 @@ __device__ __forceinline__ void expand_blocks(float* s_acc, const uint16_t* cons
   float fs = ring[0].f;            // F16 only
   load(ring[0], D, bptr(D));
   for (int i0 = 0; i0 < nblk; i0 += D) {
-    // this round's refill addresses, made scalar once (not inside the steps,
+    // the refill addresses of this pass over the ring, made scalar once (not inside the steps,
     // where each conversion would wait for the accumulator reads in flight)
     const uint16_t* bpr[D];
 #pragma unroll
