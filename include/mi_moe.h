@@ -85,8 +85,9 @@ MI_API int mi_abi_version(void);
  *   b         [batch, n, k] of ab_dtype  (K-major: row j of b[e] is output column j)
  *   m_indptr  int32 [batch + 1], device, non-decreasing, 0 <= values <= m_rows;
  *             read on the device only -- empty groups are skipped, no padding
- *   out       [m_rows, n] of out_dtype (MI_BF16, MI_F16 or MI_F32); only rows
- *             [m_indptr[0], m_indptr[batch]) are written, the rest untouched
+ *   out       [m_rows, n] of out_dtype (MI_BF16, MI_F16 or MI_F32), 16-byte
+ *             aligned; only rows [m_indptr[0], m_indptr[batch]) are written, the
+ *             rest untouched
  * Requirements: m_rows >= 0, batch >= 1, n % 256 == 0, k % 64 == 0 (the
  * device-walk backend's shape rule on the page), k >= 64.  k >= 4194304 (2^22)
  * returns MI_EUNSUPPORTED: the kernels address a 512-row panel of b through

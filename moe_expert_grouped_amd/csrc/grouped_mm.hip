@@ -1186,6 +1186,7 @@ extern "C" mi_status mi_grouped_mm_bf16(const void* a, int64_t m_rows, int64_t k
   if (m_rows == 0) return MI_OK;
   MI_REQUIRE(a != nullptr && out != nullptr, "grouped_mm_bf16: a/out is null");
   MI_REQUIRE(aligned16(a) && aligned16(b), "grouped_mm_bf16: a and b must be 16-byte aligned");
+  MI_REQUIRE(aligned16(out), "grouped_mm_bf16: out must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool f16 = ab_dtype == MI_F16;
   if (out_dtype == MI_BF16)

@@ -58,6 +58,9 @@ def test_grouped_mm_validation():
     assert st == _lib.MI_EUNSUPPORTED
     with pytest.raises(NotImplementedError, match="k < 4194304"):
         _lib.check(st)
+    msg = _err(L.mi_grouped_mm_bf16(FAKE, 64, 64, _lib.MI_BF16, FAKE, 2, 256, FAKE, FAKE + 8,
+                                    _lib.MI_BF16, NULL))
+    assert "out must be 16-byte aligned" in msg
     # an empty a is a no-op that returns before touching the device
     assert L.mi_grouped_mm_bf16(NULL, 0, 64, _lib.MI_BF16, FAKE, 2, 256, FAKE, NULL, _lib.MI_BF16, NULL) == 0
 
