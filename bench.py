@@ -65,6 +65,13 @@ TRAFFIC = {
         kernel="nvfp4_lora_kernel", src="nvfp4_lora.hip",
         file="profiles/nvfp4_lora_kernel_m4096_n8192_k8192_traffic.txt",
         what="nvfp4_lora_kernel, M=4096 N=8192 K=8192 r=16 (raw path)"),
+    # the delta is four launches: its bytes per call are the sum of theirs
+    "lora_delta": dict(
+        kernel=["plan_kernel", "list_kernel", "shrink_le_kernel", "expand_kernel"],
+        src="lora_delta.hip",
+        file="profiles/fc2_lora_delta_t8192_k8_e64_h4096_r16_traffic.txt",
+        what="FC2 LoRA delta (plan, list, shrink by (adapter, expert), expand), T=8192 "
+             "top_k=8 E=64 H=4096 8 adapters r=16, bf16 out, cold and warm calls"),
 }
 
 
@@ -182,12 +189,20 @@ def pmc_summary(op, fetch_dir, write_dir):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the op's kernel, each
     scaled by what the same counter reads for the copy probe of known size."""
     t = TRAFFIC[op]
-    pick = lambda k: t["kernel"] in k and "true" not in _short(k)
+    names = t["kernel"] if isinstance(t["kernel"], list) else [t["kernel"]]
     fr = _csv_rows(fetch_dir, "*counter_collection.csv")
     wr = _csv_rows(write_dir, "*counter_collection.csv")
-    k_f, n_kf = _pmc_avg(fr, "FETCH_SIZE", pick)
+    k_f = k_w = 0.0
+    n_kf = n_kw = 0
+    for nm in names:  # one dispatch of each kernel per call: sum their averages
+        if isinstance(t["kernel"], list):
+            pick = lambda k, nm=nm: _short(k).startswith(nm) and "true" not in _short(k)
+        else:
+            pick = lambda k, nm=nm: nm in k and "true" not in _short(k)
+        f, nf = _pmc_avg(fr, "FETCH_SIZE", pick)
+        w, nw = _pmc_avg(wr, "WRITE_SIZE", pick)
+        k_f, k_w, n_kf, n_kw = k_f + f, k_w + w, n_kf + nf, n_kw + nw
     cp_f, n_cf = _pmc_avg(fr, "FETCH_SIZE", _is_copy)
-    k_w, n_kw = _pmc_avg(wr, "WRITE_SIZE", pick)
     cp_w, n_cw = _pmc_avg(wr, "WRITE_SIZE", _is_copy)
     f_fac = COPY_PROBE_BYTES / (cp_f * 1024.0)
     w_fac = COPY_PROBE_BYTES / (cp_w * 1024.0)
@@ -207,6 +222,8 @@ def pmc_summary(op, fetch_dir, write_dir):
                  "# Counters are KiB per dispatch; each is scaled by the factor that maps the\n"
                  "# same counter on the copy probe (a 512 MiB fp32 read + 512 MiB write) to its\n"
                  "# known size.\n")
+        if len(names) > 1:
+            fh.write(f"# per call: the sum over its kernels {', '.join(names)} (one dispatch each)\n")
         fh.write(f"kernel_source_sha256_16 = {src_hash(t['src'])}\n")
         fh.write(f"fetch_kib_per_dispatch = {k_f:.1f}   # {n_kf} dispatches\n")
         fh.write(f"write_kib_per_dispatch = {k_w:.1f}   # {n_kw} dispatches\n")
